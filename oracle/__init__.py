@@ -1,0 +1,19 @@
+"""fp64 CPU oracle for exact attention. TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this package; the HIP library and its Python binding never do.
+"""
+
+from .attention import (
+    attention_backward,
+    attention_backward_head,
+    attention_forward,
+    attention_forward_rows,
+)
+
+__all__ = [
+    "attention_forward",
+    "attention_forward_rows",
+    "attention_backward",
+    "attention_backward_head",
+]

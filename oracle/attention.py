@@ -1,0 +1,175 @@
+"""fp64 CPU oracle for exact scaled-dot-product attention (forward and backward).
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path may import, call or
+link this module: only the test suite, the smoke check and the benchmark's
+CPU-baseline leg use it. It shares no code with the HIP library.
+
+What it computes, and where that comes from
+-------------------------------------------
+The pages describe attention in words only: tokens' representations are
+compared and each one's information is weighted (IPLEX blog post on
+FlashAttention-2 GPU work partitioning, section "Why long inputs put pressure
+on memory"). The conventional way, which this oracle follows on purpose,
+materialises the full score and probability matrices (same section; also the
+FlashAttention-2 abstract on the "High-Bandwidth Memory" keyword page: runtime
+and memory quadratic in sequence length). The tiled method must reach the same
+globally normalised result (section "Tiling preserves the attention
+calculation"), so the oracle is that plain definition written out:
+
+    S = scale * Q K^T                     (N x N, fp64)
+    causal: S[i, j] = -inf for j > i      (key j visible to query i iff j <= i)
+    P = softmax over each row of S        (m = row max, l = sum exp(S - m))
+    O = P V,   L = m + ln(l)              (natural-log logsumexp of scaled scores)
+
+The pages print no formula, so this is the plain reading: softmax(scale*QK^T)V
+with a caller-supplied scale (the benchmark uses 1/sqrt(d)).
+
+Backward (the pages require gradients to match within tolerance, same
+"Tiling" section; they give no equations). With the loss taken as sum(dO * O):
+
+    dV = P^T dO
+    dP = dO V^T
+    D  = rowsum(dO * O)                   (equals rowsum(P * dP))
+    dS = P * (dP - D)
+    dQ = scale * dS K,   dK = scale * dS^T Q
+
+Gradients are with respect to the unscaled inputs, hence the factor `scale`
+on dQ and dK. D is taken from the oracle's own fp64 O.
+
+Layout: Q, K, V, dO, O, dQ, dK, dV are float64 [B, N, H, d]; L is [B, H, N].
+Rows of S may be processed in chunks to bound memory. Each chunk holds whole
+rows of S, so every row's softmax is exactly the definition above; dK and dV
+are sums over query rows and are accumulated chunk by chunk.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+# Upper bound on elements of one fp64 score chunk (256 MiB).
+_MAX_CHUNK_ELEMS = 1 << 25
+
+
+def _row_chunks(n_rows: int, n_cols: int):
+    rows = max(1, min(n_rows, _MAX_CHUNK_ELEMS // max(1, n_cols)))
+    for r0 in range(0, n_rows, rows):
+        yield r0, min(n_rows, r0 + rows)
+
+
+def _scores(qh: np.ndarray, kh: np.ndarray, row0: int, causal: bool, scale: float) -> np.ndarray:
+    """Scaled scores for query rows row0.. of one head, causal mask applied as -inf."""
+    s = scale * (qh @ kh.T)
+    if causal:
+        qi = np.arange(row0, row0 + s.shape[0])[:, None]
+        kj = np.arange(kh.shape[0])[None, :]
+        s = np.where(kj > qi, -np.inf, s)
+    return s
+
+
+def _softmax_rows(s: np.ndarray):
+    """Row softmax of a score block; returns (P, m, l).
+
+    A row whose scores are all -inf (impossible for N_q = N_k causal, since key
+    i is always visible to query i) yields P = 0 and m = -inf."""
+    m = s.max(axis=1, keepdims=True)
+    m_safe = np.where(np.isfinite(m), m, 0.0)
+    e = np.exp(s - m_safe)
+    l = e.sum(axis=1, keepdims=True)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        p = np.where(l > 0, e / np.where(l > 0, l, 1.0), 0.0)
+    return p, m[:, 0], l[:, 0]
+
+
+def _check(q, k, v):
+    if q.ndim != 4 or q.shape != k.shape or q.shape != v.shape:
+        raise ValueError("q, k, v must share one [B, N, H, d] shape")
+
+
+def attention_forward(q, k, v, causal: bool, scale: float):
+    """Forward pass. Returns (O [B,N,H,d], L [B,H,N]) in float64."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    _check(q, k, v)
+    B, N, H, d = q.shape
+    o = np.zeros((B, N, H, d))
+    lse = np.zeros((B, H, N))
+    for b in range(B):
+        for h in range(H):
+            qh, kh, vh = q[b, :, h, :], k[b, :, h, :], v[b, :, h, :]
+            for r0, r1 in _row_chunks(N, N):
+                s = _scores(qh[r0:r1], kh, r0, causal, scale)
+                p, m, l = _softmax_rows(s)
+                o[b, r0:r1, h, :] = p @ vh
+                with np.errstate(divide="ignore"):
+                    lse[b, h, r0:r1] = m + np.log(l)
+    return o, lse
+
+
+def attention_forward_rows(q, k, v, causal: bool, scale: float, b: int, h: int, rows):
+    """Forward outputs for selected query rows of one (batch, head).
+
+    Each requested row is computed from its full score row, exactly as in
+    `attention_forward`; this lets a test check sampled outputs of a problem
+    too large to evaluate whole. Returns (O rows [len(rows), d], L rows)."""
+    rows = np.asarray(rows, dtype=np.int64)
+    kh = np.asarray(k[b, :, h, :], dtype=np.float64)
+    vh = np.asarray(v[b, :, h, :], dtype=np.float64)
+    o_rows = np.zeros((rows.size, kh.shape[1]))
+    l_rows = np.zeros(rows.size)
+    for t, i in enumerate(rows):
+        qi = np.asarray(q[b, i : i + 1, h, :], dtype=np.float64)
+        s = _scores(qi, kh, int(i), causal, scale)
+        p, m, l = _softmax_rows(s)
+        o_rows[t] = (p @ vh)[0]
+        l_rows[t] = m[0] + np.log(l[0])
+    return o_rows, l_rows
+
+
+def attention_backward(q, k, v, do, causal: bool, scale: float):
+    """Analytic backward of sum(dO * O). Returns (dQ, dK, dV, O, L, D).
+
+    O, L are the forward outputs (fp64); D = rowsum(dO * O) is [B, H, N]."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    _check(q, k, v)
+    if do.shape != q.shape:
+        raise ValueError("dO must have the shape of Q")
+    B, N, H, d = q.shape
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(q)
+    dv = np.zeros_like(q)
+    o = np.zeros_like(q)
+    lse = np.zeros((B, H, N))
+    dsum = np.zeros((B, H, N))
+    for b in range(B):
+        for h in range(H):
+            qh, kh, vh, doh = q[b, :, h, :], k[b, :, h, :], v[b, :, h, :], do[b, :, h, :]
+            for r0, r1 in _row_chunks(N, N):
+                s = _scores(qh[r0:r1], kh, r0, causal, scale)
+                p, m, l = _softmax_rows(s)
+                oc = p @ vh
+                o[b, r0:r1, h, :] = oc
+                with np.errstate(divide="ignore"):
+                    lse[b, h, r0:r1] = m + np.log(l)
+                dp = doh[r0:r1] @ vh.T
+                drow = np.sum(doh[r0:r1] * oc, axis=1)
+                dsum[b, h, r0:r1] = drow
+                ds = p * (dp - drow[:, None])
+                dq[b, r0:r1, h, :] = scale * (ds @ kh)
+                dk[b, :, h, :] += scale * (ds.T @ qh[r0:r1])
+                dv[b, :, h, :] += p.T @ doh[r0:r1]
+    return dq, dk, dv, o, lse, dsum
+
+
+def attention_backward_head(q, k, v, do, causal: bool, scale: float, b: int, h: int):
+    """Backward restricted to one (batch, head); returns (dQ, dK, dV) as [N, d].
+
+    Heads are independent, so this equals the matching slice of
+    `attention_backward` and lets a test check sampled heads of a large
+    problem."""
+    sl = (slice(b, b + 1), slice(None), slice(h, h + 1), slice(None))
+    dq, dk, dv, _, _, _ = attention_backward(q[sl], k[sl], v[sl], do[sl], causal, scale)
+    return dq[0, :, 0, :], dk[0, :, 0, :], dv[0, :, 0, :]

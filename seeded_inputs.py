@@ -1,0 +1,105 @@
+"""Seeded synthetic inputs shared by the oracle side and the HIP side.
+
+This module holds no attention arithmetic. It only draws random tensors,
+rounds them to bfloat16 and decodes bfloat16 bit patterns, so that the
+CPU oracle and the GPU library are fed the very same bits.
+
+Recipe (stated once, used everywhere):
+  * generator  numpy.random.Generator(PCG64(seed))
+  * draw order Q, K, V, then dO (only when a backward is wanted)
+  * each draw  standard_normal((B, N, H, d), dtype=float32), C order,
+               then fp32 -> bf16 round-to-nearest-even, kept as uint16 bits.
+
+The five benchmark workloads follow the attention-kernel sweep described in
+the IPLEX blog post on FlashAttention-2 work partitioning (section "Read the
+reported speed-ups with their conditions"): sequence length 512 to 16k, head
+dimension 64 and 128, causal masking, 16k tokens per batch.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    causal: bool
+    backward: bool
+    seed: int
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+
+# The tiny case the oracle finishes in well under a second, then the four
+# sweep points (16k tokens each) and the forward+backward training shape.
+WORKLOADS = {
+    "tiny": Workload("tiny", 1, 2, 128, 64, False, False, 1),
+    "short_noncausal": Workload("short_noncausal", 32, 16, 512, 64, False, False, 2),
+    "short_causal": Workload("short_causal", 32, 16, 512, 64, True, False, 2),
+    "mid_causal": Workload("mid_causal", 8, 16, 2048, 128, True, False, 3),
+    "long_causal": Workload("long_causal", 1, 16, 16384, 128, True, False, 4),
+    "train_causal": Workload("train_causal", 4, 16, 4096, 128, True, True, 5),
+}
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round fp32 to bfloat16 (round to nearest, ties to even); return uint16 bits.
+
+    Only finite inputs are expected (normal samples)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return rounded.astype(np.uint16)
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact upcast of bfloat16 bit patterns to float64."""
+    bits = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    bits = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def draw(B: int, N: int, H: int, d: int, seed: int, backward: bool = False):
+    """Return a dict of uint16 bf16 bit arrays q, k, v (and do) of shape [B,N,H,d]."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    names = ["q", "k", "v"] + (["do"] if backward else [])
+    out = {}
+    for name in names:
+        x = rng.standard_normal((B, N, H, d), dtype=np.float32)
+        out[name] = f32_to_bf16_bits(x)
+    return out
+
+
+def draw_workload(w: Workload):
+    return draw(w.B, w.N, w.H, w.d, w.seed, backward=w.backward)
+
+
+def bits_to_torch(bits: np.ndarray, device=None):
+    """View uint16 bf16 bits as a torch.bfloat16 tensor (optionally moved to a device)."""
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16)
+    if device is not None:
+        t = t.to(device)
+    return t
+
+
+def torch_to_bits(t) -> np.ndarray:
+    """Copy a torch.bfloat16 tensor back to host uint16 bits."""
+    import torch
+
+    return t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)

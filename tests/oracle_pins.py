@@ -1,0 +1,381 @@
+"""Pins for the fp64 attention oracle.
+
+Each pin checks the oracle against something other than itself: a closed
+form, an invariant the mathematics fixes, a brute-force scalar loop, finite
+differences, an independent library implementation, or a hand-worked example.
+Every pin takes the forward/backward callables as arguments so the same pins
+can be run against deliberately broken copies of the oracle (the mutation
+tests), each of which must fail at least one pin.
+
+A pin raises AssertionError on failure.
+"""
+
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+TOL = 1e-11  # fp64 agreement for identities that hold exactly in real arithmetic
+
+
+def _rand(shape, seed):
+    return np.random.Generator(np.random.PCG64(seed)).standard_normal(shape)
+
+
+def _close(a, b, tol=TOL, what=""):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    scale = max(1.0, float(np.max(np.abs(b))) if b.size else 1.0)
+    err = float(np.max(np.abs(a - b))) if a.size else 0.0
+    assert err <= tol * scale, f"{what}: max abs err {err:.3e} > {tol * scale:.3e}"
+
+
+# --------------------------------------------------------------------------
+# forward pins
+
+
+def pin_rows_sum_to_one(mod):
+    """With V = identity (N = d) the output is the probability matrix itself:
+    each row sums to one, entries lie in [0, 1], and causal rows are zero
+    past the diagonal."""
+    fwd, bwd = mod.attention_forward, mod.attention_backward
+    N = 8
+    q = _rand((1, N, 2, N), 11)
+    k = _rand((1, N, 2, N), 12)
+    v = np.zeros((1, N, 2, N))
+    for h in range(2):
+        v[0, :, h, :] = np.eye(N)
+    for causal in (False, True):
+        o, _ = fwd(q, k, v, causal, 0.7)
+        _close(o.sum(axis=3), np.ones((1, N, 2)), what="row sums")
+        assert np.all(o >= -TOL) and np.all(o <= 1 + TOL)
+        if causal:
+            upper = np.triu(np.ones((N, N), dtype=bool), 1)
+            for h in range(2):
+                assert np.all(np.abs(o[0, :, h, :][upper]) <= TOL), "causal leak"
+        else:
+            assert np.all(o > 0), "non-causal probabilities must be positive"
+
+
+def pin_q_zero(mod):
+    """Q = 0 makes every score 0: non-causal O_i = mean_j V_j, L_i = ln N;
+    causal O_i = mean_{j<=i} V_j, L_i = ln(i+1)."""
+    fwd, bwd = mod.attention_forward, mod.attention_backward
+    B, N, H, d = 2, 13, 3, 5
+    k = _rand((B, N, H, d), 21)
+    v = _rand((B, N, H, d), 22)
+    q = np.zeros((B, N, H, d))
+    o, lse = fwd(q, k, v, False, 0.3)
+    _close(o, np.broadcast_to(v.mean(axis=1, keepdims=True), o.shape), what="Q=0 mean")
+    _close(lse, np.full((B, H, N), math.log(N)), what="Q=0 lse")
+    o, lse = fwd(q, k, v, True, 0.3)
+    prefix = np.cumsum(v, axis=1) / np.arange(1, N + 1)[None, :, None, None]
+    _close(o, prefix, what="Q=0 causal prefix mean")
+    _close(lse, np.broadcast_to(np.log(np.arange(1, N + 1)), (B, H, N)), what="Q=0 causal lse")
+
+
+def pin_causal_row0(mod):
+    """Causal query 0 sees key 0 only: O_0 = V_0 and L_0 = scale * q_0 . k_0."""
+    fwd, bwd = mod.attention_forward, mod.attention_backward
+    B, N, H, d = 2, 9, 2, 4
+    q, k, v = _rand((B, N, H, d), 31), _rand((B, N, H, d), 32), _rand((B, N, H, d), 33)
+    scale = 0.45
+    o, lse = fwd(q, k, v, True, scale)
+    _close(o[:, 0], v[:, 0], what="row 0 output")
+    _close(lse[:, :, 0], scale * np.einsum("bhd,bhd->bh", q[:, 0], k[:, 0]), what="row 0 lse")
+
+
+def pin_causal_prefix(mod):
+    """Causal attention of the first n tokens does not depend on later tokens,
+    and the last causal row equals the last non-causal row."""
+    fwd, bwd = mod.attention_forward, mod.attention_backward
+    B, N, H, d = 1, 12, 2, 6
+    q, k, v = _rand((B, N, H, d), 41), _rand((B, N, H, d), 42), _rand((B, N, H, d), 43)
+    o, lse = fwd(q, k, v, True, 0.5)
+    for n in (1, 5, 11):
+        o2, lse2 = fwd(q[:, :n], k[:, :n], v[:, :n], True, 0.5)
+        _close(o[:, :n], o2, what=f"prefix {n}")
+        _close(lse[:, :, :n], lse2, what=f"prefix lse {n}")
+    o_nc, lse_nc = fwd(q, k, v, False, 0.5)
+    _close(o[:, -1], o_nc[:, -1], what="last row")
+    _close(lse[:, :, -1], lse_nc[:, :, -1], what="last row lse")
+
+
+def pin_permutations(mod):
+    """Non-causal: permuting queries permutes outputs; permuting keys and values
+    together changes nothing; swapping heads or batches permutes outputs."""
+    fwd, bwd = mod.attention_forward, mod.attention_backward
+    B, N, H, d = 2, 10, 3, 4
+    q, k, v = _rand((B, N, H, d), 51), _rand((B, N, H, d), 52), _rand((B, N, H, d), 53)
+    o, lse = fwd(q, k, v, False, 0.6)
+    perm = np.random.Generator(np.random.PCG64(5)).permutation(N)
+    o2, lse2 = fwd(q[:, perm], k, v, False, 0.6)
+    _close(o2, o[:, perm], what="query permutation")
+    _close(lse2, lse[:, :, perm], what="query permutation lse")
+    o3, lse3 = fwd(q, k[:, perm], v[:, perm], False, 0.6)
+    _close(o3, o, what="key/value permutation")
+    _close(lse3, lse, what="key/value permutation lse")
+    hp = [2, 0, 1]
+    o4, lse4 = fwd(q[:, :, hp], k[:, :, hp], v[:, :, hp], True, 0.6)
+    o4c, lse4c = fwd(q, k, v, True, 0.6)
+    _close(o4, o4c[:, :, hp], what="head permutation")
+    _close(lse4, lse4c[:, hp], what="head permutation lse")
+    o5, _ = fwd(q[::-1], k[::-1], v[::-1], False, 0.6)
+    _close(o5, o[::-1], what="batch permutation")
+
+
+def pin_constant_v(mod):
+    """V_j = c for all j gives O_i = c; then dS = 0, so dQ = dK = 0."""
+    fwd, bwd = mod.attention_forward, mod.attention_backward
+    B, N, H, d = 1, 7, 2, 3
+    q, k = _rand((B, N, H, d), 61), _rand((B, N, H, d), 62)
+    c = np.array([0.5, -1.25, 2.0])
+    v = np.broadcast_to(c, (B, N, H, d)).copy()
+    for causal in (False, True):
+        o, _ = fwd(q, k, v, causal, 0.8)
+        _close(o, v, what="constant V output")
+        if bwd is not None:
+            do = _rand((B, N, H, d), 63)
+            dq, dk, dv = bwd(q, k, v, do, causal, 0.8)[:3]
+            _close(dq, np.zeros_like(dq), what="constant V dQ")
+            _close(dk, np.zeros_like(dk), what="constant V dK")
+
+
+def pin_linear_in_v(mod):
+    """O is linear in V for fixed Q, K."""
+    fwd, bwd = mod.attention_forward, mod.attention_backward
+    B, N, H, d = 1, 9, 2, 4
+    q, k = _rand((B, N, H, d), 71), _rand((B, N, H, d), 72)
+    v1, v2 = _rand((B, N, H, d), 73), _rand((B, N, H, d), 74)
+    for causal in (False, True):
+        o1, _ = fwd(q, k, v1, causal, 0.4)
+        o2, _ = fwd(q, k, v2, causal, 0.4)
+        o12, _ = fwd(q, k, 2.0 * v1 - 3.0 * v2, causal, 0.4)
+        _close(o12, 2.0 * o1 - 3.0 * o2, what="linearity")
+
+
+def pin_key_shift(mod):
+    """K_j -> K_j + c adds scale * q_i . c to every score of row i: the
+    softmax (hence O) is unchanged and L_i shifts by exactly that amount."""
+    fwd, bwd = mod.attention_forward, mod.attention_backward
+    B, N, H, d = 1, 8, 2, 5
+    q, k, v = _rand((B, N, H, d), 81), _rand((B, N, H, d), 82), _rand((B, N, H, d), 83)
+    c = _rand((d,), 84)
+    scale = 0.35
+    for causal in (False, True):
+        o, lse = fwd(q, k, v, causal, scale)
+        o2, lse2 = fwd(q, k + c, v, causal, scale)
+        _close(o2, o, what="key shift output")
+        shift = scale * np.einsum("bnhd,d->bhn", q, c)
+        _close(lse2, lse + shift, what="key shift lse")
+
+
+def pin_single_token(mod):
+    """N = 1: O = V and L = scale * q . k, causal or not."""
+    fwd, bwd = mod.attention_forward, mod.attention_backward
+    q, k, v = _rand((3, 1, 2, 6), 91), _rand((3, 1, 2, 6), 92), _rand((3, 1, 2, 6), 93)
+    for causal in (False, True):
+        o, lse = fwd(q, k, v, causal, 0.9)
+        _close(o, v, what="N=1 output")
+        _close(lse, 0.9 * np.einsum("bnhd,bnhd->bhn", q, k), what="N=1 lse")
+
+
+def _brute_forward(q, k, v, causal, scale):
+    """Scalar loops with math.exp / math.fsum, no matrix products."""
+    B, N, H, d = q.shape
+    o = np.zeros((B, N, H, d))
+    lse = np.zeros((B, H, N))
+    for b in range(B):
+        for h in range(H):
+            for i in range(N):
+                keys = range(i + 1) if causal else range(N)
+                s = [scale * math.fsum(q[b, i, h, t] * k[b, j, h, t] for t in range(d)) for j in keys]
+                m = max(s)
+                w = [math.exp(x - m) for x in s]
+                tot = math.fsum(w)
+                for t in range(d):
+                    o[b, i, h, t] = math.fsum(w[n] * v[b, j, h, t] for n, j in enumerate(keys)) / tot
+                lse[b, h, i] = m + math.log(tot)
+    return o, lse
+
+
+def pin_brute_force(mod):
+    """Agreement with an independent scalar-loop implementation on tiny inputs."""
+    fwd, bwd = mod.attention_forward, mod.attention_backward
+    for (B, N, H, d), seed in (((1, 5, 2, 3), 101), ((2, 16, 1, 4), 102)):
+        q = _rand((B, N, H, d), seed)
+        k = _rand((B, N, H, d), seed + 1000)
+        v = _rand((B, N, H, d), seed + 2000)
+        for causal in (False, True):
+            o, lse = fwd(q, k, v, causal, 0.55)
+            ob, lseb = _brute_forward(q, k, v, causal, 0.55)
+            _close(o, ob, 1e-13, what="brute output")
+            _close(lse, lseb, 1e-13, what="brute lse")
+
+
+def pin_torch_sdpa(mod):
+    """Agreement with torch's CPU fp64 scaled_dot_product_attention (math path)
+    and its autograd gradients."""
+    fwd, bwd = mod.attention_forward, mod.attention_backward
+    import torch
+
+    for (B, N, H, d), seed in (((2, 11, 3, 8), 111), ((1, 32, 2, 16), 112)):
+        q = _rand((B, N, H, d), seed)
+        k = _rand((B, N, H, d), seed + 1)
+        v = _rand((B, N, H, d), seed + 2)
+        do = _rand((B, N, H, d), seed + 3)
+        for causal in (False, True):
+            tq, tk, tv = (torch.tensor(x.transpose(0, 2, 1, 3).copy(), requires_grad=True) for x in (q, k, v))
+            with torch.nn.attention.sdpa_kernel(torch.nn.attention.SDPBackend.MATH):
+                to = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal, scale=0.3)
+            to.backward(torch.tensor(do.transpose(0, 2, 1, 3).copy()))
+            o, _ = fwd(q, k, v, causal, 0.3)
+            _close(o, to.detach().numpy().transpose(0, 2, 1, 3), 1e-12, what="sdpa output")
+            if bwd is not None:
+                dq, dk, dv = bwd(q, k, v, do, causal, 0.3)[:3]
+                for name, mine, ref in (("dq", dq, tq.grad), ("dk", dk, tk.grad), ("dv", dv, tv.grad)):
+                    _close(mine, ref.numpy().transpose(0, 2, 1, 3), 1e-12, what=f"sdpa {name}")
+
+
+# --------------------------------------------------------------------------
+# backward pins
+
+
+def pin_backward_invariants(mod):
+    """Rows of dS sum to zero, so sum_j dK_j = 0 per (b, h); rows of P sum to
+    one, so sum_j dV_j = sum_i dO_i; causal dQ_0 = 0 because dS_00 = 0."""
+    fwd, bwd = mod.attention_forward, mod.attention_backward
+    B, N, H, d = 2, 9, 2, 5
+    q, k, v, do = (_rand((B, N, H, d), s) for s in (121, 122, 123, 124))
+    for causal in (False, True):
+        dq, dk, dv = bwd(q, k, v, do, causal, 0.7)[:3]
+        _close(dk.sum(axis=1), np.zeros((B, H, d)), what="sum dK")
+        _close(dv.sum(axis=1), do.sum(axis=1), what="sum dV")
+        if causal:
+            _close(dq[:, 0], np.zeros((B, H, d)), what="causal dQ_0")
+
+
+def pin_finite_differences(mod):
+    """Central differences of f = sum(dO * O) match the analytic gradients."""
+    fwd, bwd = mod.attention_forward, mod.attention_backward
+    h = 1e-6
+    for (B, N, H, d), causal, seed in (
+        ((1, 1, 2, 4), False, 131),
+        ((1, 3, 2, 1), True, 132),
+        ((1, 3, 2, 4), False, 133),
+        ((1, 8, 2, 4), True, 134),
+        ((1, 8, 2, 1), False, 135),
+    ):
+        q, k, v, do = (_rand((B, N, H, d), seed + 10 * t) for t in range(4))
+        scale = 0.6
+        grads = bwd(q, k, v, do, causal, scale)[:3]
+
+        def f(qq, kk, vv):
+            return float(np.sum(do * fwd(qq, kk, vv, causal, scale)[0]))
+
+        for which, g in zip(range(3), grads):
+            num = np.zeros_like(g)
+            for idx in np.ndindex(*g.shape):
+                args = [q.copy(), k.copy(), v.copy()]
+                args[which][idx] += h
+                fp = f(*args)
+                args[which][idx] -= 2 * h
+                fm = f(*args)
+                num[idx] = (fp - fm) / (2 * h)
+            _close(g, num, 1e-6, what=f"finite differences grad {which}")
+
+
+# --------------------------------------------------------------------------
+# hand-worked examples
+
+
+def pin_worked_examples(mod):
+    """Small cases worked out by hand from the definition (tests/golden)."""
+    fwd, bwd = mod.attention_forward, mod.attention_backward
+    with open(os.path.join(GOLDEN, "worked_examples.json")) as fh:
+        cases = json.load(fh)["cases"]
+    def value(x):
+        return math.log(x["ln"]) if isinstance(x, dict) else float(x)
+
+    def vec(xs):
+        return np.array([value(x) for x in xs], dtype=np.float64)
+
+    for case in cases:
+        for key in ("o", "lse", "dq", "dk", "dv"):
+            if key in case:
+                case[key] = vec(case[key])
+
+        def arr(name):
+            return vec(case[name]).reshape(1, -1, 1, 1)
+
+        q, k, v = arr("q"), arr("k"), arr("v")
+        o, lse = fwd(q, k, v, case["causal"], case["scale"])
+        _close(o.reshape(-1), case["o"], 1e-14, what=case["name"] + " O")
+        _close(lse.reshape(-1), case["lse"], 1e-14, what=case["name"] + " L")
+        if "do" in case and bwd is not None:
+            dq, dk, dv = bwd(q, k, v, arr("do"), case["causal"], case["scale"])[:3]
+            _close(dq.reshape(-1), case["dq"], 1e-14, what=case["name"] + " dQ")
+            _close(dk.reshape(-1), case["dk"], 1e-14, what=case["name"] + " dK")
+            _close(dv.reshape(-1), case["dv"], 1e-14, what=case["name"] + " dV")
+
+
+def pin_sampled_rows(mod):
+    """The sampled-row forward agrees with the scalar-loop implementation on
+    the rows it is asked for (including a non-contiguous, unsorted sample)."""
+    B, N, H, d = 2, 14, 3, 4
+    q, k, v = _rand((B, N, H, d), 141), _rand((B, N, H, d), 142), _rand((B, N, H, d), 143)
+    rows = [13, 0, 7, 6, 12]
+    for causal in (False, True):
+        ob, lseb = _brute_forward(q, k, v, causal, 0.65)
+        for b, h in ((0, 2), (1, 0)):
+            o, lse = mod.attention_forward_rows(q, k, v, causal, 0.65, b, h, rows)
+            _close(o, ob[b, rows, h, :], 1e-13, what="sampled rows output")
+            _close(lse, lseb[b, h, rows], 1e-13, what="sampled rows lse")
+
+
+def pin_backward_head(mod):
+    """The single-(batch, head) backward agrees with torch autograd on that
+    head of a problem with B != H."""
+    import torch
+
+    B, N, H, d = 2, 9, 3, 4
+    q, k, v, do = (_rand((B, N, H, d), s) for s in (151, 152, 153, 154))
+    for causal in (False, True):
+        tq, tk, tv = (torch.tensor(x.transpose(0, 2, 1, 3).copy(), requires_grad=True) for x in (q, k, v))
+        with torch.nn.attention.sdpa_kernel(torch.nn.attention.SDPBackend.MATH):
+            to = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal, scale=0.5)
+        to.backward(torch.tensor(do.transpose(0, 2, 1, 3).copy()))
+        for b, h in ((1, 2), (0, 1)):
+            dq, dk, dv = mod.attention_backward_head(q, k, v, do, causal, 0.5, b, h)
+            _close(dq, tq.grad[b, h].numpy(), 1e-12, what="head dQ")
+            _close(dk, tk.grad[b, h].numpy(), 1e-12, what="head dK")
+            _close(dv, tv.grad[b, h].numpy(), 1e-12, what="head dV")
+
+
+FORWARD_PINS = [
+    pin_rows_sum_to_one,
+    pin_q_zero,
+    pin_causal_row0,
+    pin_causal_prefix,
+    pin_permutations,
+    pin_linear_in_v,
+    pin_key_shift,
+    pin_single_token,
+    pin_brute_force,
+    pin_sampled_rows,
+]
+BACKWARD_PINS = [
+    pin_constant_v,
+    pin_backward_invariants,
+    pin_finite_differences,
+    pin_torch_sdpa,
+    pin_worked_examples,
+    pin_backward_head,
+]
+ALL_PINS = FORWARD_PINS + BACKWARD_PINS

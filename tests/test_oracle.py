@@ -1,0 +1,179 @@
+"""CPU tests of the fp64 oracle against its pins (no GPU needed).
+
+Besides running every pin against the oracle, this file plants plausible
+mistakes in a copy of the oracle's source (a dropped scale, a wrong mask
+index, a transposed operand, a flipped sign, ...) and requires each such
+mutant to fail at least one pin, so the pins are shown to be sensitive.
+"""
+
+import contextlib
+import importlib.util
+import os
+import types
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle.attention as oracle_attention
+import seeded_inputs as si
+from tests import oracle_pins as pins
+
+ORACLE_SRC = os.path.join(os.path.dirname(oracle_attention.__file__), "attention.py")
+
+
+@contextlib.contextmanager
+def chunk_limit(mod, elems):
+    """Force the oracle's row-chunking path with a tiny chunk bound."""
+    old = mod._MAX_CHUNK_ELEMS
+    mod._MAX_CHUNK_ELEMS = elems
+    try:
+        yield
+    finally:
+        mod._MAX_CHUNK_ELEMS = old
+
+
+@pytest.mark.parametrize("pin", pins.ALL_PINS, ids=lambda p: p.__name__)
+def test_oracle_pin(pin):
+    pin(oracle_attention)
+
+
+@pytest.mark.parametrize("pin", pins.ALL_PINS, ids=lambda p: p.__name__)
+def test_oracle_pin_chunked(pin):
+    """Same pins with query rows processed a few at a time."""
+    with chunk_limit(oracle_attention, 24):
+        pin(oracle_attention)
+
+
+# (name, text in the oracle source, planted replacement)
+MUTATIONS = [
+    ("scale dropped", "s = scale * (qh @ kh.T)", "s = (qh @ kh.T)"),
+    ("scale squared", "s = scale * (qh @ kh.T)", "s = scale * scale * (qh @ kh.T)"),
+    ("diagonal masked", "np.where(kj > qi,", "np.where(kj >= qi,"),
+    ("wrong triangle", "np.where(kj > qi,", "np.where(kj < qi,"),
+    ("chunk offset lost", "qi = np.arange(row0, row0 + s.shape[0])", "qi = np.arange(0, s.shape[0])"),
+    ("scores transposed", "(qh @ kh.T)", "(kh @ qh.T)"),
+    ("max over columns", "m = s.max(axis=1, keepdims=True)", "m = s.max(axis=0, keepdims=True)"),
+    ("sum over columns", "l = e.sum(axis=1, keepdims=True)", "l = e.sum(axis=0, keepdims=True)"),
+    ("P transposed in PV", "o[b, r0:r1, h, :] = p @ vh", "o[b, r0:r1, h, :] = p.T @ vh"),
+    ("lse without max", "lse[b, h, r0:r1] = m + np.log(l)\n    return o, lse",
+     "lse[b, h, r0:r1] = np.log(l)\n    return o, lse"),
+    ("lse base 2", "lse[b, h, r0:r1] = m + np.log(l)\n    return o, lse",
+     "lse[b, h, r0:r1] = m + np.log2(l)\n    return o, lse"),
+    ("dS sign", "ds = p * (dp - drow[:, None])", "ds = p * (dp + drow[:, None])"),
+    ("D dropped", "ds = p * (dp - drow[:, None])", "ds = p * dp"),
+    ("D from dP", "drow = np.sum(doh[r0:r1] * oc, axis=1)", "drow = np.sum(dp, axis=1)"),
+    ("dP transposed", "dp = doh[r0:r1] @ vh.T", "dp = (vh @ doh[r0:r1].T).T[:, ::-1]"),
+    ("dQ unscaled", "dq[b, r0:r1, h, :] = scale * (ds @ kh)", "dq[b, r0:r1, h, :] = (ds @ kh)"),
+    ("dQ uses Q", "dq[b, r0:r1, h, :] = scale * (ds @ kh)", "dq[b, r0:r1, h, :] = scale * (ds @ qh)"),
+    ("dK not transposed", "dk[b, :, h, :] += scale * (ds.T @ qh[r0:r1])",
+     "dk[b, :, h, :] += scale * (ds @ qh[r0:r1])"),
+    ("dK unscaled", "dk[b, :, h, :] += scale * (ds.T @ qh[r0:r1])", "dk[b, :, h, :] += (ds.T @ qh[r0:r1])"),
+    ("dV not transposed", "dv[b, :, h, :] += p.T @ doh[r0:r1]", "dv[b, :, h, :] += p @ doh[r0:r1]"),
+    ("dV overwritten per chunk", "dv[b, :, h, :] += p.T @ doh[r0:r1]", "dv[b, :, h, :] = p.T @ doh[r0:r1]"),
+    ("sampled row offset", "s = _scores(qi, kh, int(i), causal, scale)", "s = _scores(qi, kh, 0, causal, scale)"),
+    ("head slice swapped", "sl = (slice(b, b + 1), slice(None), slice(h, h + 1), slice(None))",
+     "sl = (slice(h, h + 1), slice(None), slice(b, b + 1), slice(None))"),
+]
+
+
+def _load_mutant(old, new):
+    src = open(ORACLE_SRC).read()
+    assert src.count(old) == 1, f"mutation anchor not found exactly once: {old!r}"
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(src.replace(old, new), ORACLE_SRC + " (mutant)", "exec"), mod.__dict__)
+    return mod
+
+
+def _survives(mod):
+    for chunk in (None, 24):
+        for pin in pins.ALL_PINS:
+            ctx = chunk_limit(mod, chunk) if chunk else contextlib.nullcontext()
+            try:
+                with ctx, np.errstate(all="ignore"):
+                    pin(mod)
+            except Exception:
+                return False
+    return True
+
+
+@pytest.mark.parametrize("name,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_planted_mistake_is_caught(name, old, new):
+    assert not _survives(_load_mutant(old, new)), f"mutant '{name}' passed every pin"
+
+
+def _blockwise_normalised(q, k, v, causal, scale, block):
+    """The wrong computation the pages warn against: softmax each key block on
+    its own, then add the block outputs."""
+    B, N, H, d = q.shape
+    o = np.zeros((B, N, H, d))
+    for b in range(B):
+        for h in range(H):
+            s = scale * q[b, :, h, :] @ k[b, :, h, :].T
+            if causal:
+                s = np.where(np.arange(N)[None, :] > np.arange(N)[:, None], -np.inf, s)
+            for j0 in range(0, N, block):
+                sb = s[:, j0 : j0 + block]
+                m = sb.max(axis=1, keepdims=True)
+                m = np.where(np.isfinite(m), m, 0.0)
+                e = np.exp(sb - m)
+                den = e.sum(axis=1, keepdims=True)
+                p = np.where(den > 0, e / np.where(den > 0, den, 1), 0.0)
+                o[b, :, h, :] += p @ v[b, j0 : j0 + block, h, :]
+    return o
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_blockwise_normalisation_is_not_attention(causal):
+    """Normalising each key block independently and adding the results is not
+    the same calculation (IPLEX blog, 'Tiling preserves the attention
+    calculation'): on the tiny workload it must miss the tolerance by far."""
+    w = si.WORKLOADS["tiny"]
+    bits = si.draw_workload(w)
+    q, k, v = (si.bf16_bits_to_f64(bits[n]) for n in ("q", "k", "v"))
+    o, _ = oracle.attention_forward(q, k, v, causal, w.scale)
+    wrong = _blockwise_normalised(q, k, v, causal, w.scale, 64)
+    assert np.max(np.abs(wrong - o)) > 0.5
+    assert np.mean(np.abs(wrong - o)) > 2e-2
+
+
+def test_bf16_rounding_matches_torch():
+    """The generator's fp32 -> bf16 rounding is round-to-nearest-even: it agrees
+    bit for bit with torch's conversion, including ties."""
+    import torch
+
+    rng = np.random.Generator(np.random.PCG64(7))
+    x = rng.standard_normal(1 << 16, dtype=np.float32) * np.float32(3.0)
+    ties = (np.arange(1, 2049, dtype=np.uint32) << 16 | 0x8000).view(np.float32)
+    x = np.concatenate([x, ties, -ties, np.float32([0.0, -0.0, 1e-30, 65504.0])])
+    ours = si.f32_to_bf16_bits(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+    back = si.bf16_bits_to_f64(ours)
+    assert np.array_equal(back, torch.from_numpy(x).to(torch.bfloat16).double().numpy())
+
+
+def test_generator_is_deterministic_and_ordered():
+    a = si.draw(1, 5, 2, 4, seed=3, backward=True)
+    b = si.draw(1, 5, 2, 4, seed=3, backward=True)
+    for n in ("q", "k", "v", "do"):
+        assert np.array_equal(a[n], b[n])
+    c = si.draw(1, 5, 2, 4, seed=3, backward=False)
+    for n in ("q", "k", "v"):
+        assert np.array_equal(a[n], c[n])
+    assert not np.array_equal(a["q"], a["k"])
+
+
+@pytest.mark.parametrize("name", ["tiny", "train_causal"])
+def test_bf16_floor_below_tolerance(name):
+    """Rounding the exact outputs to bf16 alone stays well inside the parity
+    tolerance, so the tolerance leaves room for the kernel's own rounding."""
+    w = si.WORKLOADS[name]
+    B = 1
+    H = 1 if name == "train_causal" else w.H
+    bits = si.draw(B, w.N, w.H, w.d, w.seed, backward=True)
+    q, k, v, do = (si.bf16_bits_to_f64(bits[n][:, :, :H]) for n in ("q", "k", "v", "do"))
+    dq, dk, dv, o, lse, _ = oracle.attention_backward(q, k, v, do, w.causal, w.scale)
+    for t in (o, dq, dk, dv):
+        floor = np.abs(si.bf16_bits_to_f64(si.f32_to_bf16_bits(t.astype(np.float32))) - t)
+        assert floor.max() < 0.5 * 2e-2 and floor.mean() < 0.5 * 2e-3
