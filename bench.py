@@ -1,0 +1,219 @@
+#!/usr/bin/env python3
+"""Attention forward+backward throughput on one MI355X.
+
+One step is one pass of the whole hot path over one batch of synthetic input:
+fa_fwd (O and logsumexp) followed by fa_bwd (dQ, dK, dV) on the training
+shape B=4, H=16, N=4096, d=128, causal, bf16, with iid N(0,1) inputs drawn
+from a fixed seed and already resident in device memory when timing starts.
+
+FLOP convention: forward 4*B*H*N^2*d, halved for causal; backward 2.5x the
+forward (five N x N x d products: the recomputed scores, dP, dV, dK, dQ).
+
+Printed: one JSON line with the whole-step TFLOP/s, the roofline of the
+dominant launch (the backward call) and of the forward kernel, both timed with
+HIP events on the stream the kernels run on, and the fp64 CPU oracle timed on
+a bounded sample of the same workload as a reported baseline.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6  # 256 CUs x 4096 dense bf16 flop/clk/CU x 2.4 GHz
+PEAK_HBM_GBS = 8000.0
+
+
+def fwd_flops(w) -> float:
+    f = 4.0 * w.B * w.H * w.N * w.N * w.d
+    return f / 2 if w.causal else f
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="train_causal")
+    ap.add_argument("--cpu-heads", type=int, default=8,
+                    help="heads of the workload the CPU oracle baseline runs (0 = skip)")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the forward sweep over the other workloads")
+    return ap.parse_args()
+
+
+def time_calls(fn, n, stream):
+    """Average duration (s) of fn() over n calls, HIP events on `stream`."""
+    import torch
+
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(n):
+        fn()
+    stop.record(stream)
+    stop.synchronize()
+    return start.elapsed_time(stop) / 1e3 / n
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; the multi-GPU path "
+                                   "is a design note only (see DESIGN.md)", "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import exact_tiled_attention_37_amd as fa
+    import seeded_inputs as si
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    fa.load_library()
+    dev = torch.device("cuda:0")
+    w = si.WORKLOADS[args.workload]
+    if not w.backward:
+        raise SystemExit(f"workload {w.name} has no backward; pick one with backward=True")
+
+    bits = si.draw_workload(w)
+    q, k, v, do = (si.bits_to_torch(bits[n], dev) for n in ("q", "k", "v", "do"))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    ws = torch.empty(fa.fa_bwd_workspace_bytes(w.B, w.N, w.H, w.d), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    resident = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+    stream = torch.cuda.current_stream()
+
+    def fwd():
+        fa.fa_fwd(q, k, v, w.causal, w.scale, out=o, lse=lse)
+
+    def bwd():
+        fa.fa_bwd(q, k, v, o, lse, do, w.causal, w.scale, dq=dq, dk=dk, dv=dv, workspace=ws)
+
+    for _ in range(args.warmup):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+
+    # Timed region: exactly K whole steps.
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1, e2 in ev:
+        e0.record(stream)
+        fwd()
+        e1.record(stream)
+        bwd()
+        e2.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fwd_s = sum(e0.elapsed_time(e1) for e0, e1, _ in ev) / 1e3 / args.steps
+    bwd_s = sum(e1.elapsed_time(e2) for _, e1, e2 in ev) / 1e3 / args.steps
+    step_s = ev[0][0].elapsed_time(ev[-1][2]) / 1e3 / args.steps
+    peak_mem = torch.cuda.max_memory_allocated()
+
+    ff = fwd_flops(w)
+    bf = 2.5 * ff
+    value = (ff + bf) / step_s / 1e12
+
+    def roof(flops, secs, kernel):
+        ach = flops / secs / 1e12
+        return {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None, "kernel": kernel,
+                "avg_launch_ms": round(secs * 1e3, 4), "flops_per_launch": flops}
+
+    detail = {
+        "gpu": torch.cuda.get_device_name(0),
+        "arch": torch.cuda.get_device_properties(0).gcnArchName,
+        "fwd_ms": round(fwd_s * 1e3, 4),
+        "bwd_ms": round(bwd_s * 1e3, 4),
+        "fwd_tflops": round(ff / fwd_s / 1e12, 2),
+        "bwd_tflops": round(bf / bwd_s / 1e12, 2),
+        "fwd_frac_of_peak": round(ff / fwd_s / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "wall_s_timed_region": round(wall, 4),
+        "resident_bytes": int(resident),
+        "peak_bytes_during_steps": int(peak_mem),
+    }
+
+    if not args.no_sweep:
+        sweep = {}
+        for name, wl in si.WORKLOADS.items():
+            b2 = si.draw(wl.B, wl.N, wl.H, wl.d, wl.seed)
+            q2, k2, v2 = (si.bits_to_torch(b2[n], dev) for n in ("q", "k", "v"))
+            o2 = torch.empty_like(q2)
+            l2 = torch.empty((wl.B, wl.H, wl.N), dtype=torch.float32, device=dev)
+            call = lambda: fa.fa_fwd(q2, k2, v2, wl.causal, wl.scale, out=o2, lse=l2)
+            for _ in range(3):
+                call()
+            torch.cuda.synchronize()
+            reps = 50 if wl.N * wl.N * wl.B * wl.H < (1 << 30) else 10
+            s = time_calls(call, reps, stream)
+            tf = fwd_flops(wl) / s / 1e12
+            sweep[name] = {"B": wl.B, "H": wl.H, "N": wl.N, "d": wl.d, "causal": wl.causal,
+                           "fwd_ms": round(s * 1e3, 4), "fwd_tflops": round(tf, 2),
+                           "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+            del q2, k2, v2, o2, l2
+        detail["fwd_sweep"] = sweep
+
+    cpu = None
+    if args.cpu_heads > 0:
+        import oracle
+        from threadpoolctl import threadpool_info
+
+        heads = min(args.cpu_heads, w.B * w.H)
+        sel = [(i // w.H, i % w.H) for i in range(heads)]
+        q64, k64, v64, do64 = (si.bf16_bits_to_f64(bits[n]) for n in ("q", "k", "v", "do"))
+        t1 = time.perf_counter()
+        for b, h in sel:
+            sl = (slice(b, b + 1), slice(None), slice(h, h + 1), slice(None))
+            oracle.attention_backward(q64[sl], k64[sl], v64[sl], do64[sl], w.causal, w.scale)
+        cpu_s = time.perf_counter() - t1
+        per_head = (ff + bf) / (w.B * w.H)
+        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+        cpu = {"value": round(per_head * heads / cpu_s / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+               "kind": "oracle",
+               "sample": f"fp64 oracle forward+backward of {heads} of the {w.B * w.H} (batch, head) pairs "
+                         f"of B={w.B} H={w.H} N={w.N} d={w.d} causal; {cpu_s:.1f} s"}
+
+    line = {
+        "metric": "attention fwd/bwd TFLOP/s at 1 MI355X; % of bf16 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"attention fwd+bwd B={w.B} H={w.H} N={w.N} d={w.d} "
+                               f"{'causal' if w.causal else 'non-causal'}",
+                   "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
+                   "global_batch": w.B, "seq_len": w.N, "parallelism": "single GPU"},
+        "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "roofline": roof(bf, bwd_s, "fa_bwd call (bwd_pre + bwd_main + bwd_finalize kernels)"),
+        "roofline_fwd": roof(ff, fwd_s, "fwd_kernel"),
+        "cpu_baseline": cpu,
+        "detail": detail,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

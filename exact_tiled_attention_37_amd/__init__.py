@@ -1,0 +1,169 @@
+"""Exact tiled attention for MI355X (gfx950): thin Python binding.
+
+The binding only marshals arguments. Every step of the computation runs in
+the HIP kernels of libfa_mi355x.so, reached through the C ABI declared in
+include/fa.h; PyTorch is used only to own device memory and streams. There
+is no fallback: if the library is missing or cannot be loaded, every call
+raises.
+
+Tensors use the library's layouts: q, k, v, o, do, dq, dk, dv are
+torch.bfloat16 [B, N, H, d] contiguous CUDA (HIP) tensors; lse is
+torch.float32 [B, H, N].
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+__all__ = [
+    "FaError",
+    "lib_path",
+    "load_library",
+    "fa_fwd",
+    "fa_bwd",
+    "fa_bwd_workspace_bytes",
+    "fa_status_string",
+    "fa_version",
+    "EXPORTED_SYMBOLS",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libfa_mi355x.so"
+EXPORTED_SYMBOLS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_string", "fa_version")
+
+_lib = None
+
+
+class FaError(RuntimeError):
+    """A non-zero status returned by the library."""
+
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {fa_status_string(status)} (status {status})")
+
+
+def lib_path() -> str:
+    return os.path.join(_PKG, _LIB_NAME)
+
+
+def load_library():
+    """Load libfa_mi355x.so (built by exact_tiled_attention_37_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = lib_path()
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m exact_tiled_attention_37_amd.build` "
+            "(there is no non-HIP fallback)"
+        )
+    lib = ctypes.CDLL(path)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
+    lib.fa_fwd.restype = i
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, vp]
+    lib.fa_bwd.restype = i
+    lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i]
+    lib.fa_bwd_workspace_bytes.restype = sz
+    lib.fa_status_string.argtypes = [i]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_version.argtypes = []
+    lib.fa_version.restype = i
+    _lib = lib
+    return lib
+
+
+def fa_status_string(status: int) -> str:
+    return load_library().fa_status_string(int(status)).decode()
+
+
+def fa_version() -> int:
+    return int(load_library().fa_version())
+
+
+def fa_bwd_workspace_bytes(B: int, N: int, H: int, d: int) -> int:
+    return int(load_library().fa_bwd_workspace_bytes(B, N, H, d))
+
+
+def _check_bnhd(name, t, shape=None):
+    import torch
+
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be torch.bfloat16, got {t.dtype}")
+    if t.dim() != 4:
+        raise ValueError(f"{name} must be [B, N, H, d], got shape {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _check_lse(t, B, N, H):
+    import torch
+
+    if t.dtype != torch.float32 or tuple(t.shape) != (B, H, N) or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"lse must be a contiguous float32 device tensor of shape {(B, H, N)}")
+
+
+def _stream_handle(device) -> int:
+    import torch
+
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def fa_fwd(q, k, v, causal: bool, softmax_scale: Optional[float] = None, out=None, lse=None):
+    """Forward pass on the current stream of q's device. Returns (o, lse)."""
+    import torch
+
+    _check_bnhd("q", q)
+    B, N, H, d = q.shape
+    _check_bnhd("k", k, q.shape)
+    _check_bnhd("v", v, q.shape)
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        out = torch.empty_like(q)
+    _check_bnhd("out", out, q.shape)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check_lse(lse, B, N, H)
+    st = load_library().fa_fwd(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+        B, N, H, d, int(bool(causal)), scale, _stream_handle(q.device),
+    )
+    if st != 0:
+        raise FaError(st, "fa_fwd")
+    return out, lse
+
+
+def fa_bwd(q, k, v, o, lse, do, causal: bool, softmax_scale: Optional[float] = None,
+           dq=None, dk=None, dv=None, workspace=None) -> Tuple:
+    """Backward pass on the current stream of q's device. Returns (dq, dk, dv)."""
+    import torch
+
+    _check_bnhd("q", q)
+    B, N, H, d = q.shape
+    for name, t in (("k", k), ("v", v), ("o", o), ("do", do)):
+        _check_bnhd(name, t, q.shape)
+    _check_lse(lse, B, N, H)
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _check_bnhd(name, t, q.shape)
+    need = fa_bwd_workspace_bytes(B, N, H, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    st = load_library().fa_bwd(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
+        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), workspace.numel(),
+        B, N, H, d, int(bool(causal)), scale, _stream_handle(q.device),
+    )
+    if st != 0:
+        raise FaError(st, "fa_bwd")
+    return dq, dk, dv

@@ -1,0 +1,121 @@
+// C ABI of the library: argument validation, device check and dispatch to the
+// gfx950 kernels. Declarations and the full contract are in include/fa.h.
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "fa.h"
+#include "fa_launch.hpp"
+
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+constexpr int kMaxDevices = 64;
+
+// 0 = not checked yet, 1 = gfx950, 2 = something else.
+std::atomic<int> g_device_state[kMaxDevices];
+
+fa_status check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return FA_ERR_DEVICE;
+  int st = g_device_state[dev].load(std::memory_order_acquire);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return FA_ERR_HIP;
+    st = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_device_state[dev].store(st, std::memory_order_release);
+  }
+  return st == 1 ? FA_OK : FA_ERR_DEVICE;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+fa_status check_shape(int B, int N, int H, int d) {
+  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if (B < 1 || N < 1 || H < 1) return FA_ERR_SHAPE;
+  const long long elems = (long long)B * N * H * d;
+  if (elems >= (1LL << 31)) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+template <typename F>
+fa_status dispatch(int d, int causal, F&& f) {
+  hipError_t e;
+  if (d == 64)
+    e = causal ? f(std::integral_constant<int, 64>{}, std::true_type{})
+               : f(std::integral_constant<int, 64>{}, std::false_type{});
+  else
+    e = causal ? f(std::integral_constant<int, 128>{}, std::true_type{})
+               : f(std::integral_constant<int, 128>{}, std::false_type{});
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int N,
+                 int H, int d, int causal, float softmax_scale, hipStream_t stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  fa_status st = check_shape(B, N, H, d);
+  if (st != FA_OK) return st;
+  if (!std::isfinite(softmax_scale)) return FA_ERR_SCALE;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
+    return FA_ERR_ALIGN;
+  st = check_device();
+  if (st != FA_OK) return st;
+  (void)hipGetLastError();  // do not report an earlier, unrelated error as ours
+  const fa::FwdArgs a{q, k, v, o, lse, B, N, H, softmax_scale, stream};
+  return dispatch(d, causal, [&](auto D, auto C) { return fa::launch_fwd<decltype(D)::value, decltype(C)::value>(a); });
+}
+
+size_t fa_bwd_workspace_bytes(int B, int N, int H, int d) {
+  if (check_shape(B, N, H, d) != FA_OK) return 0;
+  return fa::bwd_dq_acc_bytes(B, N, H, d) + fa::bwd_dsum_bytes(B, N, H);
+}
+
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                 const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                 size_t workspace_bytes, int B, int N, int H, int d, int causal,
+                 float softmax_scale, hipStream_t stream) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
+  fa_status st = check_shape(B, N, H, d);
+  if (st != FA_OK) return st;
+  if (!std::isfinite(softmax_scale)) return FA_ERR_SCALE;
+  if (!workspace || workspace_bytes < fa_bwd_workspace_bytes(B, N, H, d)) return FA_ERR_WORKSPACE;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
+      !aligned(lse, 4) || !aligned(workspace, 256))
+    return FA_ERR_ALIGN;
+  st = check_device();
+  if (st != FA_OK) return st;
+  (void)hipGetLastError();
+  char* ws = static_cast<char*>(workspace);
+  fa::BwdArgs a{q, k, v, o, lse, dout, dq, dk, dv,
+                reinterpret_cast<float*>(ws),
+                reinterpret_cast<float*>(ws + fa::bwd_dq_acc_bytes(B, N, H, d)),
+                B, N, H, softmax_scale, stream};
+  return dispatch(d, causal, [&](auto D, auto C) { return fa::launch_bwd<decltype(D)::value, decltype(C)::value>(a); });
+}
+
+const char* fa_status_string(fa_status status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULL: return "a required pointer is NULL";
+    case FA_ERR_SHAPE: return "invalid shape: B, N, H must be >= 1 and B*N*H*d < 2^31";
+    case FA_ERR_HEADDIM: return "unsupported head dimension: d must be 64 or 128";
+    case FA_ERR_ALIGN: return "misaligned pointer: tensors need 16 bytes, lse 4, workspace 256";
+    case FA_ERR_SCALE: return "softmax_scale is not finite";
+    case FA_ERR_WORKSPACE: return "workspace missing or smaller than fa_bwd_workspace_bytes()";
+    case FA_ERR_HIP: return "a HIP runtime call or kernel launch failed";
+    case FA_ERR_DEVICE: return "the current device is not a gfx950 (MI355X) GPU";
+  }
+  return "unknown status";
+}
+
+int fa_version(void) { return kVersion; }
+
+}  // extern "C"

@@ -1,0 +1,138 @@
+// Device-side building blocks shared by the forward and backward kernels
+// (gfx950 / CDNA4 only).
+//
+// Register layouts used throughout (verified on the device for
+// v_mfma_f32_32x32x16_bf16, lane l, g = l / 32):
+//   A operand (32 x 16, M x K): lane l holds row m = l % 32, k = 8g .. 8g+7
+//   B operand (16 x 32, K x N): lane l holds column n = l % 32, k = 8g .. 8g+7
+//   C/D (32 x 32):              lane l holds column n = l % 32 and rows
+//                               m = 8*(r/4) + 4g + (r%4) for r = 0..15
+// Only the pairing of A's and B's k slots matters for the product, so an
+// operand may present its k values in any order as long as the other operand
+// uses the same order.
+//
+// LDS tiles hold rows of d bfloat16 (d/8 chunks of 16 bytes). Chunk c of row
+// r is stored at chunk position c ^ swz(r). The swizzle is chosen so that
+// both access patterns the kernels use are free of bank conflicts:
+//   * row reads: 32 lanes read the same chunk of 32 consecutive rows;
+//   * transpose reads (ds_read_b64_tr_b16): a 16-lane group reads two
+//     adjacent chunks of 4 consecutive rows, and neighbouring groups read
+//     the next two chunks of the same rows.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define FA_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kNumXcd = 8;  // MI355X: 8 accelerator complex dies, one L2 each
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Chunk swizzle for a tile with D columns (see the header comment).
+// D = 32 is the narrow dS^T tile of the backward pass (4 chunks per row).
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+  static_assert(D == 32 || D == 64 || D == 128, "tile width");
+  if constexpr (D == 128)
+    return 4 * (row & 3) + ((row >> 2) & 3);
+  else if constexpr (D == 64)
+    return 4 * ((row >> 1) & 1) + ((row >> 2) & 3);
+  else
+    return (row >> 2) & 3;
+}
+
+// Byte offset of 16-byte chunk c of row `row` in a swizzled tile.
+template <int D>
+__device__ __forceinline__ int tile_off(int row, int c) {
+  return (row * (D / 8) + (c ^ swz<D>(row))) * 16;
+}
+
+// Generic pointers into __shared__ arrays are converted to LDS (address
+// space 3) pointers so that ds_read / ds_write instructions are emitted.
+__device__ __forceinline__ u32x4 lds_read16(const char* base, int off) {
+  return *(const FA_LDS u32x4*)((const FA_LDS char*)base + off);
+}
+__device__ __forceinline__ void lds_write16(char* base, int off, u32x4 v) {
+  *(FA_LDS u32x4*)((FA_LDS char*)base + off) = v;
+}
+__device__ __forceinline__ void lds_write8(char* base, int off, u32x2 v) {
+  *(FA_LDS u32x2*)((FA_LDS char*)base + off) = v;
+}
+
+// Row-read operand: 8 consecutive elements (chunk c) of row `row`.
+template <int D>
+__device__ __forceinline__ bf16x8 read_row8(const char* tile, int row, int c) {
+  u32x4 v = lds_read16(tile, tile_off<D>(row, c));
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane t supplies the address
+// of 4 consecutive 16-bit elements ("chunk t"); lane j receives element
+// j%4 of chunks j/4, j/4+4, j/4+8, j/4+12 (measured on the device).
+__device__ __forceinline__ i16x4 lds_read_tr(const char* base, int off) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)((FA_LDS char*)base + off));
+}
+
+// Column operand from a row-major tile (rows = the k dimension).
+// Returns, for this lane's column col0 + (lane % 16), the 8 elements of rows
+// rowA .. rowA+3 followed by rowB .. rowB+3, where rowA/rowB are given for the
+// lane's 16-lane group. col0 must be a multiple of 16.
+template <int D>
+__device__ __forceinline__ bf16x8 read_col8(const char* tile, int rowA, int rowB, int col0, int lane) {
+  const int j = lane & 15;
+  const int col = col0 + 4 * (j & 3);
+  const int c = col >> 3, half = (col >> 2) & 1;
+  const int ra = rowA + (j >> 2), rb = rowB + (j >> 2);
+  i16x4 lo = lds_read_tr(tile, tile_off<D>(ra, c) + 8 * half);
+  i16x4 hi = lds_read_tr(tile, tile_off<D>(rb, c) + 8 * half);
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Combine a value with the same value of lane l ^ 32 (v_permlane32_swap).
+__device__ __forceinline__ float xhalf_max(float x) {
+  uint32_t u = __float_as_uint(x);
+  auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+  uint32_t u = __float_as_uint(x);
+  auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ bf16x8 to_bf16x8(f32x8 x) { return __builtin_convertvector(x, bf16x8); }
+__device__ __forceinline__ bf16x4 to_bf16x4(f32x4 x) { return __builtin_convertvector(x, bf16x4); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Blocks are dispatched round-robin over the XCDs (block i goes to XCD i % 8).
+// Remap so that each XCD receives one contiguous range of logical blocks:
+// consecutive logical blocks (the query blocks of one head) then share an L2.
+// The map is a bijection of [0, total) for any total, so correctness never
+// depends on the dispatch order.
+__device__ __forceinline__ int xcd_remap(int bid, int total) {
+  const int per = total / kNumXcd, rem = total % kNumXcd;
+  const int x = bid % kNumXcd, idx = bid / kNumXcd;
+  return (x < rem) ? x * (per + 1) + idx : rem * (per + 1) + (x - rem) * per + idx;
+}
+
+}  // namespace fa

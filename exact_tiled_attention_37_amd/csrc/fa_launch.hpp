@@ -1,0 +1,48 @@
+// Host-side launch interface between the C ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace fa {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int B, N, H;
+  float scale;
+  hipStream_t stream;
+};
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const float* lse;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dq_acc;  // [B, N, H, d] fp32 workspace
+  float* dsum;    // [B, H, N]    fp32 workspace, D = rowsum(dO * O)
+  int B, N, H;
+  float scale;
+  hipStream_t stream;
+};
+
+template <int D, bool CAUSAL>
+hipError_t launch_fwd(const FwdArgs& a);
+
+template <int D, bool CAUSAL>
+hipError_t launch_bwd(const BwdArgs& a);
+
+// Workspace layout of the backward pass (both parts 256-byte aligned).
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+inline size_t bwd_dq_acc_bytes(long B, long N, long H, long d) { return align256(size_t(B * N * H * d) * 4); }
+inline size_t bwd_dsum_bytes(long B, long N, long H) { return align256(size_t(B * H * N) * 4); }
+
+}  // namespace fa

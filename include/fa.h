@@ -1,0 +1,117 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) exact tiled attention library.
+ *
+ * The library computes exact scaled-dot-product attention the way the
+ * FlashAttention-2 abstract (on the "High-Bandwidth Memory" keyword page)
+ * and the IPLEX blog post on FlashAttention-2 GPU work partitioning describe
+ * it: Q/K/V tiles are staged on chip, an online softmax keeps running row
+ * statistics and rescales partial outputs (post section "Tiling preserves the
+ * attention calculation"), no N x N score or probability matrix is written to
+ * device memory, work is spread over batch x heads x query blocks and the
+ * query rows of a block are split across wavefronts that share the K/V tiles
+ * (section "Three changes improve GPU utilisation").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *   - All tensor arguments are DEVICE pointers on the current HIP device.
+ *   - q, k, v, o, dout, dq, dk, dv: bfloat16, contiguous, layout [B, N, H, d]
+ *     (token-major: element (b, n, h, j) is at ((b*N + n)*H + h)*d + j).
+ *     They must be 16-byte aligned.
+ *   - lse: float32, contiguous, layout [B, H, N]; natural-log logsumexp of the
+ *     scaled scores of each query row, L_i = ln sum_j exp(scale * q_i . k_j)
+ *     over the visible keys j. 4-byte aligned.
+ *   - Causal: key j is visible to query i iff j <= i (equal query and key
+ *     lengths). Non-causal: every key is visible.
+ *   - softmax_scale: any finite float (1/sqrt(d) is the usual choice).
+ *   - Supported head dimensions: d = 64 and d = 128. Any N >= 1, B >= 1,
+ *     H >= 1 with B*N*H*d < 2^31.
+ *   - Work is enqueued on `stream` (0 = the null stream) and the call returns
+ *     without synchronising. Device faults surface at the caller's next
+ *     synchronisation. Validation happens before anything is enqueued; a
+ *     non-FA_OK status means nothing was launched.
+ *   - The library allocates no device memory and keeps no per-call state;
+ *     the caller owns every buffer. Calls on different streams may run
+ *     concurrently as long as their output buffers do not overlap.
+ *   - Outputs must not alias inputs.
+ */
+#ifndef FA_MI355X_H
+#define FA_MI355X_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifndef FA_API
+#define FA_API __attribute__((visibility("default")))
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fa_status {
+    FA_OK = 0,
+    FA_ERR_NULL = 1,      /* a required pointer is NULL                         */
+    FA_ERR_SHAPE = 2,     /* B, N or H < 1, or the tensors exceed 2^31 elements */
+    FA_ERR_HEADDIM = 3,   /* d is not 64 or 128                                 */
+    FA_ERR_ALIGN = 4,     /* a pointer is not aligned as required               */
+    FA_ERR_SCALE = 5,     /* softmax_scale is not finite                        */
+    FA_ERR_WORKSPACE = 6, /* workspace missing or smaller than required         */
+    FA_ERR_HIP = 7,       /* a HIP runtime call or kernel launch failed         */
+    FA_ERR_DEVICE = 8     /* the current device is not a gfx950 (MI355X) GPU    */
+} fa_status;
+
+/*
+ * Forward pass: O = softmax(scale * Q K^T [+ causal mask]) V and its logsumexp.
+ * (FlashAttention-2 abstract; IPLEX post, sections "Tiling preserves the
+ * attention calculation" and "Three changes improve GPU utilisation".)
+ *
+ *   q, k, v   [B, N, H, d] bf16 inputs (read only)
+ *   o         [B, N, H, d] bf16 output, rounded to nearest even
+ *   lse       [B, H, N]    fp32 output, natural-log logsumexp (see above);
+ *             it is what fa_bwd needs to recompute the probabilities
+ */
+FA_API fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int N, int H, int d, int causal, float softmax_scale,
+                 hipStream_t stream);
+
+/*
+ * Bytes of device workspace fa_bwd needs for this problem size (a float32
+ * dQ accumulator [B, N, H, d] and the float32 row terms D = rowsum(dO * O),
+ * [B, H, N], each 256-byte aligned). Returns 0 for an invalid shape.
+ */
+FA_API size_t fa_bwd_workspace_bytes(int B, int N, int H, int d);
+
+/*
+ * Backward pass of the forward above, recomputing the probabilities from the
+ * saved logsumexp instead of storing them (the gradients must match within
+ * tolerance: IPLEX post, section "Tiling preserves the attention
+ * calculation"). With loss = sum(dO * O):
+ *   D = rowsum(dO * O), dS = P * (dP - D) with dP = dO V^T,
+ *   dV = P^T dO,  dQ = scale * dS K,  dK = scale * dS^T Q.
+ *
+ *   q, k, v      [B, N, H, d] bf16, the forward's inputs
+ *   o, lse       the forward's outputs for the same inputs and flags
+ *   dout         [B, N, H, d] bf16 upstream gradient dO
+ *   dq, dk, dv   [B, N, H, d] bf16 outputs, rounded to nearest even
+ *   workspace    device scratch of at least fa_bwd_workspace_bytes(B,N,H,d)
+ *                bytes, 256-byte aligned, owned by the caller; its contents on
+ *                entry do not matter and on return are unspecified. Two calls
+ *                in flight at once need two workspaces.
+ */
+FA_API fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
+                 const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                 void* workspace, size_t workspace_bytes,
+                 int B, int N, int H, int d, int causal, float softmax_scale,
+                 hipStream_t stream);
+
+/* Human-readable text of a status code (a static string; never NULL). */
+FA_API const char* fa_status_string(fa_status status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+FA_API int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_MI355X_H */

@@ -1,0 +1,137 @@
+"""Host-side tests of the C ABI (no GPU needed).
+
+Every call here fails argument validation, which the library performs before
+it touches the device, so no kernel is ever launched and fake non-null
+pointers are never dereferenced.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_tiled_attention_37_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_HEADDIM, FA_ERR_ALIGN = 0, 1, 2, 3, 4
+FA_ERR_SCALE, FA_ERR_WORKSPACE, FA_ERR_HIP, FA_ERR_DEVICE = 5, 6, 7, 8
+
+P = 0x10000  # a fake, 256-byte aligned device address; never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"FA_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fa.lib_path()):
+        pytest.fail("libfa_mi355x.so is not built: run `python -m exact_tiled_attention_37_amd.build`")
+    return fa.load_library()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    assert sorted(names) == sorted(fa.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    raw = ctypes.CDLL(fa.lib_path())
+    for name in declared_functions():
+        assert hasattr(raw, name), f"{name} is declared in fa.h but not exported"
+
+
+def test_status_strings_and_version(lib):
+    for st in range(9):
+        s = fa.fa_status_string(st)
+        assert isinstance(s, str) and s
+    assert fa.fa_status_string(FA_OK) == "ok"
+    assert fa.fa_status_string(1234) == "unknown status"
+    assert fa.fa_version() == 100
+
+
+def test_workspace_bytes(lib):
+    B, N, H, d = 4, 4096, 16, 128
+    dq = B * N * H * d * 4
+    dsum = B * H * N * 4
+    pad = lambda x: (x + 255) // 256 * 256
+    assert fa.fa_bwd_workspace_bytes(B, N, H, d) == pad(dq) + pad(dsum)
+    assert fa.fa_bwd_workspace_bytes(1, 3, 1, 64) == pad(3 * 64 * 4) + pad(3 * 4)
+    assert fa.fa_bwd_workspace_bytes(1, 3, 1, 96) == 0
+    assert fa.fa_bwd_workspace_bytes(0, 3, 1, 64) == 0
+    assert fa.fa_bwd_workspace_bytes(1 << 14, 1 << 14, 16, 128) == 0  # > 2^31 elements
+
+
+def fwd(lib, q=P, k=P, v=P, o=P, lse=P, B=1, N=8, H=2, d=64, causal=0, scale=0.125):
+    return lib.fa_fwd(q, k, v, o, lse, B, N, H, d, causal, scale, None)
+
+
+def bwd(lib, ws_bytes=1 << 20, ws=P, B=1, N=8, H=2, d=64, scale=0.125, **ptrs):
+    p = dict(q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P)
+    p.update(ptrs)
+    return lib.fa_bwd(p["q"], p["k"], p["v"], p["o"], p["lse"], p["do"], p["dq"], p["dk"], p["dv"],
+                      ws, ws_bytes, B, N, H, d, 0, scale, None)
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "o", "lse"])
+def test_fwd_null_pointer(lib, which):
+    assert fwd(lib, **{which: None}) == FA_ERR_NULL
+
+
+@pytest.mark.parametrize("d", [0, 32, 80, 96, 256])
+def test_fwd_head_dim(lib, d):
+    assert fwd(lib, d=d) == FA_ERR_HEADDIM
+
+
+@pytest.mark.parametrize("B,N,H", [(0, 8, 2), (1, 0, 2), (1, 8, 0), (-1, 8, 2), (4096, 65536, 16)])
+def test_fwd_shape(lib, B, N, H):
+    assert fwd(lib, B=B, N=N, H=H) == FA_ERR_SHAPE
+
+
+@pytest.mark.parametrize("scale", [float("inf"), float("-inf"), float("nan")])
+def test_fwd_scale(lib, scale):
+    assert fwd(lib, scale=scale) == FA_ERR_SCALE
+
+
+@pytest.mark.parametrize("which,addr", [("q", P + 8), ("k", P + 2), ("v", P + 4), ("o", P + 1), ("lse", P + 2)])
+def test_fwd_alignment(lib, which, addr):
+    assert fwd(lib, **{which: addr}) == FA_ERR_ALIGN
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "o", "lse", "do", "dq", "dk", "dv"])
+def test_bwd_null_pointer(lib, which):
+    assert bwd(lib, **{which: None}) == FA_ERR_NULL
+
+
+def test_bwd_workspace(lib):
+    need = fa.fa_bwd_workspace_bytes(1, 8, 2, 64)
+    assert bwd(lib, ws_bytes=need - 1) == FA_ERR_WORKSPACE
+    assert bwd(lib, ws=None) == FA_ERR_WORKSPACE
+    assert bwd(lib, ws=P + 128, ws_bytes=need) == FA_ERR_ALIGN
+
+
+def test_bwd_shape_headdim_scale(lib):
+    assert bwd(lib, d=96) == FA_ERR_HEADDIM
+    assert bwd(lib, N=0) == FA_ERR_SHAPE
+    assert bwd(lib, scale=float("nan")) == FA_ERR_SCALE
+
+
+@pytest.mark.parametrize("which", ["q", "do", "dq", "dk", "dv"])
+def test_bwd_alignment(lib, which):
+    assert bwd(lib, **{which: P + 8}) == FA_ERR_ALIGN
+
+
+def test_binding_rejects_wrong_tensors(lib):
+    import torch
+
+    q = torch.zeros(1, 8, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):  # host tensor
+        fa.fa_fwd(q, q, q, causal=False)
+    with pytest.raises(TypeError):
+        fa.fa_fwd(q.float(), q, q, causal=False)
+    with pytest.raises(ValueError):
+        fa.fa_fwd(q[0], q, q, causal=False)

@@ -1,0 +1,278 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle.
+
+Every test feeds the same seeded bf16 bits to both sides and compares element
+by element. Tolerances: O, dQ, dK, dV max-abs <= 2e-2 and mean-abs <= 2e-3;
+the fp32 logsumexp max-abs <= 1e-3. Small shapes (several tiles plus a ragged
+tail) are compared whole; the five benchmark workloads run at full size in the
+same launch configuration the benchmark times, and are compared on sampled
+heads or rows that the oracle evaluates one by one.
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import exact_tiled_attention_37_amd as fa
+import oracle
+import seeded_inputs as si
+
+pytestmark = pytest.mark.gpu
+
+MAX_TOL, MEAN_TOL, LSE_TOL = 2e-2, 2e-3, 1e-3
+
+
+def announce(msg):
+    sys.__stderr__.write(f"[gpu-case] {msg}\n")
+    sys.__stderr__.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible: GPU tests need an MI355X")
+    fa.load_library()
+    return torch.device("cuda:0")
+
+
+def dev(bits):
+    return si.bits_to_torch(bits, "cuda")
+
+
+def f64(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def check(name, got, ref, max_tol=MAX_TOL, mean_tol=MEAN_TOL):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, f"{name}: shape {got.shape} vs {ref.shape}"
+    assert np.all(np.isfinite(got)), f"{name}: non-finite values"
+    err = np.abs(got - ref)
+    mx, mn = float(err.max()), float(err.mean())
+    assert mx <= max_tol and mn <= mean_tol, (
+        f"{name}: max-abs {mx:.3e} (tol {max_tol}), mean-abs {mn:.3e} (tol {mean_tol}), "
+        f"at {np.unravel_index(int(err.argmax()), err.shape)}"
+    )
+
+
+def gpu_fwd(bits, causal, scale):
+    import torch
+
+    q, k, v = dev(bits["q"]), dev(bits["k"]), dev(bits["v"])
+    o, lse = fa.fa_fwd(q, k, v, causal, scale)
+    torch.cuda.synchronize()
+    return q, k, v, o, lse
+
+
+def gpu_bwd(q, k, v, o, lse, do_bits, causal, scale, workspace=None):
+    import torch
+
+    do = dev(do_bits)
+    dq, dk, dv = fa.fa_bwd(q, k, v, o, lse, do, causal, scale, workspace=workspace)
+    torch.cuda.synchronize()
+    return dq, dk, dv
+
+
+# ---------------------------------------------------------------------------
+# small shapes: whole-tensor comparison, forward and backward
+
+SMALL = [
+    (1, 1, 1, 64), (1, 3, 2, 64), (2, 17, 3, 128), (1, 64, 2, 64), (1, 127, 2, 128),
+    (2, 129, 1, 64), (1, 200, 2, 128), (1, 333, 3, 64), (1, 1000, 1, 128), (1, 256, 2, 128),
+]
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "B%dN%dH%dd%d" % s)
+def test_small_fwd_bwd(shape, causal):
+    B, N, H, d = shape
+    seed = 1000 + N * 7 + d + int(causal)
+    scale = 1.0 / math.sqrt(d)
+    announce(f"small fwd+bwd shape={shape} causal={causal} seed={seed}")
+    bits = si.draw(B, N, H, d, seed, backward=True)
+    q64, k64, v64, do64 = (si.bf16_bits_to_f64(bits[n]) for n in ("q", "k", "v", "do"))
+    rq, rk, rv, ro, rl, _ = oracle.attention_backward(q64, k64, v64, do64, causal, scale)
+    q, k, v, o, lse = gpu_fwd(bits, causal, scale)
+    check("O", f64(o), ro)
+    check("LSE", f64(lse), rl, LSE_TOL, LSE_TOL)
+    dq, dk, dv = gpu_bwd(q, k, v, o, lse, bits["do"], causal, scale)
+    check("dQ", f64(dq), rq)
+    check("dK", f64(dk), rk)
+    check("dV", f64(dv), rv)
+
+
+def check_rel(name, got, ref):
+    """Tolerance for scales other than 1/sqrt(d): the fixed absolute bounds
+    assume O(1) outputs, but bf16 rounding of P, dS and of the outputs gives
+    errors proportional to the output's magnitude M = max|ref|, which grows
+    with |scale|. The bound keeps the absolute tolerance up to M = 2 and
+    scales it with M beyond (2e-2 * M / 2 is about 2.5 bf16 ulps of M)."""
+    m = max(1.0, float(np.max(np.abs(ref))) / 2.0)
+    check(name, got, ref, MAX_TOL * m, MEAN_TOL * m)
+
+
+@pytest.mark.parametrize("scale", [-0.2, 0.0, 0.9, 2.5], ids=lambda s: f"scale{s}")
+@pytest.mark.parametrize("d", [64, 128])
+def test_other_scales(scale, d):
+    B, N, H = 1, 150, 2
+    for causal in (False, True):
+        announce(f"scale={scale} d={d} causal={causal}")
+        bits = si.draw(B, N, H, d, 77 + d, backward=True)
+        q64, k64, v64, do64 = (si.bf16_bits_to_f64(bits[n]) for n in ("q", "k", "v", "do"))
+        rq, rk, rv, ro, rl, _ = oracle.attention_backward(q64, k64, v64, do64, causal, scale)
+        q, k, v, o, lse = gpu_fwd(bits, causal, scale)
+        check("O", f64(o), ro)
+        check("LSE", f64(lse), rl, LSE_TOL, LSE_TOL)
+        dq, dk, dv = gpu_bwd(q, k, v, o, lse, bits["do"], causal, scale)
+        check_rel("dQ", f64(dq), rq)
+        check_rel("dK", f64(dk), rk)
+        check_rel("dV", f64(dv), rv)
+
+
+# ---------------------------------------------------------------------------
+# closed forms and exact properties on the GPU
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_zero_queries_closed_form(d):
+    """Q = 0: causal O_i is the prefix mean of V and L_i = ln(i + 1)."""
+    import torch
+
+    B, N, H = 1, 300, 2
+    announce(f"Q=0 closed form d={d}")
+    bits = si.draw(B, N, H, d, 5 + d)
+    bits["q"] = np.zeros_like(bits["q"])
+    q, k, v, o, lse = gpu_fwd(bits, True, 1.0 / math.sqrt(d))
+    v64 = si.bf16_bits_to_f64(bits["v"])
+    prefix = np.cumsum(v64, axis=1) / np.arange(1, N + 1)[None, :, None, None]
+    check("O prefix mean", f64(o), prefix, 2e-2, 2e-3)
+    ref_l = np.broadcast_to(np.log(np.arange(1, N + 1)), (B, H, N))
+    check("LSE ln(i+1)", f64(lse), ref_l, 1e-5, 1e-5)
+    _, _, _, o2, lse2 = gpu_fwd(bits, False, 0.3)
+    check("O mean", f64(o2), np.broadcast_to(v64.mean(axis=1, keepdims=True), o2.shape))
+    check("LSE ln N", f64(lse2), np.full((B, H, N), math.log(N)), 1e-5, 1e-5)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_causal_row0_is_v0(d):
+    """Causal query 0 sees only key 0, so O_0 = V_0 (expected bit-exact)."""
+    announce(f"causal row0 d={d}")
+    bits = si.draw(2, 130, 3, d, 9 + d)
+    q, k, v, o, lse = gpu_fwd(bits, True, 1.0 / math.sqrt(d))
+    got = si.torch_to_bits(o)[:, 0]
+    ref = bits["v"][:, 0]
+    diff_ulps = np.abs(got.astype(np.int32) - ref.astype(np.int32))
+    assert diff_ulps.max() <= 1 and np.mean(diff_ulps == 0) > 0.99
+
+
+def test_deterministic_and_head_permutation():
+    """The forward is bit-reproducible, and permuting heads permutes outputs
+    bit-exactly (rows are independent; placement does not change the math)."""
+    import torch
+
+    B, N, H, d = 2, 700, 4, 128
+    announce("determinism + head permutation")
+    bits = si.draw(B, N, H, d, 31, backward=True)
+    q, k, v, o1, l1 = gpu_fwd(bits, True, 0.1)
+    _, _, _, o2, l2 = gpu_fwd(bits, True, 0.1)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    perm = [2, 0, 3, 1]
+    pbits = {n: np.ascontiguousarray(bits[n][:, :, perm]) for n in bits}
+    _, _, _, o3, l3 = gpu_fwd(pbits, True, 0.1)
+    assert torch.equal(o3, o1[:, :, perm]) and torch.equal(l3, l1[:, perm])
+    dq1, dk1, dv1 = gpu_bwd(q, k, v, o1, l1, bits["do"], True, 0.1)
+    dq2, dk2, dv2 = gpu_bwd(q, k, v, o1, l1, bits["do"], True, 0.1)
+    assert torch.equal(dk1, dk2) and torch.equal(dv1, dv2)
+    check("dQ repeat", f64(dq2), f64(dq1), 1e-2, 1e-4)
+
+
+def test_workspace_contents_do_not_matter():
+    import torch
+
+    B, N, H, d = 1, 513, 2, 64
+    announce("workspace garbage")
+    bits = si.draw(B, N, H, d, 41, backward=True)
+    q, k, v, o, lse = gpu_fwd(bits, False, 0.125)
+    need = fa.fa_bwd_workspace_bytes(B, N, H, d)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+    dq1, dk1, dv1 = gpu_bwd(q, k, v, o, lse, bits["do"], False, 0.125, workspace=ws)
+    dq2, dk2, dv2 = gpu_bwd(q, k, v, o, lse, bits["do"], False, 0.125)
+    assert torch.equal(dk1, dk2) and torch.equal(dv1, dv2)
+    check("dQ", f64(dq1), f64(dq2), 1e-2, 1e-4)
+
+
+# ---------------------------------------------------------------------------
+# the benchmark workloads at full size
+
+HEAD_SAMPLES = {
+    "tiny": [(0, 0), (0, 1)],
+    "short_noncausal": [(0, 0), (7, 5), (16, 9), (31, 15)],
+    "short_causal": [(0, 0), (7, 5), (16, 9), (31, 15)],
+    "mid_causal": [(0, 0), (3, 7), (7, 15)],
+    "train_causal": [(0, 0), (3, 15)],
+}
+
+
+def _heads(x, b, h):
+    return x[b : b + 1, :, h : h + 1, :]
+
+
+@pytest.mark.parametrize("name", ["tiny", "short_noncausal", "short_causal", "mid_causal"])
+def test_workload_forward(name):
+    w = si.WORKLOADS[name]
+    announce(f"workload fwd {name} B={w.B} N={w.N} H={w.H} d={w.d} causal={w.causal}")
+    bits = si.draw_workload(w)
+    q, k, v, o, lse = gpu_fwd(bits, w.causal, w.scale)
+    o_np, l_np = f64(o), f64(lse)
+    assert np.all(np.isfinite(o_np)) and np.all(np.isfinite(l_np))
+    q64, k64, v64 = (si.bf16_bits_to_f64(bits[n]) for n in ("q", "k", "v"))
+    for b, h in HEAD_SAMPLES[name]:
+        ro, rl = oracle.attention_forward(_heads(q64, b, h), _heads(k64, b, h), _heads(v64, b, h), w.causal, w.scale)
+        check(f"O head {(b, h)}", _heads(o_np, b, h), ro)
+        check(f"LSE head {(b, h)}", l_np[b : b + 1, h : h + 1], rl, LSE_TOL, LSE_TOL)
+
+
+def test_workload_long_causal_sampled_rows():
+    w = si.WORKLOADS["long_causal"]
+    announce(f"workload fwd long_causal N={w.N}")
+    bits = si.draw_workload(w)
+    q, k, v, o, lse = gpu_fwd(bits, w.causal, w.scale)
+    o_np, l_np = f64(o), f64(lse)
+    assert np.all(np.isfinite(o_np)) and np.all(np.isfinite(l_np))
+    q64, k64, v64 = (si.bf16_bits_to_f64(bits[n]) for n in ("q", "k", "v"))
+    rng = np.random.Generator(np.random.PCG64(123))
+    fixed = [0, 1, 2, 63, 64, 127, 128, 129, 4095, 8191, 8192, 12345, 16256, 16383]
+    for h in (0, 9, 15):
+        rows = sorted(set(fixed) | set(rng.integers(0, w.N, 40).tolist()))
+        ro, rl = oracle.attention_forward_rows(q64, k64, v64, True, w.scale, 0, h, rows)
+        check(f"O rows head {h}", o_np[0, rows, h, :], ro)
+        check(f"LSE rows head {h}", l_np[0, h, rows], rl, LSE_TOL, LSE_TOL)
+
+
+def test_workload_train_forward_backward():
+    w = si.WORKLOADS["train_causal"]
+    announce(f"workload fwd+bwd train_causal B={w.B} N={w.N} H={w.H}")
+    bits = si.draw_workload(w)
+    q, k, v, o, lse = gpu_fwd(bits, w.causal, w.scale)
+    dq, dk, dv = gpu_bwd(q, k, v, o, lse, bits["do"], w.causal, w.scale)
+    o_np, l_np = f64(o), f64(lse)
+    dq_np, dk_np, dv_np = f64(dq), f64(dk), f64(dv)
+    for t in (o_np, l_np, dq_np, dk_np, dv_np):
+        assert np.all(np.isfinite(t))
+    q64, k64, v64, do64 = (si.bf16_bits_to_f64(bits[n]) for n in ("q", "k", "v", "do"))
+    # invariants over every head: sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i
+    tol_sum = MAX_TOL * math.sqrt(w.N)
+    assert np.max(np.abs(dk_np.sum(axis=1))) <= tol_sum
+    assert np.max(np.abs(dv_np.sum(axis=1) - do64.sum(axis=1))) <= tol_sum
+    for b, h in HEAD_SAMPLES["train_causal"]:
+        sl = lambda x: _heads(x, b, h)
+        rq, rk, rv, ro, rl, _ = oracle.attention_backward(sl(q64), sl(k64), sl(v64), sl(do64), True, w.scale)
+        check(f"O head {(b, h)}", sl(o_np), ro)
+        check(f"LSE head {(b, h)}", l_np[b : b + 1, h : h + 1], rl, LSE_TOL, LSE_TOL)
+        check(f"dQ head {(b, h)}", sl(dq_np), rq)
+        check(f"dK head {(b, h)}", sl(dk_np), rk)
+        check(f"dV head {(b, h)}", sl(dv_np), rv)
