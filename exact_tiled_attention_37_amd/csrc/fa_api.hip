@@ -13,6 +13,7 @@ namespace {
 
 constexpr int kVersion = 100;  // 0.1.0
 constexpr int kMaxDevices = 64;
+constexpr long long kMaxElems = (1LL << 31) - (1LL << 16);
 
 // 0 = not checked yet, 1 = gfx950, 2 = something else.
 std::atomic<int> g_device_state[kMaxDevices];
@@ -36,8 +37,10 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 fa_status check_shape(int B, int N, int H, int d) {
   if (d != 64 && d != 128) return FA_ERR_HEADDIM;
   if (B < 1 || N < 1 || H < 1) return FA_ERR_SHAPE;
+  // Byte offsets within one sequence must stay well below 2^32 (buffer
+  // loads use 32-bit offsets and an out-of-range sentinel near 2^32).
   const long long elems = (long long)B * N * H * d;
-  if (elems >= (1LL << 31)) return FA_ERR_SHAPE;
+  if (elems > kMaxElems) return FA_ERR_SHAPE;
   return FA_OK;
 }
 
@@ -74,7 +77,7 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
 
 size_t fa_bwd_workspace_bytes(int B, int N, int H, int d) {
   if (check_shape(B, N, H, d) != FA_OK) return 0;
-  return fa::bwd_dq_acc_bytes(B, N, H, d) + fa::bwd_dsum_bytes(B, N, H);
+  return 2 * fa::bwd_row_bytes(B, N, H);
 }
 
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -96,7 +99,7 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
   char* ws = static_cast<char*>(workspace);
   fa::BwdArgs a{q, k, v, o, lse, dout, dq, dk, dv,
                 reinterpret_cast<float*>(ws),
-                reinterpret_cast<float*>(ws + fa::bwd_dq_acc_bytes(B, N, H, d)),
+                reinterpret_cast<float*>(ws + fa::bwd_row_bytes(B, N, H)),
                 B, N, H, softmax_scale, stream};
   return dispatch(d, causal, [&](auto D, auto C) { return fa::launch_bwd<decltype(D)::value, decltype(C)::value>(a); });
 }
@@ -105,7 +108,7 @@ const char* fa_status_string(fa_status status) {
   switch (status) {
     case FA_OK: return "ok";
     case FA_ERR_NULL: return "a required pointer is NULL";
-    case FA_ERR_SHAPE: return "invalid shape: B, N, H must be >= 1 and B*N*H*d < 2^31";
+    case FA_ERR_SHAPE: return "invalid shape: B, N, H must be >= 1 and B*N*H*d <= 2^31 - 2^16";
     case FA_ERR_HEADDIM: return "unsupported head dimension: d must be 64 or 128";
     case FA_ERR_ALIGN: return "misaligned pointer: tensors need 16 bytes, lse 4, workspace 256";
     case FA_ERR_SCALE: return "softmax_scale is not finite";

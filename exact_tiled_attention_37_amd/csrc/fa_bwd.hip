@@ -9,29 +9,37 @@
 //   P  = exp(scale * Q K^T - L)         (masked entries are 0)
 //   dV = P^T dO,  dP = dO V^T,  D = rowsum(dO * O),  dS = P * (dP - D)
 //   dQ = scale * dS K,  dK = scale * dS^T Q
-// No N x N matrix is stored: every tile of P and dS lives in registers (and
-// one 128 x 32 tile of dS in LDS) only.
+// No N x N matrix is stored anywhere: every tile of P and dS exists only in
+// registers.
 //
-// Three kernels, all on the caller's stream:
-//   1. pre-pass: D = rowsum(dO * O) per query row; zeroes the fp32 dQ
-//      accumulator (a kernel rather than a memset, so the call can be
-//      captured in a graph).
-//   2. main: one workgroup per (block of 128 keys, head, batch); each of the
-//      4 wavefronts owns 32 keys, keeps its K and V rows in registers and its
-//      dK, dV accumulators in registers, and streams 32-row blocks of Q and
-//      dO through double-buffered LDS. Per step and wave:
-//        S = Q K^T, dP = dO V^T           (lane l owns key l % 32)
-//        P, dS elementwise                (L and D per row from LDS)
-//        dV^T += dO^T P, dK^T += Q^T dS   (dO^T, Q^T by LDS transpose reads;
-//                                          P, dS straight from registers)
-//      dS is then written transposed to LDS, and the workgroup computes its
-//      contribution to dQ of the 32 rows (dS K over its 128 keys), which is
-//      added to the fp32 accumulator with hardware float atomics.
-//   3. finalize: dQ = bf16(scale * accumulator).
-// Causal: a key block only visits query blocks at or below the diagonal,
-// waves skip steps that are fully masked for their keys, and only steps on
-// the diagonal apply the mask. A negative scale negates Q on load, as in the
-// forward pass.
+// Three kernels on the caller's stream:
+//   1. pre-pass: per query row, D = rowsum(dO * O) and L * log2(e).
+//   2. dK/dV: one workgroup per (block of 128 keys, head, batch); each of the
+//      4 wavefronts owns 32 keys and keeps their K, V rows and the dK, dV
+//      accumulators in registers, while 32-row blocks of Q and dO stream
+//      through double-buffered LDS (loaded straight into LDS). Per block:
+//        S = Q K^T, dP = dO V^T            (lane l owns key l % 32)
+//        P, dS elementwise                 (L, D per row from LDS)
+//        dV^T += dO^T P, dK^T += Q^T dS    (dO^T, Q^T by LDS transpose reads)
+//   3. dQ: one workgroup per (block of 128 query rows, head, batch), laid out
+//      like the forward pass; each wave owns 32 rows and keeps their Q, dO
+//      rows and the dQ accumulator in registers while K/V tiles stream
+//      through LDS. Per tile:
+//        S^T = K Q^T, dP^T = V dO^T        (lane l owns query row l % 32)
+//        P^T, dS^T elementwise             (L, D of the lane's own row)
+//        dQ^T += K^T dS^T                  (K^T by LDS transpose reads)
+// Splitting dQ from dK/dV costs two extra products per tile pair (S and dP
+// are formed in both kernels) but needs no atomics, no fp32 dQ accumulator in
+// memory, no exchange of dS through LDS and no cross-workgroup
+// synchronisation, and dQ comes out deterministic.
+//
+// Rows past the end of the sequence are read as zeros (buffer range check).
+// They then contribute nothing: a zero Q or dO row makes that row's terms of
+// dK and dV vanish, and a zero K row makes its term of dQ vanish; outputs of
+// such rows are not stored. Causal: only blocks at or below the diagonal are
+// visited, waves skip fully masked blocks, only diagonal blocks are masked.
+// A negative scale is handled by negating the register-resident operand (K
+// in dK/dV, Q in dQ) so that the scores keep the caller's sign.
 
 #include "fa_common.hpp"
 #include "fa_launch.hpp"
@@ -40,17 +48,20 @@ namespace fa {
 
 namespace {
 
-constexpr int kBwdBKV = 128;  // keys per workgroup (4 waves x 32)
-constexpr int kBwdBQ = 32;    // query rows per step
 constexpr int kBwdThreads = 256;
+constexpr int kKvBlock = 128;  // keys per dK/dV workgroup (4 waves x 32)
+constexpr int kQStep = 32;     // query rows per dK/dV step
+constexpr int kQBlock = 128;   // query rows per dQ workgroup (4 waves x 32)
+constexpr int kKTile = 64;     // keys per dQ tile
 
 // ---------------------------------------------------------------------------
-// 1. D = rowsum(dO * O); zero the dQ accumulator. Eight lanes per token row.
+// 1. D = rowsum(dO * O) and L * log2(e), [B, H, N] each. Eight lanes per row.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16* __restrict__ O,
                                                        const bf16* __restrict__ dO,
-                                                       float* __restrict__ dsum,
-                                                       float* __restrict__ dq_acc, int N, int H,
+                                                       const float* __restrict__ LSE,
+                                                       float* __restrict__ lse2,
+                                                       float* __restrict__ dsum, int N, int H,
                                                        long rows) {
   constexpr int PER = D / 8;  // elements per lane
   const long t = (long)blockIdx.x * blockDim.x + threadIdx.x;
@@ -74,31 +85,30 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16* __restrict__ O
     const int h = (int)(r - bn * H);
     const long b = bn / N;
     const long n = bn - b * N;
-    dsum[(b * H + h) * N + n] = acc;
+    const long i = (b * H + h) * N + n;
+    dsum[i] = acc;
+    lse2[i] = LSE[i] * kLog2e;
   }
-#pragma unroll
-  for (int c = 0; c < PER / 4; ++c)
-    *reinterpret_cast<f32x4*>(dq_acc + off + 4 * c) = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
 // ---------------------------------------------------------------------------
-// 2. Main kernel.
+// 2. dK, dV.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kBwdThreads) void bwd_main_kernel(
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dkdv_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dsum,
-    float* __restrict__ dQacc, bf16* __restrict__ dK, bf16* __restrict__ dV, int N, int H,
-    int nkb, int total_blocks, float c2, uint32_t q_sign, float dk_scale) {
+    const bf16* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ dsum,
+    bf16* __restrict__ dK, bf16* __restrict__ dV, int N, int H, int nkb, int total_blocks,
+    float c2, uint32_t k_sign, float dk_scale) {
   constexpr int CH = D / 8;
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
-  constexpr int QT = kBwdBQ * D * 2;          // bytes of one Q or dO tile
-  constexpr int KT = kBwdBKV * D * 2;         // bytes of the K tile
-  constexpr int ST = kBwdBKV * kBwdBQ * 2;    // bytes of the dS^T tile
-  constexpr int QLOADS = kBwdBQ * CH / kBwdThreads;
-  constexpr int KLOADS = kBwdBKV * CH / kBwdThreads;
-  __shared__ __attribute__((aligned(16))) char smem[4 * QT + KT + ST];
-  __shared__ __attribute__((aligned(16))) float srow[2][2][kBwdBQ];  // [buf][L*log2e, D][row]
+  constexpr int QT = kQStep * D * 2;            // bytes of one Q or dO tile
+  constexpr int DMA_PER_WAVE = QT / 1024 / 4;   // 1 KiB wave loads per tile per wave
+  __shared__ __attribute__((aligned(1024))) char buf0[2 * QT];  // Q tile, then dO tile
+  __shared__ __attribute__((aligned(1024))) char buf1[2 * QT];
+  __shared__ __attribute__((aligned(256))) float row0[2 * 64];  // L*log2e, then D
+  __shared__ __attribute__((aligned(256))) float row1[2 * 64];
+  __shared__ __attribute__((aligned(1024))) char vblk[kKvBlock * D * 2];  // this block's V rows
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -108,83 +118,62 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_main_kernel(
   const int head = logical / nkb;
   const int kblk = logical - head * nkb;  // block 0 has the most causal work: it goes first
   const int b = head / H, h = head - b * H;
-  const long tok = (long)H * D;
-  const long base = ((long)b * N * H + h) * D;
-  const bf16* Qh = Q + base;
-  const bf16* Kh = K + base;
-  const bf16* Vh = V + base;
-  const bf16* dOh = dO + base;
-  const float* Lh = LSE + (long)head * N;
-  const float* Dh = Dsum + (long)head * N;
+  const long hoff = ((long)b * N * H + h) * D;
+  const uint32_t tokb = (uint32_t)H * D * 2;
+  const uint32_t nrec = (uint32_t)(N - 1) * tokb + D * 2;
+  const auto rq = make_rsrc(Q + hoff, nrec);
+  const auto rdo = make_rsrc(dO + hoff, nrec);
+  const auto rl = make_rsrc(lse2 + (long)head * N, (uint32_t)N * 4);
+  const auto rd = make_rsrc(dsum + (long)head * N, (uint32_t)N * 4);
 
-  const int kb0 = kblk * kBwdBKV;
+  const int kb0 = kblk * kKvBlock;
   const int kw0 = kb0 + 32 * wave;
   const int mykey = kw0 + l32;
 
-  char* const ktile = smem + 4 * QT;
-  char* const stile = ktile + KT;
-
-  // This wave's K and V rows as B operands of S = Q K^T and dP = dO V^T.
-  bf16x8 kf[KS], vf[KS];
+  // This wave's K rows as B operands of S = Q K^T (registers), and the
+  // block's V rows (LDS, read as B operands of dP = dO V^T).
+  bf16x8 kf[KS];
+  {
+    const auto rk = make_rsrc(K + hoff, nrec);
+    const uint32_t koff = mykey < N ? (uint32_t)mykey * tokb + 16 * g : kOobOffset;
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
-    if (mykey < N) {
-      x = *reinterpret_cast<const u32x4*>(Kh + mykey * tok + 16 * ks + 8 * g);
-      y = *reinterpret_cast<const u32x4*>(Vh + mykey * tok + 16 * ks + 8 * g);
+    for (int ks = 0; ks < KS; ++ks) kf[ks] = __builtin_bit_cast(bf16x8, buf_load16(rk, koff + 32 * ks) ^ k_sign);
+    const auto rv = make_rsrc(V + hoff, nrec);
+    constexpr int VLOADS = kKvBlock * D * 2 / 1024 / 4;
+#pragma unroll
+    for (int t = 0; t < VLOADS; ++t) {
+      const int p = 64 * (wave + 4 * t) + lane;
+      const int row = p / CH, pc = p % CH;
+      const int key = kb0 + row;
+      const uint32_t off = key < N ? (uint32_t)key * tokb + (uint32_t)(pc ^ swz<D>(row)) * 16 : kOobOffset;
+      buf_load16_lds(rv, vblk + 1024 * (wave + 4 * t), off);
     }
-    kf[ks] = __builtin_bit_cast(bf16x8, x);
-    vf[ks] = __builtin_bit_cast(bf16x8, y);
-  }
-  // The whole key block in LDS, for the dQ product.
-#pragma unroll
-  for (int p = 0; p < KLOADS; ++p) {
-    const int cidx = tid + kBwdThreads * p;
-    const int row = cidx / CH, c = cidx % CH;
-    const int key = kb0 + row;
-    u32x4 x = {0u, 0u, 0u, 0u};
-    if (key < N) x = *reinterpret_cast<const u32x4*>(Kh + key * tok + c * 8);
-    lds_write16(ktile, tile_off<D>(row, c), x);
   }
 
-  const int nqs = (N + kBwdBQ - 1) / kBwdBQ;
-  const int qs_begin = CAUSAL ? kb0 / kBwdBQ : 0;
-
-  u32x4 qreg[QLOADS], doreg[QLOADS];
-  float rowv = 0.f;
-  auto gload = [&](int step) {
+  int dma_row[DMA_PER_WAVE];
+  uint32_t dma_col[DMA_PER_WAVE];
 #pragma unroll
-    for (int p = 0; p < QLOADS; ++p) {
-      const int cidx = tid + kBwdThreads * p;
-      const int row = cidx / CH, c = cidx % CH;
-      const int q = step * kBwdBQ + row;
-      if (q < N) {
-        qreg[p] = *reinterpret_cast<const u32x4*>(Qh + q * tok + c * 8) ^ q_sign;
-        doreg[p] = *reinterpret_cast<const u32x4*>(dOh + q * tok + c * 8);
-      } else {
-        qreg[p] = u32x4{0u, 0u, 0u, 0u};
-        doreg[p] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-    if (tid < 2 * kBwdBQ) {
-      const int q = step * kBwdBQ + (tid & (kBwdBQ - 1));
-      if (tid < kBwdBQ)
-        rowv = (q < N) ? Lh[q] * kLog2e : INFINITY;  // P = 0 for rows past the end
-      else
-        rowv = (q < N) ? Dh[q] : 0.f;
-    }
-  };
-  auto swrite = [&](int buf) {
-    char* qt = smem + buf * 2 * QT;
-    char* dot = qt + QT;
+  for (int t = 0; t < DMA_PER_WAVE; ++t) {
+    const int p = 64 * (wave + 4 * t) + lane;
+    const int row = p / CH, pc = p % CH;
+    dma_row[t] = row;
+    dma_col[t] = (uint32_t)(pc ^ swz<D>(row)) * 16;
+  }
+  auto issue = [&](int step, char* dst, float* rows) {
+    const int q0 = step * kQStep;
 #pragma unroll
-    for (int p = 0; p < QLOADS; ++p) {
-      const int cidx = tid + kBwdThreads * p;
-      const int row = cidx / CH, c = cidx % CH;
-      lds_write16(qt, tile_off<D>(row, c), qreg[p]);
-      lds_write16(dot, tile_off<D>(row, c), doreg[p]);
+    for (int t = 0; t < DMA_PER_WAVE; ++t) {
+      const int q = q0 + dma_row[t];
+      const uint32_t off = q < N ? (uint32_t)q * tokb + dma_col[t] : kOobOffset;
+      char* l = dst + 1024 * (wave + 4 * t);
+      buf_load16_lds(rq, l, off);
+      buf_load16_lds(rdo, l + QT, off);
     }
-    if (tid < 2 * kBwdBQ) srow[buf][tid / kBwdBQ][tid & (kBwdBQ - 1)] = rowv;
+    if (wave == 0) {  // 64 row terms per load; the 32 past this step are unused
+      const uint32_t off = (uint32_t)(q0 + lane) * 4;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (FA_LDS void*)rows, 4, (int)off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (FA_LDS void*)(rows + 64), 4, (int)off, 0, 0, 0);
+    }
   };
 
   f32x16 dvacc[DB], dkacc[DB];
@@ -194,110 +183,73 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_main_kernel(
     dkacc[i] = f32x16{};
   }
 
-  if (qs_begin < nqs) {
-    gload(qs_begin);
-    swrite(0);
-  }
-  __syncthreads();
-
-  for (int step = qs_begin; step < nqs; ++step) {
-    const int buf = (step - qs_begin) & 1;
-    if (step + 1 < nqs) gload(step + 1);
-    const int q0 = step * kBwdBQ;
-    const char* qt = smem + buf * 2 * QT;
+  auto compute = [&](int step, const char* qt, const float* rows) {
+    const int q0 = step * kQStep;
+    if (CAUSAL && kw0 > q0 + kQStep - 1) return;  // wave-uniform: all of its keys are masked
     const char* dot = qt + QT;
-    const float* l2 = srow[buf][0];
-    const float* dd = srow[buf][1];
-
-    const bool active = !CAUSAL || kw0 <= q0 + kBwdBQ - 1;  // wave-uniform
-    if (active) {
-      f32x16 s = f32x16{}, dp = f32x16{};
+    f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        s = mfma32(read_row8<D>(qt, l32, 2 * ks + g), kf[ks], s);
-        dp = mfma32(read_row8<D>(dot, l32, 2 * ks + g), vf[ks], dp);
-      }
-      const bool need_mask = (CAUSAL && kw0 + 31 > q0) || (kw0 + 32 > N);
-      f32x16 pv, dsv;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qi = 8 * (r >> 2) + 4 * g + (r & 3);
-        float p = fast_exp2(__builtin_fmaf(s[r], c2, -l2[qi]));
-        if (need_mask && ((CAUSAL && mykey > q0 + qi) || mykey >= N)) p = 0.f;
-        pv[r] = p;
-        dsv[r] = p * (dp[r] - dd[qi]);
-      }
-      bf16x8 pb[2], dsb[2];
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        f32x8 a, c;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          a[e] = pv[8 * hh + e];
-          c[e] = dsv[8 * hh + e];
-        }
-        pb[hh] = to_bf16x8(a);
-        dsb[hh] = to_bf16x8(c);
-      }
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const int col0 = 32 * db + 16 * (G & 1);
-          const bf16x8 a_do = read_col8<D>(dot, 16 * hh + 4 * g, 16 * hh + 8 + 4 * g, col0, lane);
-          dvacc[db] = mfma32(a_do, pb[hh], dvacc[db]);
-          const bf16x8 a_q = read_col8<D>(qt, 16 * hh + 4 * g, 16 * hh + 8 + 4 * g, col0, lane);
-          dkacc[db] = mfma32(a_q, dsb[hh], dkacc[db]);
-        }
-      // dS^T rows of this wave's keys: row = key, columns = the 32 query rows.
-#pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        const bf16x4 v4 = to_bf16x4(f32x4{dsv[4 * rq], dsv[4 * rq + 1], dsv[4 * rq + 2], dsv[4 * rq + 3]});
-        lds_write8(stile, tile_off<32>(32 * wave + l32, rq) + 8 * g, __builtin_bit_cast(u32x2, v4));
-      }
-    } else {
-#pragma unroll
-      for (int rq = 0; rq < 4; ++rq)
-        lds_write8(stile, tile_off<32>(32 * wave + l32, rq) + 8 * g, u32x2{0u, 0u});
+    for (int ks = 0; ks < KS; ++ks) {
+      s = mfma32(read_row8<D>(qt, l32, 2 * ks + g), kf[ks], s);
+      dp = mfma32(read_row8<D>(dot, l32, 2 * ks + g), read_row8<D>(vblk, 32 * wave + l32, 2 * ks + g), dp);
     }
+    const bool need_mask = CAUSAL && kw0 + 31 > q0;
+    f32x8 p8[2], ds8[2];
+#pragma unroll
+    for (int rq4 = 0; rq4 < 4; ++rq4) {
+      const int qi0 = 8 * rq4 + 4 * g;
+      const f32x4 l4 = *reinterpret_cast<const FA_LDS f32x4*>((const FA_LDS float*)rows + qi0);
+      const f32x4 d4 = *reinterpret_cast<const FA_LDS f32x4*>((const FA_LDS float*)rows + 64 + qi0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * rq4 + e;
+        float p = fast_exp2(__builtin_fmaf(s[r], c2, -l4[e]));
+        if (need_mask && mykey > q0 + qi0 + e) p = 0.f;
+        p8[r >> 3][r & 7] = p;
+        ds8[r >> 3][r & 7] = p * (dp[r] - d4[e]);
+      }
+    }
+    const bf16x8 pb[2] = {to_bf16x8(p8[0]), to_bf16x8(p8[1])};
+    const bf16x8 dsb[2] = {to_bf16x8(ds8[0]), to_bf16x8(ds8[1])};
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int col0 = 32 * db + 16 * (G & 1);
+        dvacc[db] = mfma32(read_col8<D>(dot, 16 * hh + 4 * g, 16 * hh + 8 + 4 * g, col0, lane), pb[hh], dvacc[db]);
+        dkacc[db] = mfma32(read_col8<D>(qt, 16 * hh + 4 * g, 16 * hh + 8 + 4 * g, col0, lane), dsb[hh], dkacc[db]);
+      }
+  };
+
+  const int nqs = (N + kQStep - 1) / kQStep;
+  const int s0 = CAUSAL ? kb0 / kQStep : 0;
+  issue(s0, buf0, row0);
+  wait_vmem();
+  __syncthreads();
+  for (int step = s0; step < nqs; step += 2) {
+    if (step + 1 < nqs) issue(step + 1, buf1, row1);
+    compute(step, buf0, row0);
+    wait_vmem();
     __syncthreads();
-
-    // dQ rows q0..q0+31 += dS K over this block's keys (fp32 atomics).
-    {
-      constexpr int STEPS = (D == 128) ? 8 : 4;
-      const int db = (D == 128) ? wave : (wave & 1);
-      const int kbase = (D == 128) ? 0 : 64 * (wave >> 1);
-      f32x16 dq = f32x16{};
-#pragma unroll
-      for (int t = 0; t < STEPS; ++t) {
-        const int kr = kbase + 16 * t;
-        const bf16x8 a = read_col8<32>(stile, kr + 4 * g, kr + 8 + 4 * g, 16 * (G & 1), lane);
-        const bf16x8 bk = read_col8<D>(ktile, kr + 4 * g, kr + 8 + 4 * g, 32 * db + 16 * (G & 1), lane);
-        dq = mfma32(a, bk, dq);
-      }
-      float* dqh = dQacc + base + 32 * db + l32;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int q = q0 + 8 * (r >> 2) + 4 * g + (r & 3);
-        if (q < N) unsafeAtomicAdd(dqh + q * tok, dq[r]);
-      }
-    }
-    if (step + 1 < nqs) swrite(buf ^ 1);
+    if (step + 1 >= nqs) break;
+    if (step + 2 < nqs) issue(step + 2, buf0, row0);
+    compute(step + 1, buf1, row1);
+    wait_vmem();
     __syncthreads();
   }
 
   if (mykey < N) {
-    bf16* dkrow = dK + base + mykey * tok;
-    bf16* dvrow = dV + base + mykey * tok;
+    bf16* dkrow = dK + hoff + (long)mykey * H * D;
+    bf16* dvrow = dV + hoff + (long)mykey * H * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        const int d0 = 32 * db + 8 * rq + 4 * g;
-        const f32x4 k4 = {dkacc[db][4 * rq] * dk_scale, dkacc[db][4 * rq + 1] * dk_scale,
-                          dkacc[db][4 * rq + 2] * dk_scale, dkacc[db][4 * rq + 3] * dk_scale};
-        const f32x4 v4 = {dvacc[db][4 * rq], dvacc[db][4 * rq + 1], dvacc[db][4 * rq + 2],
-                          dvacc[db][4 * rq + 3]};
+      for (int rq4 = 0; rq4 < 4; ++rq4) {
+        const int d0 = 32 * db + 8 * rq4 + 4 * g;
+        const f32x4 k4 = {dkacc[db][4 * rq4] * dk_scale, dkacc[db][4 * rq4 + 1] * dk_scale,
+                          dkacc[db][4 * rq4 + 2] * dk_scale, dkacc[db][4 * rq4 + 3] * dk_scale};
+        const f32x4 v4 = {dvacc[db][4 * rq4], dvacc[db][4 * rq4 + 1], dvacc[db][4 * rq4 + 2],
+                          dvacc[db][4 * rq4 + 3]};
         *reinterpret_cast<bf16x4*>(dkrow + d0) = to_bf16x4(k4);
         *reinterpret_cast<bf16x4*>(dvrow + d0) = to_bf16x4(v4);
       }
@@ -305,17 +257,148 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_main_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// 3. dQ = bf16(scale * accumulator), 8 elements per thread.
-__global__ __launch_bounds__(256) void bwd_finalize_kernel(const float* __restrict__ acc,
-                                                            bf16* __restrict__ dq, float scale,
-                                                            long n8) {
-  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n8) return;
-  const f32x4 a = *reinterpret_cast<const f32x4*>(acc + 8 * i);
-  const f32x4 c = *reinterpret_cast<const f32x4*>(acc + 8 * i + 4);
-  const f32x8 x = {a[0] * scale, a[1] * scale, a[2] * scale, a[3] * scale,
-                   c[0] * scale, c[1] * scale, c[2] * scale, c[3] * scale};
-  *reinterpret_cast<bf16x8*>(dq + 8 * i) = to_bf16x8(x);
+// 3. dQ.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_kernel(
+    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+    const bf16* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ dsum,
+    bf16* __restrict__ dQ, int N, int H, int nqb, int total_blocks, float c2, uint32_t q_sign,
+    float dq_scale) {
+  constexpr int CH = D / 8;
+  constexpr int KS = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int TILE = kKTile * D * 2;          // bytes of one K or V tile
+  constexpr int DMA_PER_WAVE = TILE / 1024 / 4;
+  __shared__ __attribute__((aligned(1024))) char kv0[2 * TILE];  // K tile, then V tile
+  __shared__ __attribute__((aligned(1024))) char kv1[2 * TILE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5, l32 = lane & 31, G = lane >> 4;
+
+  const int logical = xcd_remap(blockIdx.x, total_blocks);
+  const int head = logical / nqb;
+  const int qblk = nqb - 1 - (logical - head * nqb);  // longest causal rows first
+  const int b = head / H, h = head - b * H;
+  const long hoff = ((long)b * N * H + h) * D;
+  const uint32_t tokb = (uint32_t)H * D * 2;
+  const uint32_t nrec = (uint32_t)(N - 1) * tokb + D * 2;
+  const auto rk = make_rsrc(K + hoff, nrec);
+  const auto rv = make_rsrc(V + hoff, nrec);
+
+  const int qw0 = qblk * kQBlock + wave * 32;
+  const int myq = qw0 + l32;
+
+  // This wave's Q and dO rows as B operands of S^T = K Q^T and dP^T = V dO^T.
+  bf16x8 qf[KS], dof[KS];
+  float l2 = 0.f, dd = 0.f;
+  {
+    const auto rq = make_rsrc(Q + hoff, nrec);
+    const auto rdo = make_rsrc(dO + hoff, nrec);
+    const uint32_t qoff = myq < N ? (uint32_t)myq * tokb + 16 * g : kOobOffset;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      qf[ks] = __builtin_bit_cast(bf16x8, buf_load16(rq, qoff + 32 * ks) ^ q_sign);
+      dof[ks] = __builtin_bit_cast(bf16x8, buf_load16(rdo, qoff + 32 * ks));
+    }
+    if (myq < N) {
+      l2 = lse2[(long)head * N + myq];
+      dd = dsum[(long)head * N + myq];
+    }
+  }
+
+  int dma_row[DMA_PER_WAVE];
+  uint32_t dma_col[DMA_PER_WAVE];
+#pragma unroll
+  for (int t = 0; t < DMA_PER_WAVE; ++t) {
+    const int p = 64 * (wave + 4 * t) + lane;
+    const int row = p / CH, pc = p % CH;
+    dma_row[t] = row;
+    dma_col[t] = (uint32_t)(pc ^ swz<D>(row)) * 16;
+  }
+  auto issue = [&](int tile, char* dst) {
+#pragma unroll
+    for (int t = 0; t < DMA_PER_WAVE; ++t) {
+      const int key = tile * kKTile + dma_row[t];
+      const uint32_t off = key < N ? (uint32_t)key * tokb + dma_col[t] : kOobOffset;
+      char* l = dst + 1024 * (wave + 4 * t);
+      buf_load16_lds(rk, l, off);
+      buf_load16_lds(rv, l + TILE, off);
+    }
+  };
+
+  f32x16 dqacc[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) dqacc[i] = f32x16{};
+
+  auto compute = [&](int j, const char* kt) {
+    const int key0 = j * kKTile;
+    if (CAUSAL && key0 > qw0 + 31) return;
+    const char* vt = kt + TILE;
+    const bool need_mask = CAUSAL && key0 + kKTile - 1 > qw0;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        s = mfma32(read_row8<D>(kt, kb * 32 + l32, 2 * ks + g), qf[ks], s);
+        dp = mfma32(read_row8<D>(vt, kb * 32 + l32, 2 * ks + g), dof[ks], dp);
+      }
+      bf16x8 dsf[2];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        f32x8 x;
+#pragma unroll
+        for (int s8 = 0; s8 < 8; ++s8) {
+          const int r = 8 * hh + s8;
+          float p = fast_exp2(__builtin_fmaf(s[r], c2, -l2));
+          if (need_mask) {
+            const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+            if (key > myq) p = 0.f;
+          }
+          x[s8] = p * (dp[r] - dd);
+        }
+        dsf[hh] = to_bf16x8(x);
+      }
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const int kr = 32 * kb + 16 * hh;
+          const bf16x8 a = read_col8<D>(kt, kr + 4 * g, kr + 8 + 4 * g, 32 * db + 16 * (G & 1), lane);
+          dqacc[db] = mfma32(a, dsf[hh], dqacc[db]);
+        }
+    }
+  };
+
+  const int kv_len = CAUSAL ? min(N, (qblk + 1) * kQBlock) : N;
+  const int ntiles = (kv_len + kKTile - 1) / kKTile;
+  issue(0, kv0);
+  wait_vmem();
+  __syncthreads();
+  for (int j = 0; j < ntiles; j += 2) {
+    if (j + 1 < ntiles) issue(j + 1, kv1);
+    compute(j, kv0);
+    wait_vmem();
+    __syncthreads();
+    if (j + 1 >= ntiles) break;
+    if (j + 2 < ntiles) issue(j + 2, kv0);
+    compute(j + 1, kv1);
+    wait_vmem();
+    __syncthreads();
+  }
+
+  if (myq < N) {
+    bf16* qrow = dQ + hoff + (long)myq * H * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int rq4 = 0; rq4 < 4; ++rq4) {
+        const f32x4 x = {dqacc[db][4 * rq4] * dq_scale, dqacc[db][4 * rq4 + 1] * dq_scale,
+                         dqacc[db][4 * rq4 + 2] * dq_scale, dqacc[db][4 * rq4 + 3] * dq_scale};
+        *reinterpret_cast<bf16x4*>(qrow + 32 * db + 8 * rq4 + 4 * g) = to_bf16x4(x);
+      }
+  }
 }
 
 }  // namespace
@@ -323,33 +406,34 @@ __global__ __launch_bounds__(256) void bwd_finalize_kernel(const float* __restri
 template <int D, bool CAUSAL>
 hipError_t launch_bwd(const BwdArgs& a) {
   const long rows = (long)a.B * a.N * a.H;
+  const float c2 = fabsf(a.scale) * kLog2e;
+  const uint32_t sign = a.scale < 0.f ? 0x80008000u : 0u;
   {
-    const long threads = rows * 8;
-    const unsigned grid = (unsigned)((threads + 255) / 256);
+    const unsigned grid = (unsigned)((rows * 8 + 255) / 256);
     hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3(grid), dim3(256), 0, a.stream,
-                       static_cast<const bf16*>(a.o), static_cast<const bf16*>(a.dout), a.dsum,
-                       a.dq_acc, a.N, a.H, rows);
+                       static_cast<const bf16*>(a.o), static_cast<const bf16*>(a.dout), a.lse,
+                       a.lse2, a.dsum, a.N, a.H, rows);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   {
-    const int nkb = (a.N + kBwdBKV - 1) / kBwdBKV;
+    const int nkb = (a.N + kKvBlock - 1) / kKvBlock;
     const int total = a.B * a.H * nkb;
-    const float c2 = fabsf(a.scale) * kLog2e;
-    const uint32_t q_sign = a.scale < 0.f ? 0x80008000u : 0u;
-    hipLaunchKernelGGL((bwd_main_kernel<D, CAUSAL>), dim3(total), dim3(kBwdThreads), 0, a.stream,
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(total), dim3(kBwdThreads), 0, a.stream,
                        static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k),
-                       static_cast<const bf16*>(a.v), static_cast<const bf16*>(a.dout), a.lse,
-                       a.dsum, a.dq_acc, static_cast<bf16*>(a.dk), static_cast<bf16*>(a.dv), a.N,
-                       a.H, nkb, total, c2, q_sign, fabsf(a.scale));
+                       static_cast<const bf16*>(a.v), static_cast<const bf16*>(a.dout), a.lse2,
+                       a.dsum, static_cast<bf16*>(a.dk), static_cast<bf16*>(a.dv), a.N, a.H, nkb,
+                       total, c2, sign, a.scale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   {
-    const long n8 = rows * D / 8;
-    const unsigned grid = (unsigned)((n8 + 255) / 256);
-    hipLaunchKernelGGL(bwd_finalize_kernel, dim3(grid), dim3(256), 0, a.stream, a.dq_acc,
-                       static_cast<bf16*>(a.dq), a.scale, n8);
+    const int nqb = (a.N + kQBlock - 1) / kQBlock;
+    const int total = a.B * a.H * nqb;
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(total), dim3(kBwdThreads), 0, a.stream,
+                       static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k),
+                       static_cast<const bf16*>(a.v), static_cast<const bf16*>(a.dout), a.lse2,
+                       a.dsum, static_cast<bf16*>(a.dq), a.N, a.H, nqb, total, c2, sign, a.scale);
     return hipGetLastError();
   }
 }

@@ -124,6 +124,30 @@ __device__ __forceinline__ bf16x4 to_bf16x4(f32x4 x) { return __builtin_convertv
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Buffer resource over `nbytes` bytes starting at `base`. Loads whose byte
+// offset falls outside [0, nbytes) return zeros (the hardware range check),
+// which is how rows past the end of a sequence are read.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes, 0x00020000);
+}
+// An offset that is outside every resource made above (nbytes < 2^32 - 16).
+constexpr uint32_t kOobOffset = 0xFFFFFFF0u;
+
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+
+// 16 bytes per lane straight from memory into LDS (no registers): lane i of
+// the wave writes LDS bytes [lds + 16 i, lds + 16 i + 16). `lds` must be the
+// same for the whole wave.
+__device__ __forceinline__ void buf_load16_lds(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (FA_LDS void*)lds, 16, (int)off, 0, 0, 0);
+}
+
+// s_waitcnt vmcnt(0): all of this wave's vector memory loads (including the
+// ones that write LDS directly) have completed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // Blocks are dispatched round-robin over the XCDs (block i goes to XCD i % 8).
 // Remap so that each XCD receives one contiguous range of logical blocks:
 // consecutive logical blocks (the query blocks of one head) then share an L2.

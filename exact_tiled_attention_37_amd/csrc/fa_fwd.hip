@@ -12,15 +12,24 @@
 // so long sequences with few heads still fill the chip; inside a workgroup
 // each of the 4 wavefronts owns 32 query rows and all of them share the K/V
 // tiles staged in LDS, so no partial results are exchanged between waves.
+// Two workgroups share a CU (8 waves, 2 per SIMD), so one wave's softmax
+// arithmetic overlaps the other's matrix instructions.
 //
-// Per wave and K/V tile (64 keys):
+// K/V tiles (64 keys) move from memory straight into LDS with buffer loads
+// that write LDS directly (no register staging), double-buffered: the next
+// tile streams in while the current one is used. Rows past the end of the
+// sequence come back as zeros from the buffer range check.
+//
+// Per wave and tile:
 //   S^T = K Q^T     (MFMA; lane l owns query row l % 32, so a row's scores
 //                    sit in two lanes: l and l ^ 32)
 //   online softmax in the log2 domain: c2 = |scale| * log2(e) is folded into
-//   one FMA per score before exp2; the row max and the rescale factor need a
-//   single cross-half exchange; the running sum stays per lane and is only
-//   combined in the epilogue; the division by the row sum is deferred to the
-//   epilogue.
+//   one FMA per score before exp2; the row max needs a single cross-half
+//   exchange; the running sum stays per lane until the epilogue; the
+//   division by the row sum is deferred to the epilogue; and the running
+//   max (with the rescale of the partial output) is only moved when a row's
+//   max grows by more than 2^8, which keeps every exponent <= 8 while
+//   skipping almost all rescales.
 //   O^T += V^T P^T  (MFMA; P^T is taken straight from the S^T accumulator
 //                    registers, V^T is read with LDS transpose loads)
 // Causal masking: tiles entirely above the diagonal are never visited, and a
@@ -38,155 +47,154 @@ namespace {
 constexpr int kFwdBR = 128;     // query rows per workgroup
 constexpr int kFwdBC = 64;      // keys per K/V tile
 constexpr int kFwdThreads = 256;
+constexpr float kRescaleSlack = 8.f;  // log2 units a row max may exceed the running max
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kFwdThreads) void fwd_kernel(
+__global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     bf16* __restrict__ O, float* __restrict__ LSE, int N, int H, int nqb, int total_blocks,
     float c2, uint32_t q_sign) {
   constexpr int CH = D / 8;                        // 16-byte chunks per row
   constexpr int TILE = kFwdBC * D * 2;             // bytes of one K or V tile
-  constexpr int LOADS = kFwdBC * CH / kFwdThreads; // 16-byte loads per thread per tile
+  constexpr int DMA_PER_WAVE = TILE / 1024 / 4;    // 1 KiB wave loads per tile per wave
   constexpr int KS = D / 16;                       // MFMA k-steps over d
   constexpr int DB = D / 32;                       // 32-wide output column blocks
-  __shared__ __attribute__((aligned(16))) char smem[2 * 2 * TILE];
+  __shared__ __attribute__((aligned(1024))) char kv0[2 * TILE];  // K tile, then V tile
+  __shared__ __attribute__((aligned(1024))) char kv1[2 * TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int g = lane >> 5, l32 = lane & 31;
+  const int g = lane >> 5, l32 = lane & 31, G = lane >> 4;
 
   const int logical = xcd_remap(blockIdx.x, total_blocks);
   const int head = logical / nqb;                  // b * H + h
   const int qblk = nqb - 1 - (logical - head * nqb);  // longest causal rows first
   const int b = head / H, h = head - b * H;
-  const long tok = (long)H * D;                    // elements between tokens
-  const long base = ((long)b * N * H + h) * D;
-  const bf16* Qh = Q + base;
-  const bf16* Kh = K + base;
-  const bf16* Vh = V + base;
+  const long hoff = ((long)b * N * H + h) * D;     // element offset of token 0
+  const uint32_t tokb = (uint32_t)H * D * 2;       // bytes between tokens
+  const uint32_t nrec = (uint32_t)(N - 1) * tokb + D * 2;
+  const auto rq = make_rsrc(Q + hoff, nrec);
+  const auto rk = make_rsrc(K + hoff, nrec);
+  const auto rv = make_rsrc(V + hoff, nrec);
 
   const int qw0 = qblk * kFwdBR + wave * 32;       // first query row of this wave
   const int myq = qw0 + l32;
 
   // Q as the B operand of S^T = K Q^T: row myq, d = 16*ks + 8*g .. +7.
   bf16x8 qf[KS];
+  {
+    const uint32_t qoff = myq < N ? (uint32_t)myq * tokb + 16 * g : kOobOffset;
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    u32x4 x = {0u, 0u, 0u, 0u};
-    if (myq < N) x = *reinterpret_cast<const u32x4*>(Qh + myq * tok + 16 * ks + 8 * g);
-    x ^= q_sign;
-    qf[ks] = __builtin_bit_cast(bf16x8, x);
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, buf_load16(rq, qoff + 32 * ks) ^ q_sign);
   }
+
+  // LDS-DMA source offsets: wave load u = wave + 4 t fills LDS bytes
+  // [1024 u, 1024 u + 1024) of a tile; lane i fills chunk position 64 u + i.
+  int dma_row[DMA_PER_WAVE];
+  uint32_t dma_col[DMA_PER_WAVE];
+#pragma unroll
+  for (int t = 0; t < DMA_PER_WAVE; ++t) {
+    const int p = 64 * (wave + 4 * t) + lane;
+    const int row = p / CH, pc = p % CH;
+    dma_row[t] = row;
+    dma_col[t] = (uint32_t)(pc ^ swz<D>(row)) * 16;
+  }
+  auto issue = [&](int tile, char* dst) {
+#pragma unroll
+    for (int t = 0; t < DMA_PER_WAVE; ++t) {
+      const int key = tile * kFwdBC + dma_row[t];
+      const uint32_t off = key < N ? (uint32_t)key * tokb + dma_col[t] : kOobOffset;
+      char* l = dst + 1024 * (wave + 4 * t);
+      buf_load16_lds(rk, l, off);
+      buf_load16_lds(rv, l + TILE, off);
+    }
+  };
 
   const int kv_len = CAUSAL ? min(N, (qblk + 1) * kFwdBR) : N;
   const int ntiles = (kv_len + kFwdBC - 1) / kFwdBC;
 
-  u32x4 kreg[LOADS], vreg[LOADS];
-  auto gload = [&](int tile) {
-#pragma unroll
-    for (int p = 0; p < LOADS; ++p) {
-      const int cidx = tid + kFwdThreads * p;
-      const int row = cidx / CH, c = cidx % CH;
-      const int key = tile * kFwdBC + row;
-      if (key < N) {
-        kreg[p] = *reinterpret_cast<const u32x4*>(Kh + key * tok + c * 8);
-        vreg[p] = *reinterpret_cast<const u32x4*>(Vh + key * tok + c * 8);
-      } else {
-        kreg[p] = u32x4{0u, 0u, 0u, 0u};
-        vreg[p] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-  };
-  auto swrite = [&](int buf) {
-    char* kt = smem + buf * 2 * TILE;
-    char* vt = kt + TILE;
-#pragma unroll
-    for (int p = 0; p < LOADS; ++p) {
-      const int cidx = tid + kFwdThreads * p;
-      const int row = cidx / CH, c = cidx % CH;
-      lds_write16(kt, tile_off<D>(row, c), kreg[p]);
-      lds_write16(vt, tile_off<D>(row, c), vreg[p]);
-    }
-  };
-
-  gload(0);
-  swrite(0);
-  __syncthreads();
-
   f32x16 oacc[DB];
 #pragma unroll
   for (int i = 0; i < DB; ++i) oacc[i] = f32x16{};
-  float m_run = -INFINITY;  // running max of c2 * score (log2 domain)
+  float m_run = -INFINITY;  // running max of c2 * score (log2 domain), possibly stale by <= 8
   float l_run = 0.f;        // this lane's share of the running sum
 
-  for (int j = 0; j < ntiles; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < ntiles) gload(j + 1);
+  auto compute = [&](int j, const char* kt) {
     const int key0 = j * kFwdBC;
-    const bool active = !CAUSAL || key0 <= qw0 + 31;  // wave-uniform
-    if (active) {
-      const char* kt = smem + buf * 2 * TILE;
-      const char* vt = kt + TILE;
-      f32x16 s[2];
+    if (CAUSAL && key0 > qw0 + 31) return;  // wave-uniform: fully masked for this wave
+    const char* vt = kt + TILE;
+    f32x16 s[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = f32x16{};
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = f32x16{};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          s[kb] = mfma32(read_row8<D>(kt, kb * 32 + l32, 2 * ks + g), qf[ks], s[kb]);
-      }
-      const bool need_mask = (CAUSAL && key0 + kFwdBC - 1 > qw0) || (key0 + kFwdBC > N);
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-            const bool masked = (CAUSAL && key > myq) || key >= N;
-            if (masked) s[kb][r] = -INFINITY;
-          }
-      }
-      float mx = -INFINITY;
+      for (int ks = 0; ks < KS; ++ks)
+        s[kb] = mfma32(read_row8<D>(kt, kb * 32 + l32, 2 * ks + g), qf[ks], s[kb]);
+    }
+    const bool need_mask = (CAUSAL && key0 + kFwdBC - 1 > qw0) || (key0 + kFwdBC > N);
+    if (need_mask) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-      mx = xhalf_max(mx);
-      const float tile_m = (mx == -INFINITY) ? -INFINITY : mx * c2;
-      const float m_new = fmaxf(m_run, tile_m);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
-      m_run = m_new;
-
-      bf16x8 pf[4];
-      float lsum = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        f32x8 p;
-#pragma unroll
-        for (int s8 = 0; s8 < 8; ++s8) {
-          const float sv = s[ks >> 1][8 * (ks & 1) + s8];
-          float e = fast_exp2(__builtin_fmaf(sv, c2, -m_use));
-          if (need_mask) e = (sv == -INFINITY) ? 0.f : e;
-          p[s8] = e;
-          lsum += e;
-        }
-        pf[ks] = to_bf16x8(p);
-      }
-      l_run = l_run * alpha + lsum;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
-
-      const int G = lane >> 4;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const bf16x8 a = read_col8<D>(vt, 16 * ks + 4 * g, 16 * ks + 8 + 4 * g, 32 * db + 16 * (G & 1), lane);
-          oacc[db] = mfma32(a, pf[ks], oacc[db]);
+        for (int r = 0; r < 16; ++r) {
+          const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+          if ((CAUSAL && key > myq) || key >= N) s[kb][r] = -INFINITY;
         }
     }
-    if (j + 1 < ntiles) swrite(buf ^ 1);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    mx = xhalf_max(mx);
+    const float tile_m = (mx == -INFINITY) ? -INFINITY : mx * c2;
+    const bool grow = tile_m > m_run + kRescaleSlack;
+    if (__builtin_amdgcn_ballot_w64(grow)) {  // wave-uniform
+      const float m_new = grow ? tile_m : m_run;
+      // 0 when m_run = -inf, 1 when unchanged (and when no key was visible yet)
+      const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+
+    bf16x8 pf[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      f32x8 p;
+#pragma unroll
+      for (int s8 = 0; s8 < 8; ++s8) {
+        const float sv = s[ks >> 1][8 * (ks & 1) + s8];
+        float e = fast_exp2(__builtin_fmaf(sv, c2, -m_use));
+        if (need_mask) e = (sv == -INFINITY) ? 0.f : e;
+        p[s8] = e;
+        l_run += e;
+      }
+      pf[ks] = to_bf16x8(p);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const bf16x8 a = read_col8<D>(vt, 16 * ks + 4 * g, 16 * ks + 8 + 4 * g, 32 * db + 16 * (G & 1), lane);
+        oacc[db] = mfma32(a, pf[ks], oacc[db]);
+      }
+  };
+
+  issue(0, kv0);
+  wait_vmem();
+  __syncthreads();
+  for (int j = 0; j < ntiles; j += 2) {
+    if (j + 1 < ntiles) issue(j + 1, kv1);
+    compute(j, kv0);
+    wait_vmem();
+    __syncthreads();
+    if (j + 1 >= ntiles) break;
+    if (j + 2 < ntiles) issue(j + 2, kv0);
+    compute(j + 1, kv1);
+    wait_vmem();
     __syncthreads();
   }
 
@@ -194,14 +202,14 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_kernel(
   const float inv = 1.f / l_tot;
   if (myq < N) {
     if (g == 0) LSE[(long)head * N + myq] = (m_run + log2f(l_tot)) * kLn2;
-    bf16* orow = O + base + myq * tok;
+    bf16* orow = O + hoff + (long)myq * H * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        f32x4 x = {oacc[db][4 * rq] * inv, oacc[db][4 * rq + 1] * inv, oacc[db][4 * rq + 2] * inv,
-                   oacc[db][4 * rq + 3] * inv};
-        *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * rq + 4 * g) = to_bf16x4(x);
+      for (int rq4 = 0; rq4 < 4; ++rq4) {
+        f32x4 x = {oacc[db][4 * rq4] * inv, oacc[db][4 * rq4 + 1] * inv, oacc[db][4 * rq4 + 2] * inv,
+                   oacc[db][4 * rq4 + 3] * inv};
+        *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * rq4 + 4 * g) = to_bf16x4(x);
       }
   }
 }

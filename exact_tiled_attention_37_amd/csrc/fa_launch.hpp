@@ -27,8 +27,8 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* dq_acc;  // [B, N, H, d] fp32 workspace
-  float* dsum;    // [B, H, N]    fp32 workspace, D = rowsum(dO * O)
+  float* lse2;    // [B, H, N] fp32 workspace, L * log2(e)
+  float* dsum;    // [B, H, N] fp32 workspace, D = rowsum(dO * O)
   int B, N, H;
   float scale;
   hipStream_t stream;
@@ -40,9 +40,9 @@ hipError_t launch_fwd(const FwdArgs& a);
 template <int D, bool CAUSAL>
 hipError_t launch_bwd(const BwdArgs& a);
 
-// Workspace layout of the backward pass (both parts 256-byte aligned).
+// Workspace layout of the backward pass: L * log2(e), then D; each part is a
+// float32 [B, H, N] array starting on a 256-byte boundary.
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
-inline size_t bwd_dq_acc_bytes(long B, long N, long H, long d) { return align256(size_t(B * N * H * d) * 4); }
-inline size_t bwd_dsum_bytes(long B, long N, long H) { return align256(size_t(B * H * N) * 4); }
+inline size_t bwd_row_bytes(long B, long N, long H) { return align256(size_t(B * H * N) * 4); }
 
 }  // namespace fa

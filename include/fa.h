@@ -24,7 +24,7 @@
  *     lengths). Non-causal: every key is visible.
  *   - softmax_scale: any finite float (1/sqrt(d) is the usual choice).
  *   - Supported head dimensions: d = 64 and d = 128. Any N >= 1, B >= 1,
- *     H >= 1 with B*N*H*d < 2^31.
+ *     H >= 1 with B*N*H*d <= 2^31 - 2^16.
  *   - Work is enqueued on `stream` (0 = the null stream) and the call returns
  *     without synchronising. Device faults surface at the caller's next
  *     synchronisation. Validation happens before anything is enqueued; a
@@ -51,7 +51,7 @@ extern "C" {
 typedef enum fa_status {
     FA_OK = 0,
     FA_ERR_NULL = 1,      /* a required pointer is NULL                         */
-    FA_ERR_SHAPE = 2,     /* B, N or H < 1, or the tensors exceed 2^31 elements */
+    FA_ERR_SHAPE = 2,     /* B, N or H < 1, or B*N*H*d > 2^31 - 2^16         */
     FA_ERR_HEADDIM = 3,   /* d is not 64 or 128                                 */
     FA_ERR_ALIGN = 4,     /* a pointer is not aligned as required               */
     FA_ERR_SCALE = 5,     /* softmax_scale is not finite                        */
@@ -75,9 +75,9 @@ FA_API fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, fl
                  hipStream_t stream);
 
 /*
- * Bytes of device workspace fa_bwd needs for this problem size (a float32
- * dQ accumulator [B, N, H, d] and the float32 row terms D = rowsum(dO * O),
- * [B, H, N], each 256-byte aligned). Returns 0 for an invalid shape.
+ * Bytes of device workspace fa_bwd needs for this problem size: two float32
+ * [B, H, N] arrays (the row terms D = rowsum(dO * O) and L * log2(e)), each
+ * starting on a 256-byte boundary. Returns 0 for an invalid shape.
  */
 FA_API size_t fa_bwd_workspace_bytes(int B, int N, int H, int d);
 
