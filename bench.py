@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--cpu-heads", type=int, default=8,
                     help="heads of the workload the CPU oracle baseline runs (0 = skip)")
     ap.add_argument("--no-sweep", action="store_true", help="skip the forward sweep over the other workloads")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (3 times) so that profiler byte "
+                         "counters can be scaled against a transfer of known size")
     return ap.parse_args()
 
 
@@ -148,6 +151,16 @@ def main():
         "resident_bytes": int(resident),
         "peak_bytes_during_steps": int(peak_mem),
     }
+
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        detail["copy_calibration_bytes"] = n
+        del src, dst
 
     if not args.no_sweep:
         sweep = {}

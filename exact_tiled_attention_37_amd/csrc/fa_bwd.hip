@@ -41,6 +41,8 @@
 // A negative scale is handled by negating the register-resident operand (K
 // in dK/dV, Q in dQ) so that the scores keep the caller's sign.
 
+#include <type_traits>
+
 #include "fa_common.hpp"
 #include "fa_launch.hpp"
 
@@ -99,16 +101,17 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
     const bf16* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ dsum,
     bf16* __restrict__ dK, bf16* __restrict__ dV, int N, int H, int nkb, int total_blocks,
     float c2, uint32_t k_sign, float dk_scale) {
-  constexpr int CH = D / 8;
+  using TQ = Tile<kQStep, D>;    // one Q or dO block (rows = queries)
+  using TV = Tile<kKvBlock, D>;  // the workgroup's V rows (rows = keys)
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
-  constexpr int QT = kQStep * D * 2;            // bytes of one Q or dO tile
-  constexpr int DMA_PER_WAVE = QT / 1024 / 4;   // 1 KiB wave loads per tile per wave
+  constexpr int QT = TQ::BYTES;
+  constexpr int DMA_PER_WAVE = TQ::LOADS / 4;
   __shared__ __attribute__((aligned(1024))) char buf0[2 * QT];  // Q tile, then dO tile
   __shared__ __attribute__((aligned(1024))) char buf1[2 * QT];
   __shared__ __attribute__((aligned(256))) float row0[2 * 64];  // L*log2e, then D
   __shared__ __attribute__((aligned(256))) float row1[2 * 64];
-  __shared__ __attribute__((aligned(1024))) char vblk[kKvBlock * D * 2];  // this block's V rows
+  __shared__ __attribute__((aligned(1024))) char vblk[TV::BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -139,33 +142,23 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) kf[ks] = __builtin_bit_cast(bf16x8, buf_load16(rk, koff + 32 * ks) ^ k_sign);
     const auto rv = make_rsrc(V + hoff, nrec);
-    constexpr int VLOADS = kKvBlock * D * 2 / 1024 / 4;
 #pragma unroll
-    for (int t = 0; t < VLOADS; ++t) {
-      const int p = 64 * (wave + 4 * t) + lane;
-      const int row = p / CH, pc = p % CH;
-      const int key = kb0 + row;
-      const uint32_t off = key < N ? (uint32_t)key * tokb + (uint32_t)(pc ^ swz<D>(row)) * 16 : kOobOffset;
-      buf_load16_lds(rv, vblk + 1024 * (wave + 4 * t), off);
+    for (int t = 0; t < TV::LOADS / 4; ++t) {
+      const int u = wave + 4 * t;
+      const int key = kb0 + TV::dma_row(u, lane);
+      const uint32_t off = key < N ? (uint32_t)key * tokb + 16u * TV::dma_chunk(u, lane) : kOobOffset;
+      buf_load16_lds(rv, vblk + TV::dma_dst(u), off);
     }
   }
 
-  int dma_row[DMA_PER_WAVE];
-  uint32_t dma_col[DMA_PER_WAVE];
-#pragma unroll
-  for (int t = 0; t < DMA_PER_WAVE; ++t) {
-    const int p = 64 * (wave + 4 * t) + lane;
-    const int row = p / CH, pc = p % CH;
-    dma_row[t] = row;
-    dma_col[t] = (uint32_t)(pc ^ swz<D>(row)) * 16;
-  }
-  auto issue = [&](int step, char* dst, float* rows) {
+  auto issue = [&](int step, char* dst, float* rows) __attribute__((always_inline)) {
     const int q0 = step * kQStep;
 #pragma unroll
     for (int t = 0; t < DMA_PER_WAVE; ++t) {
-      const int q = q0 + dma_row[t];
-      const uint32_t off = q < N ? (uint32_t)q * tokb + dma_col[t] : kOobOffset;
-      char* l = dst + 1024 * (wave + 4 * t);
+      const int u = wave + 4 * t;
+      const int q = q0 + TQ::dma_row(u, lane);
+      const uint32_t off = q < N ? (uint32_t)q * tokb + 16u * TQ::dma_chunk(u, lane) : kOobOffset;
+      char* l = dst + TQ::dma_dst(u);
       buf_load16_lds(rq, l, off);
       buf_load16_lds(rdo, l + QT, off);
     }
@@ -183,17 +176,18 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
     dkacc[i] = f32x16{};
   }
 
-  auto compute = [&](int step, const char* qt, const float* rows) {
+  // One step of 32 query rows. MASK: the causal mask is applied (steps that
+  // straddle the diagonal); the other steps have no per-element masking.
+  auto compute = [&](int step, const char* qt, const float* rows, auto mask_tag) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     const int q0 = step * kQStep;
-    if (CAUSAL && kw0 > q0 + kQStep - 1) return;  // wave-uniform: all of its keys are masked
     const char* dot = qt + QT;
     f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      s = mfma32(read_row8<D>(qt, l32, 2 * ks + g), kf[ks], s);
-      dp = mfma32(read_row8<D>(dot, l32, 2 * ks + g), read_row8<D>(vblk, 32 * wave + l32, 2 * ks + g), dp);
+      s = mfma32(TQ::row8(qt, l32, 2 * ks + g), kf[ks], s);
+      dp = mfma32(TQ::row8(dot, l32, 2 * ks + g), TV::row8(vblk, 32 * wave + l32, 2 * ks + g), dp);
     }
-    const bool need_mask = CAUSAL && kw0 + 31 > q0;
     f32x8 p8[2], ds8[2];
 #pragma unroll
     for (int rq4 = 0; rq4 < 4; ++rq4) {
@@ -204,7 +198,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * rq4 + e;
         float p = fast_exp2(__builtin_fmaf(s[r], c2, -l4[e]));
-        if (need_mask && mykey > q0 + qi0 + e) p = 0.f;
+        if constexpr (MASK) p = (mykey > q0 + qi0 + e) ? 0.f : p;
         p8[r >> 3][r & 7] = p;
         ds8[r >> 3][r & 7] = p * (dp[r] - d4[e]);
       }
@@ -216,24 +210,43 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const int col0 = 32 * db + 16 * (G & 1);
-        dvacc[db] = mfma32(read_col8<D>(dot, 16 * hh + 4 * g, 16 * hh + 8 + 4 * g, col0, lane), pb[hh], dvacc[db]);
-        dkacc[db] = mfma32(read_col8<D>(qt, 16 * hh + 4 * g, 16 * hh + 8 + 4 * g, col0, lane), dsb[hh], dkacc[db]);
+        dvacc[db] = mfma32(TQ::col8(dot, 16 * hh + 4 * g, 16 * hh + 8 + 4 * g, col0, lane), pb[hh], dvacc[db]);
+        dkacc[db] = mfma32(TQ::col8(qt, 16 * hh + 4 * g, 16 * hh + 8 + 4 * g, col0, lane), dsb[hh], dkacc[db]);
       }
   };
 
+  // Causal: query blocks start at the diagonal; the first kKvBlock / kQStep
+  // of them straddle it and are masked, the rest need no mask. Both loops go
+  // through the steps in pairs so each LDS buffer is named statically.
   const int nqs = (N + kQStep - 1) / kQStep;
   const int s0 = CAUSAL ? kb0 / kQStep : 0;
+  const int sm = CAUSAL ? min(nqs, s0 + kKvBlock / kQStep) : s0;  // masked steps: [s0, sm)
   issue(s0, buf0, row0);
   wait_vmem();
   __syncthreads();
-  for (int step = s0; step < nqs; step += 2) {
+  int step = s0;
+  for (; step < sm; step += 2) {
     if (step + 1 < nqs) issue(step + 1, buf1, row1);
-    compute(step, buf0, row0);
+    compute(step, buf0, row0, std::true_type{});
+    wait_vmem();
+    __syncthreads();
+    if (step + 1 >= nqs) {  // that was the last step: nothing left for the next loop
+      step = nqs;
+      break;
+    }
+    if (step + 2 < nqs) issue(step + 2, buf0, row0);
+    compute(step + 1, buf1, row1, std::integral_constant<bool, CAUSAL>{});
+    wait_vmem();
+    __syncthreads();
+  }
+  for (; step < nqs; step += 2) {
+    if (step + 1 < nqs) issue(step + 1, buf1, row1);
+    compute(step, buf0, row0, std::false_type{});
     wait_vmem();
     __syncthreads();
     if (step + 1 >= nqs) break;
     if (step + 2 < nqs) issue(step + 2, buf0, row0);
-    compute(step + 1, buf1, row1);
+    compute(step + 1, buf1, row1, std::false_type{});
     wait_vmem();
     __syncthreads();
   }
@@ -264,11 +277,11 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
     const bf16* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ dsum,
     bf16* __restrict__ dQ, int N, int H, int nqb, int total_blocks, float c2, uint32_t q_sign,
     float dq_scale) {
-  constexpr int CH = D / 8;
+  using T = Tile<kKTile, D>;  // one K or V tile (rows = keys)
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
-  constexpr int TILE = kKTile * D * 2;          // bytes of one K or V tile
-  constexpr int DMA_PER_WAVE = TILE / 1024 / 4;
+  constexpr int TILE = T::BYTES;
+  constexpr int DMA_PER_WAVE = T::LOADS / 4;
   __shared__ __attribute__((aligned(1024))) char kv0[2 * TILE];  // K tile, then V tile
   __shared__ __attribute__((aligned(1024))) char kv1[2 * TILE];
 
@@ -307,21 +320,13 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
     }
   }
 
-  int dma_row[DMA_PER_WAVE];
-  uint32_t dma_col[DMA_PER_WAVE];
-#pragma unroll
-  for (int t = 0; t < DMA_PER_WAVE; ++t) {
-    const int p = 64 * (wave + 4 * t) + lane;
-    const int row = p / CH, pc = p % CH;
-    dma_row[t] = row;
-    dma_col[t] = (uint32_t)(pc ^ swz<D>(row)) * 16;
-  }
-  auto issue = [&](int tile, char* dst) {
+  auto issue = [&](int tile, char* dst) __attribute__((always_inline)) {
 #pragma unroll
     for (int t = 0; t < DMA_PER_WAVE; ++t) {
-      const int key = tile * kKTile + dma_row[t];
-      const uint32_t off = key < N ? (uint32_t)key * tokb + dma_col[t] : kOobOffset;
-      char* l = dst + 1024 * (wave + 4 * t);
+      const int u = wave + 4 * t;
+      const int key = tile * kKTile + T::dma_row(u, lane);
+      const uint32_t off = key < N ? (uint32_t)key * tokb + 16u * T::dma_chunk(u, lane) : kOobOffset;
+      char* l = dst + T::dma_dst(u);
       buf_load16_lds(rk, l, off);
       buf_load16_lds(rv, l + TILE, off);
     }
@@ -331,18 +336,18 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
   for (int i = 0; i < DB; ++i) dqacc[i] = f32x16{};
 
-  auto compute = [&](int j, const char* kt) {
+  // One tile of 64 keys, one 32-key half at a time. MASK: causal diagonal.
+  auto compute = [&](int j, const char* kt, auto mask_tag) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     const int key0 = j * kKTile;
-    if (CAUSAL && key0 > qw0 + 31) return;
     const char* vt = kt + TILE;
-    const bool need_mask = CAUSAL && key0 + kKTile - 1 > qw0;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        s = mfma32(read_row8<D>(kt, kb * 32 + l32, 2 * ks + g), qf[ks], s);
-        dp = mfma32(read_row8<D>(vt, kb * 32 + l32, 2 * ks + g), dof[ks], dp);
+        s = mfma32(T::row8(kt, kb * 32 + l32, 2 * ks + g), qf[ks], s);
+        dp = mfma32(T::row8(vt, kb * 32 + l32, 2 * ks + g), dof[ks], dp);
       }
       bf16x8 dsf[2];
 #pragma unroll
@@ -352,9 +357,9 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
         for (int s8 = 0; s8 < 8; ++s8) {
           const int r = 8 * hh + s8;
           float p = fast_exp2(__builtin_fmaf(s[r], c2, -l2));
-          if (need_mask) {
+          if constexpr (MASK) {
             const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-            if (key > myq) p = 0.f;
+            p = (key > myq) ? 0.f : p;
           }
           x[s8] = p * (dp[r] - dd);
         }
@@ -365,25 +370,39 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
           const int kr = 32 * kb + 16 * hh;
-          const bf16x8 a = read_col8<D>(kt, kr + 4 * g, kr + 8 + 4 * g, 32 * db + 16 * (G & 1), lane);
+          const bf16x8 a = T::col8(kt, kr + 4 * g, kr + 8 + 4 * g, 32 * db + 16 * (G & 1), lane);
           dqacc[db] = mfma32(a, dsf[hh], dqacc[db]);
         }
     }
   };
 
+  // Causal: tiles from jm on straddle the diagonal (masked); earlier tiles
+  // need no mask. Keys past N need none: their K and V rows read as zero.
   const int kv_len = CAUSAL ? min(N, (qblk + 1) * kQBlock) : N;
   const int ntiles = (kv_len + kKTile - 1) / kKTile;
+  const int jm = CAUSAL ? qblk * (kQBlock / kKTile) : ntiles;
   issue(0, kv0);
   wait_vmem();
   __syncthreads();
-  for (int j = 0; j < ntiles; j += 2) {
+  int j = 0;
+  for (; j + 1 < jm; j += 2) {
+    issue(j + 1, kv1);
+    compute(j, kv0, std::false_type{});
+    wait_vmem();
+    __syncthreads();
+    if (j + 2 < ntiles) issue(j + 2, kv0);
+    compute(j + 1, kv1, std::false_type{});
+    wait_vmem();
+    __syncthreads();
+  }
+  for (; j < ntiles; j += 2) {
     if (j + 1 < ntiles) issue(j + 1, kv1);
-    compute(j, kv0);
+    compute(j, kv0, std::integral_constant<bool, CAUSAL>{});
     wait_vmem();
     __syncthreads();
     if (j + 1 >= ntiles) break;
     if (j + 2 < ntiles) issue(j + 2, kv0);
-    compute(j + 1, kv1);
+    compute(j + 1, kv1, std::integral_constant<bool, CAUSAL>{});
     wait_vmem();
     __syncthreads();
   }

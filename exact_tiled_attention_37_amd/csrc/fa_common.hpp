@@ -11,13 +11,19 @@
 // operand may present its k values in any order as long as the other operand
 // uses the same order.
 //
-// LDS tiles hold rows of d bfloat16 (d/8 chunks of 16 bytes). Chunk c of row
-// r is stored at chunk position c ^ swz(r). The swizzle is chosen so that
-// both access patterns the kernels use are free of bank conflicts:
-//   * row reads: 32 lanes read the same chunk of 32 consecutive rows;
-//   * transpose reads (ds_read_b64_tr_b16): a 16-lane group reads two
-//     adjacent chunks of 4 consecutive rows, and neighbouring groups read
-//     the next two chunks of the same rows.
+// LDS tiles (see Tile below) store a row-major R x D bfloat16 block as
+// 1 KiB blocks of 16 rows x 4 chunks (a chunk is 16 bytes: 8 elements of a
+// row), with the chunk order inside each 64-byte row slice XOR-swizzled by
+// row / 4. Then:
+//   * a whole-wave LDS-direct load of 1 KiB fills one block from 16 rows x
+//     64 contiguous bytes of memory;
+//   * row reads (16 lanes read the same chunk of 16 consecutive rows) and
+//     transpose reads (ds_read_b64_tr_b16: a 16-lane group reads two
+//     adjacent chunks of 4 consecutive rows, the next group the next two
+//     chunks of the same rows) hit 16 distinct 16-byte bank slots, i.e. no
+//     bank conflicts;
+//   * every LDS address is one of two per-lane bases plus a compile-time
+//     offset, so the reads need no address arithmetic.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -45,25 +51,6 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Chunk swizzle for a tile with D columns (see the header comment).
-// D = 32 is the narrow dS^T tile of the backward pass (4 chunks per row).
-template <int D>
-__device__ __forceinline__ int swz(int row) {
-  static_assert(D == 32 || D == 64 || D == 128, "tile width");
-  if constexpr (D == 128)
-    return 4 * (row & 3) + ((row >> 2) & 3);
-  else if constexpr (D == 64)
-    return 4 * ((row >> 1) & 1) + ((row >> 2) & 3);
-  else
-    return (row >> 2) & 3;
-}
-
-// Byte offset of 16-byte chunk c of row `row` in a swizzled tile.
-template <int D>
-__device__ __forceinline__ int tile_off(int row, int c) {
-  return (row * (D / 8) + (c ^ swz<D>(row))) * 16;
-}
-
 // Generic pointers into __shared__ arrays are converted to LDS (address
 // space 3) pointers so that ds_read / ds_write instructions are emitted.
 __device__ __forceinline__ u32x4 lds_read16(const char* base, int off) {
@@ -76,13 +63,6 @@ __device__ __forceinline__ void lds_write8(char* base, int off, u32x2 v) {
   *(FA_LDS u32x2*)((FA_LDS char*)base + off) = v;
 }
 
-// Row-read operand: 8 consecutive elements (chunk c) of row `row`.
-template <int D>
-__device__ __forceinline__ bf16x8 read_row8(const char* tile, int row, int c) {
-  u32x4 v = lds_read16(tile, tile_off<D>(row, c));
-  return __builtin_bit_cast(bf16x8, v);
-}
-
 // ds_read_b64_tr_b16: within each 16-lane group, lane t supplies the address
 // of 4 consecutive 16-bit elements ("chunk t"); lane j receives element
 // j%4 of chunks j/4, j/4+4, j/4+8, j/4+12 (measured on the device).
@@ -90,22 +70,50 @@ __device__ __forceinline__ i16x4 lds_read_tr(const char* base, int off) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)((FA_LDS char*)base + off));
 }
 
-// Column operand from a row-major tile (rows = the k dimension).
-// Returns, for this lane's column col0 + (lane % 16), the 8 elements of rows
-// rowA .. rowA+3 followed by rowB .. rowB+3, where rowA/rowB are given for the
-// lane's 16-lane group. col0 must be a multiple of 16.
-template <int D>
-__device__ __forceinline__ bf16x8 read_col8(const char* tile, int rowA, int rowB, int col0, int lane) {
-  const int j = lane & 15;
-  const int col = col0 + 4 * (j & 3);
-  const int c = col >> 3, half = (col >> 2) & 1;
-  const int ra = rowA + (j >> 2), rb = rowB + (j >> 2);
-  i16x4 lo = lds_read_tr(tile, tile_off<D>(ra, c) + 8 * half);
-  i16x4 hi = lds_read_tr(tile, tile_off<D>(rb, c) + 8 * half);
-  typedef short i16x8 __attribute__((ext_vector_type(8)));
-  i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  return __builtin_bit_cast(bf16x8, v);
-}
+// LDS tile of R rows (R = 32, 64 or 128) by D bfloat16 columns, laid out as
+// described at the top of this file: block (row / 16, chunk / 4) at
+// ((row / 16) * (D / 32) + chunk / 4) * 1024 bytes; inside a block, row r
+// (0..15) and chunk c (0..3) sit in 16-byte slot 4 r + (c ^ (r / 4)).
+template <int R, int D>
+struct Tile {
+  static_assert(R == 32 || R == 64 || R == 128, "tile rows");
+  static_assert(D == 64 || D == 128, "head dimension");
+  static constexpr int CH = D / 8;      // chunks per row
+  static constexpr int NCB = CH / 4;    // 4-chunk blocks per row
+  static constexpr int BYTES = R * D * 2;
+  static constexpr int LOADS = BYTES / 1024;  // whole-wave 1 KiB loads per tile
+
+  __device__ static constexpr int addr(int row, int c) {
+    const int rl = row & 15;
+    return (((row >> 4) * NCB + (c >> 2)) << 10) + ((rl << 2) + ((c & 3) ^ (rl >> 2))) * 16;
+  }
+  // Whole-wave load u fills block u (bytes [1024 u, 1024 u + 1024)); lane i
+  // writes slot i, which holds chunk dma_chunk of row dma_row.
+  __device__ static constexpr int dma_dst(int u) { return u << 10; }
+  __device__ static constexpr int dma_row(int u, int lane) { return (u / NCB) * 16 + (lane >> 2); }
+  __device__ static constexpr int dma_chunk(int u, int lane) {
+    return (u % NCB) * 4 + ((lane & 3) ^ ((lane >> 2) >> 2));
+  }
+
+  // Row read: chunk c (elements 8c..8c+7) of row `row`.
+  __device__ static bf16x8 row8(const char* t, int row, int c) {
+    return __builtin_bit_cast(bf16x8, lds_read16(t, addr(row, c)));
+  }
+  // Column read through two transpose loads: for this lane's column
+  // col0 + (lane % 16) the 8 elements of rows rowA..rowA+3, rowB..rowB+3
+  // (rowA/rowB given for the lane's 16-lane group and multiples of 4; col0 a
+  // multiple of 16).
+  __device__ static bf16x8 col8(const char* t, int rowA, int rowB, int col0, int lane) {
+    const int j = lane & 15;
+    const int col = col0 + 4 * (j & 3);
+    const int c = col >> 3, half = (col >> 2) & 1;
+    i16x4 lo = lds_read_tr(t, addr(rowA + (j >> 2), c) + 8 * half);
+    i16x4 hi = lds_read_tr(t, addr(rowB + (j >> 2), c) + 8 * half);
+    typedef short i16x8 __attribute__((ext_vector_type(8)));
+    i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v);
+  }
+};
 
 // Combine a value with the same value of lane l ^ 32 (v_permlane32_swap).
 __device__ __forceinline__ float xhalf_max(float x) {

@@ -37,6 +37,8 @@
 // straddle the diagonal (or the ragged end of the sequence) apply a mask.
 // A negative softmax scale is handled by negating Q when it is loaded.
 
+#include <type_traits>
+
 #include "fa_common.hpp"
 #include "fa_launch.hpp"
 
@@ -54,9 +56,9 @@ __global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     bf16* __restrict__ O, float* __restrict__ LSE, int N, int H, int nqb, int total_blocks,
     float c2, uint32_t q_sign) {
-  constexpr int CH = D / 8;                        // 16-byte chunks per row
-  constexpr int TILE = kFwdBC * D * 2;             // bytes of one K or V tile
-  constexpr int DMA_PER_WAVE = TILE / 1024 / 4;    // 1 KiB wave loads per tile per wave
+  using T = Tile<kFwdBC, D>;                       // one K or V tile in LDS
+  constexpr int TILE = T::BYTES;
+  constexpr int DMA_PER_WAVE = T::LOADS / 4;       // 1 KiB wave loads per tile per wave
   constexpr int KS = D / 16;                       // MFMA k-steps over d
   constexpr int DB = D / 32;                       // 32-wide output column blocks
   __shared__ __attribute__((aligned(1024))) char kv0[2 * TILE];  // K tile, then V tile
@@ -88,23 +90,15 @@ __global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
     for (int ks = 0; ks < KS; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, buf_load16(rq, qoff + 32 * ks) ^ q_sign);
   }
 
-  // LDS-DMA source offsets: wave load u = wave + 4 t fills LDS bytes
-  // [1024 u, 1024 u + 1024) of a tile; lane i fills chunk position 64 u + i.
-  int dma_row[DMA_PER_WAVE];
-  uint32_t dma_col[DMA_PER_WAVE];
-#pragma unroll
-  for (int t = 0; t < DMA_PER_WAVE; ++t) {
-    const int p = 64 * (wave + 4 * t) + lane;
-    const int row = p / CH, pc = p % CH;
-    dma_row[t] = row;
-    dma_col[t] = (uint32_t)(pc ^ swz<D>(row)) * 16;
-  }
-  auto issue = [&](int tile, char* dst) {
+  // LDS-DMA: wave load u = wave + 4 t of a tile; lane i fills the chunk
+  // (row, column) the layout assigns to it. A tile row is a key.
+  auto issue = [&](int tile, char* dst) __attribute__((always_inline)) {
 #pragma unroll
     for (int t = 0; t < DMA_PER_WAVE; ++t) {
-      const int key = tile * kFwdBC + dma_row[t];
-      const uint32_t off = key < N ? (uint32_t)key * tokb + dma_col[t] : kOobOffset;
-      char* l = dst + 1024 * (wave + 4 * t);
+      const int u = wave + 4 * t;
+      const int key = tile * kFwdBC + T::dma_row(u, lane);
+      const uint32_t off = key < N ? (uint32_t)key * tokb + 16u * T::dma_chunk(u, lane) : kOobOffset;
+      char* l = dst + T::dma_dst(u);
       buf_load16_lds(rk, l, off);
       buf_load16_lds(rv, l + TILE, off);
     }
@@ -119,9 +113,12 @@ __global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   float m_run = -INFINITY;  // running max of c2 * score (log2 domain), possibly stale by <= 8
   float l_run = 0.f;        // this lane's share of the running sum
 
-  auto compute = [&](int j, const char* kt) {
+  // One K/V tile. MASK selects the variant for tiles that straddle the
+  // causal diagonal or the end of the sequence; all other tiles run the
+  // variant without any per-element masking.
+  auto compute = [&](int j, const char* kt, auto mask_tag) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     const int key0 = j * kFwdBC;
-    if (CAUSAL && key0 > qw0 + 31) return;  // wave-uniform: fully masked for this wave
     const char* vt = kt + TILE;
     f32x16 s[2];
 #pragma unroll
@@ -129,10 +126,9 @@ __global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
       s[kb] = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        s[kb] = mfma32(read_row8<D>(kt, kb * 32 + l32, 2 * ks + g), qf[ks], s[kb]);
+        s[kb] = mfma32(T::row8(kt, kb * 32 + l32, 2 * ks + g), qf[ks], s[kb]);
     }
-    const bool need_mask = (CAUSAL && key0 + kFwdBC - 1 > qw0) || (key0 + kFwdBC > N);
-    if (need_mask) {
+    if constexpr (MASK) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -149,7 +145,8 @@ __global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
     mx = xhalf_max(mx);
     const float tile_m = (mx == -INFINITY) ? -INFINITY : mx * c2;
     const bool grow = tile_m > m_run + kRescaleSlack;
-    if (__builtin_amdgcn_ballot_w64(grow)) {  // wave-uniform
+    if (__builtin_amdgcn_ballot_w64(grow)) {  // wave-uniform, rarely taken
+      asm volatile("" ::: "memory");          // keep it a branch (no speculation)
       const float m_new = grow ? tile_m : m_run;
       // 0 when m_run = -inf, 1 when unchanged (and when no key was visible yet)
       const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
@@ -160,6 +157,9 @@ __global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
     }
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
 
+    // P in bf16 for the PV product; the row sum stays in fp32 (the
+    // logsumexp is checked against the exact value, so it must not inherit
+    // the bf16 rounding of P).
     bf16x8 pf[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
@@ -168,7 +168,7 @@ __global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
       for (int s8 = 0; s8 < 8; ++s8) {
         const float sv = s[ks >> 1][8 * (ks & 1) + s8];
         float e = fast_exp2(__builtin_fmaf(sv, c2, -m_use));
-        if (need_mask) e = (sv == -INFINITY) ? 0.f : e;
+        if constexpr (MASK) e = (sv == -INFINITY) ? 0.f : e;  // exact zero even when c2 = 0
         p[s8] = e;
         l_run += e;
       }
@@ -178,22 +178,37 @@ __global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const bf16x8 a = read_col8<D>(vt, 16 * ks + 4 * g, 16 * ks + 8 + 4 * g, 32 * db + 16 * (G & 1), lane);
+        const bf16x8 a = T::col8(vt, 16 * ks + 4 * g, 16 * ks + 8 + 4 * g, 32 * db + 16 * (G & 1), lane);
         oacc[db] = mfma32(a, pf[ks], oacc[db]);
       }
   };
-
+  // Tiles before jm need no mask for any wave of this workgroup; they run in
+  // a loop of their own so that the masked variant never joins the hot loop.
+  // Both loops go through the tiles in pairs so that each LDS buffer is named
+  // statically (tile j lives in buffer j % 2).
+  const int jm = CAUSAL ? min(qblk * (kFwdBR / kFwdBC), N / kFwdBC) : N / kFwdBC;
   issue(0, kv0);
   wait_vmem();
   __syncthreads();
-  for (int j = 0; j < ntiles; j += 2) {
+  int j = 0;
+  for (; j + 1 < jm; j += 2) {
+    issue(j + 1, kv1);
+    compute(j, kv0, std::false_type{});
+    wait_vmem();
+    __syncthreads();
+    if (j + 2 < ntiles) issue(j + 2, kv0);
+    compute(j + 1, kv1, std::false_type{});
+    wait_vmem();
+    __syncthreads();
+  }
+  for (; j < ntiles; j += 2) {
     if (j + 1 < ntiles) issue(j + 1, kv1);
-    compute(j, kv0);
+    compute(j, kv0, std::true_type{});
     wait_vmem();
     __syncthreads();
     if (j + 1 >= ntiles) break;
     if (j + 2 < ntiles) issue(j + 2, kv0);
-    compute(j + 1, kv1);
+    compute(j + 1, kv1, std::true_type{});
     wait_vmem();
     __syncthreads();
   }
