@@ -12,15 +12,15 @@
 // so long sequences with few heads still fill the chip; inside a workgroup
 // each of the 4 wavefronts owns 32 query rows and all of them share the K/V
 // tiles staged in LDS, so no partial results are exchanged between waves.
-// Two workgroups share a CU (8 waves, 2 per SIMD), so one wave's softmax
-// arithmetic overlaps the other's matrix instructions.
+// Two (d = 128) or three (d = 64) workgroups share a CU, so one wave's
+// softmax arithmetic overlaps another's matrix instructions.
 //
-// K/V tiles (64 keys) move from memory straight into LDS with buffer loads
+// K/V tiles move from memory straight into LDS with buffer loads
 // that write LDS directly (no register staging), double-buffered: the next
 // tile streams in while the current one is used. Rows past the end of the
 // sequence come back as zeros from the buffer range check.
 //
-// Per wave and tile:
+// Per wave and K/V tile (64 keys at d = 128, 32 at d = 64):
 //   S^T = K Q^T     (MFMA; lane l owns query row l % 32, so a row's scores
 //                    sit in two lanes: l and l ^ 32)
 //   online softmax in the log2 domain: c2 = |scale| * log2(e) is folded into
@@ -47,15 +47,24 @@ namespace fa {
 namespace {
 
 constexpr int kFwdBR = 128;     // query rows per workgroup
-constexpr int kFwdBC = 64;      // keys per K/V tile
 constexpr int kFwdThreads = 256;
+
+// Per head dimension: keys per K/V tile and waves per SIMD. d = 64 uses
+// 32-key tiles so that three workgroups fit per CU (fewer registers and LDS
+// per workgroup); d = 128 uses 64-key tiles at two workgroups per CU.
+template <int D> struct FwdCfg;
+template <> struct FwdCfg<64> { static constexpr int BC = 32, WAVES_PER_SIMD = 3; };
+template <> struct FwdCfg<128> { static constexpr int BC = 64, WAVES_PER_SIMD = 2; };
 constexpr float kRescaleSlack = 8.f;  // log2 units a row max may exceed the running max
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_kernel(
+__global__ __launch_bounds__(kFwdThreads)
+__attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_PER_SIMD))) void fwd_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     bf16* __restrict__ O, float* __restrict__ LSE, int N, int H, int nqb, int total_blocks,
     float c2, uint32_t q_sign) {
+  constexpr int kFwdBC = FwdCfg<D>::BC;            // keys per K/V tile
+  constexpr int KB = kFwdBC / 32;                  // 32-key score blocks per tile
   using T = Tile<kFwdBC, D>;                       // one K or V tile in LDS
   constexpr int TILE = T::BYTES;
   constexpr int DMA_PER_WAVE = T::LOADS / 4;       // 1 KiB wave loads per tile per wave
@@ -120,17 +129,17 @@ __global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
     constexpr bool MASK = decltype(mask_tag)::value;
     const int key0 = j * kFwdBC;
     const char* vt = kt + TILE;
-    f32x16 s[2];
+    // The KB accumulation chains are interleaved (independent MFMAs back to back).
+    f32x16 s[KB];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16{};
+    for (int kb = 0; kb < KB; ++kb) s[kb] = f32x16{};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        s[kb] = mfma32(T::row8(kt, kb * 32 + l32, 2 * ks + g), qf[ks], s[kb]);
-    }
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) s[kb] = mfma32(T::row8(kt, kb * 32 + l32, 2 * ks + g), qf[ks], s[kb]);
     if constexpr (MASK) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
@@ -139,7 +148,7 @@ __global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
     }
     float mx = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
     mx = xhalf_max(mx);
@@ -160,9 +169,9 @@ __global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
     // P in bf16 for the PV product; the row sum stays in fp32 (the
     // logsumexp is checked against the exact value, so it must not inherit
     // the bf16 rounding of P).
-    bf16x8 pf[4];
+    bf16x8 pf[2 * KB];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+    for (int ks = 0; ks < 2 * KB; ++ks) {
       f32x8 p;
 #pragma unroll
       for (int s8 = 0; s8 < 8; ++s8) {
@@ -175,7 +184,7 @@ __global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
       pf[ks] = to_bf16x8(p);
     }
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
+    for (int ks = 0; ks < 2 * KB; ++ks)
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const bf16x8 a = T::col8(vt, 16 * ks + 4 * g, 16 * ks + 8 + 4 * g, 32 * db + 16 * (G & 1), lane);
