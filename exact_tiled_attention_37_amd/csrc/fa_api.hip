@@ -37,8 +37,8 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 fa_status check_shape(int B, int N, int H, int d) {
   if (d != 64 && d != 128) return FA_ERR_HEADDIM;
   if (B < 1 || N < 1 || H < 1) return FA_ERR_SHAPE;
-  // Byte offsets within one sequence must stay well below 2^32 (buffer
-  // loads use 32-bit offsets and an out-of-range sentinel near 2^32).
+  // Byte offsets within one sequence must stay below 2^32: buffer loads use
+  // 32-bit offsets, and rows past the end are addressed at N * row bytes.
   const long long elems = (long long)B * N * H * d;
   if (elems > kMaxElems) return FA_ERR_SHAPE;
   return FA_OK;

@@ -138,15 +138,14 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   bf16x8 kf[KS];
   {
     const auto rk = make_rsrc(K + hoff, nrec);
-    const uint32_t koff = mykey < N ? (uint32_t)mykey * tokb + 16 * g : kOobOffset;
+    const uint32_t koff = row_off(mykey, N, tokb, 16 * g);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) kf[ks] = __builtin_bit_cast(bf16x8, buf_load16(rk, koff + 32 * ks) ^ k_sign);
     const auto rv = make_rsrc(V + hoff, nrec);
 #pragma unroll
     for (int t = 0; t < TV::LOADS / 4; ++t) {
       const int u = wave + 4 * t;
-      const int key = kb0 + TV::dma_row(u, lane);
-      const uint32_t off = key < N ? (uint32_t)key * tokb + 16u * TV::dma_chunk(u, lane) : kOobOffset;
+      const uint32_t off = row_off(kb0 + TV::dma_row(u, lane), N, tokb, 16u * TV::dma_chunk(u, lane));
       buf_load16_lds(rv, vblk + TV::dma_dst(u), off);
     }
   }
@@ -156,8 +155,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
     for (int t = 0; t < DMA_PER_WAVE; ++t) {
       const int u = wave + 4 * t;
-      const int q = q0 + TQ::dma_row(u, lane);
-      const uint32_t off = q < N ? (uint32_t)q * tokb + 16u * TQ::dma_chunk(u, lane) : kOobOffset;
+      const uint32_t off = row_off(q0 + TQ::dma_row(u, lane), N, tokb, 16u * TQ::dma_chunk(u, lane));
       char* l = dst + TQ::dma_dst(u);
       buf_load16_lds(rq, l, off);
       buf_load16_lds(rdo, l + QT, off);
@@ -308,7 +306,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   {
     const auto rq = make_rsrc(Q + hoff, nrec);
     const auto rdo = make_rsrc(dO + hoff, nrec);
-    const uint32_t qoff = myq < N ? (uint32_t)myq * tokb + 16 * g : kOobOffset;
+    const uint32_t qoff = row_off(myq, N, tokb, 16 * g);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       qf[ks] = __builtin_bit_cast(bf16x8, buf_load16(rq, qoff + 32 * ks) ^ q_sign);
@@ -324,8 +322,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
     for (int t = 0; t < DMA_PER_WAVE; ++t) {
       const int u = wave + 4 * t;
-      const int key = tile * kKTile + T::dma_row(u, lane);
-      const uint32_t off = key < N ? (uint32_t)key * tokb + 16u * T::dma_chunk(u, lane) : kOobOffset;
+      const uint32_t off = row_off(tile * kKTile + T::dma_row(u, lane), N, tokb, 16u * T::dma_chunk(u, lane));
       char* l = dst + T::dma_dst(u);
       buf_load16_lds(rk, l, off);
       buf_load16_lds(rv, l + TILE, off);

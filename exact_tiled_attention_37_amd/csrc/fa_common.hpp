@@ -132,14 +132,32 @@ __device__ __forceinline__ bf16x4 to_bf16x4(f32x4 x) { return __builtin_convertv
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Reductions over the values of an MFMA accumulator as a few independent
+// chains (short dependency depth); each chain of three-input maxima becomes
+// v_max3 instructions.
+__device__ __forceinline__ float max16(const f32x16& v, float init) {
+  float a = fmaxf(fmaxf(fmaxf(fmaxf(fmaxf(fmaxf(fmaxf(v[0], v[1]), v[2]), v[3]), v[4]), v[5]), v[6]), v[7]);
+  float b = fmaxf(fmaxf(fmaxf(fmaxf(fmaxf(fmaxf(fmaxf(v[8], v[9]), v[10]), v[11]), v[12]), v[13]), v[14]), v[15]);
+  return fmaxf(fmaxf(a, b), init);
+}
+__device__ __forceinline__ float sum8(const f32x8& v) {
+  return ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+}
+
+// Byte offset of row `row` (chunk offset col) inside a buffer resource made
+// over rows [0, n): rows at or past n are clamped to n, whose offset is
+// already past the resource's end, so they read as zeros. n * row_bytes must
+// stay below 2^32 (guaranteed by the element limit the library enforces).
+__device__ __forceinline__ uint32_t row_off(int row, int n, uint32_t row_bytes, uint32_t col) {
+  return (uint32_t)min(row, n) * row_bytes + col;
+}
+
 // Buffer resource over `nbytes` bytes starting at `base`. Loads whose byte
 // offset falls outside [0, nbytes) return zeros (the hardware range check),
 // which is how rows past the end of a sequence are read.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t nbytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes, 0x00020000);
 }
-// An offset that is outside every resource made above (nbytes < 2^32 - 16).
-constexpr uint32_t kOobOffset = 0xFFFFFFF0u;
 
 __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));

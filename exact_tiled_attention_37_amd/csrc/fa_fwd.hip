@@ -94,7 +94,7 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
   // Q as the B operand of S^T = K Q^T: row myq, d = 16*ks + 8*g .. +7.
   bf16x8 qf[KS];
   {
-    const uint32_t qoff = myq < N ? (uint32_t)myq * tokb + 16 * g : kOobOffset;
+    const uint32_t qoff = row_off(myq, N, tokb, 16 * g);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, buf_load16(rq, qoff + 32 * ks) ^ q_sign);
   }
@@ -105,8 +105,7 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
 #pragma unroll
     for (int t = 0; t < DMA_PER_WAVE; ++t) {
       const int u = wave + 4 * t;
-      const int key = tile * kFwdBC + T::dma_row(u, lane);
-      const uint32_t off = key < N ? (uint32_t)key * tokb + 16u * T::dma_chunk(u, lane) : kOobOffset;
+      const uint32_t off = row_off(tile * kFwdBC + T::dma_row(u, lane), N, tokb, 16u * T::dma_chunk(u, lane));
       char* l = dst + T::dma_dst(u);
       buf_load16_lds(rk, l, off);
       buf_load16_lds(rv, l + TILE, off);
@@ -146,11 +145,9 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
           if ((CAUSAL && key > myq) || key >= N) s[kb][r] = -INFINITY;
         }
     }
-    float mx = -INFINITY;
+    float mx = max16(s[0], -INFINITY);
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    for (int kb = 1; kb < KB; ++kb) mx = max16(s[kb], mx);
     mx = xhalf_max(mx);
     const float tile_m = (mx == -INFINITY) ? -INFINITY : mx * c2;
     const bool grow = tile_m > m_run + kRescaleSlack;
@@ -179,8 +176,8 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
         float e = fast_exp2(__builtin_fmaf(sv, c2, -m_use));
         if constexpr (MASK) e = (sv == -INFINITY) ? 0.f : e;  // exact zero even when c2 = 0
         p[s8] = e;
-        l_run += e;
       }
+      l_run += sum8(p);
       pf[ks] = to_bf16x8(p);
     }
 #pragma unroll
