@@ -8,12 +8,16 @@ from .attention import (
     attention_backward,
     attention_backward_head,
     attention_forward,
+    attention_forward_chunk,
     attention_forward_rows,
+    merge_chunks,
 )
 
 __all__ = [
     "attention_forward",
+    "attention_forward_chunk",
     "attention_forward_rows",
+    "merge_chunks",
     "attention_backward",
     "attention_backward_head",
 ]

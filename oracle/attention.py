@@ -173,3 +173,82 @@ def attention_backward_head(q, k, v, do, causal: bool, scale: float, b: int, h: 
     sl = (slice(b, b + 1), slice(None), slice(h, h + 1), slice(None))
     dq, dk, dv, _, _, _ = attention_backward(q[sl], k[sl], v[sl], do[sl], causal, scale)
     return dq[0, :, 0, :], dk[0, :, 0, :], dv[0, :, 0, :]
+
+
+# ---------------------------------------------------------------------------
+# Key-range chunks and their merge.
+#
+# The Ring Attention entry on the "High-Bandwidth Memory" keyword page
+# describes attention computed block by block: each device keeps its own
+# query block while key/value blocks circulate, and every pass attends the
+# local queries to one key/value block. The IPLEX post (section "Tiling
+# preserves the attention calculation") states that such blocks must
+# combine into the globally normalised result. The pages print no formula
+# for the combination; the plain reading, written out here, is that a chunk
+# is ordinary attention restricted to its keys, reported with its own
+# logsumexp, and that chunks combine by weighting each chunk's normalised
+# output with its share of the total softmax mass:
+#
+#     chunk c over keys K_c:  O_c = softmax(S[:, K_c]) V[K_c],
+#                             L_c = ln sum_{j in K_c} exp(S[:, j])
+#     merge:  L = ln sum_c exp(L_c),   O = sum_c exp(L_c - L) O_c
+#
+# Positions are global: query row i of a chunk sits at q_start + i and key
+# row j at k_start + j; with the causal mask key j is visible to query i iff
+# k_start + j <= q_start + i. A row that sees no key of a chunk has O_c = 0
+# and L_c = -inf (it carries no mass); a row that sees no key of any chunk
+# merges to O = 0 and L = -inf.
+
+
+def attention_forward_chunk(q, k, v, causal: bool, scale: float, q_start: int = 0, k_start: int = 0):
+    """Attention of a query chunk (rows at global positions q_start..) over a
+    key chunk (positions k_start..). q is [B, Nq, H, d]; k and v are
+    [B, Nk, H, d]. Returns (O_c [B, Nq, H, d], L_c [B, H, Nq]) in float64,
+    with O_c = 0 and L_c = -inf for rows that see no key of the chunk."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    if q.ndim != 4 or k.shape != v.shape or k.ndim != 4 or q.shape[0] != k.shape[0] or q.shape[2:] != k.shape[2:]:
+        raise ValueError("q must be [B, Nq, H, d] and k, v [B, Nk, H, d]")
+    B, Nq, H, d = q.shape
+    Nk = k.shape[1]
+    o = np.zeros((B, Nq, H, d))
+    lse = np.full((B, H, Nq), -np.inf)
+    if Nk == 0:
+        return o, lse
+    for b in range(B):
+        for h in range(H):
+            qh, kh, vh = q[b, :, h, :], k[b, :, h, :], v[b, :, h, :]
+            for r0, r1 in _row_chunks(Nq, Nk):
+                s = scale * (qh[r0:r1] @ kh.T)
+                if causal:
+                    qpos = (q_start + np.arange(r0, r1))[:, None]
+                    kpos = (k_start + np.arange(Nk))[None, :]
+                    s = np.where(kpos > qpos, -np.inf, s)
+                p, m, l = _softmax_rows(s)
+                o[b, r0:r1, h, :] = p @ vh
+                with np.errstate(divide="ignore"):
+                    lse[b, h, r0:r1] = np.where(l > 0, m + np.log(np.where(l > 0, l, 1.0)), -np.inf)
+    return o, lse
+
+
+def merge_chunks(o_parts, lse_parts):
+    """Combine chunk results over disjoint key sets: o_parts [C, B, Nq, H, d],
+    lse_parts [C, B, H, Nq] (natural log, -inf for an empty chunk row).
+    Returns (O [B, Nq, H, d], L [B, H, Nq]) in float64."""
+    o_parts = np.asarray(o_parts, dtype=np.float64)
+    lse_parts = np.asarray(lse_parts, dtype=np.float64)
+    if o_parts.ndim != 5 or lse_parts.ndim != 4 or o_parts.shape[0] != lse_parts.shape[0]:
+        raise ValueError("o_parts must be [C, B, Nq, H, d] and lse_parts [C, B, H, Nq]")
+    C, B, Nq, H, d = o_parts.shape
+    if lse_parts.shape != (C, B, H, Nq):
+        raise ValueError("lse_parts must be [C, B, H, Nq]")
+    mx = lse_parts.max(axis=0)                                  # [B, H, Nq]
+    mx_safe = np.where(np.isfinite(mx), mx, 0.0)
+    w = np.exp(lse_parts - mx_safe[None])                       # exp(-inf) = 0 for empty rows
+    tot = w.sum(axis=0)                                         # [B, H, Nq]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        lse = np.where(tot > 0, mx_safe + np.log(np.where(tot > 0, tot, 1.0)), -np.inf)
+        frac = np.where(tot[None] > 0, w / np.where(tot > 0, tot, 1.0)[None], 0.0)  # [C, B, H, Nq]
+    o = np.einsum("cbhn,cbnhd->bnhd", frac, o_parts)
+    return o, lse

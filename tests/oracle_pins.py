@@ -358,6 +358,137 @@ def pin_backward_head(mod):
             _close(dv, tv.grad[b, h].numpy(), 1e-12, what="head dV")
 
 
+# --------------------------------------------------------------------------
+# key-range chunk and merge pins
+
+
+def _brute_chunk(q, k, v, causal, scale, q_start, k_start):
+    """Scalar loops over global positions, no matrix products; a row that
+    sees no key of the chunk gives O = 0 and L = -inf."""
+    B, Nq, H, d = q.shape
+    Nk = k.shape[1]
+    o = np.zeros((B, Nq, H, d))
+    lse = np.full((B, H, Nq), -np.inf)
+    for b in range(B):
+        for h in range(H):
+            for i in range(Nq):
+                keys = [j for j in range(Nk) if not causal or k_start + j <= q_start + i]
+                if not keys:
+                    continue
+                s = [scale * math.fsum(q[b, i, h, t] * k[b, j, h, t] for t in range(d)) for j in keys]
+                m = max(s)
+                w = [math.exp(x - m) for x in s]
+                tot = math.fsum(w)
+                for t in range(d):
+                    o[b, i, h, t] = math.fsum(w[n] * v[b, j, h, t] for n, j in enumerate(keys)) / tot
+                lse[b, h, i] = m + math.log(tot)
+    return o, lse
+
+
+def _close_inf(a, b, tol=TOL, what=""):
+    """_close that also accepts matching -inf entries."""
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    ninf = np.isneginf(b)
+    assert np.array_equal(np.isneginf(a), ninf), f"{what}: -inf pattern differs"
+    _close(np.where(ninf, 0.0, a), np.where(ninf, 0.0, b), tol, what)
+
+
+def pin_chunk_brute_force(mod):
+    """A query chunk against a key chunk at global offsets agrees with scalar
+    loops, including rows that see part of the chunk or none of it."""
+    cases = [((1, 6, 7, 2, 3), (0, 0), 301), ((1, 5, 9, 1, 4), (4, 2), 302),
+             ((2, 7, 4, 1, 2), (3, 6), 303), ((1, 5, 8, 2, 3), (10, 0), 304)]
+    for (B, Nq, Nk, H, d), (qs, ks), seed in cases:
+        q = _rand((B, Nq, H, d), seed)
+        k = _rand((B, Nk, H, d), seed + 1000)
+        v = _rand((B, Nk, H, d), seed + 2000)
+        for causal in (False, True):
+            o, lse = mod.attention_forward_chunk(q, k, v, causal, 0.6, qs, ks)
+            ob, lseb = _brute_chunk(q, k, v, causal, 0.6, qs, ks)
+            _close(o, ob, 1e-13, what="chunk brute output")
+            _close_inf(lse, lseb, 1e-13, what="chunk brute lse")
+
+
+def pin_chunk_merge_is_full_attention(mod):
+    """Splitting the keys into consecutive chunks (one of them empty) and
+    merging the chunk results gives full attention; so does taking a query
+    block at its global position."""
+    B, N, H, d = 2, 37, 2, 5
+    q, k, v = (_rand((B, N, H, d), 310 + t) for t in range(3))
+    bounds = [0, 1, 9, 9, 20, 31, 37]
+    for causal in (False, True):
+        o_full, l_full = mod.attention_forward(q, k, v, causal, 0.45)
+        for r0, r1 in ((0, N), (13, 29)):
+            parts = [mod.attention_forward_chunk(q[:, r0:r1], k[:, a:b], v[:, a:b], causal, 0.45, r0, a)
+                     for a, b in zip(bounds[:-1], bounds[1:])]
+            o, lse = mod.merge_chunks(np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts]))
+            _close(o, o_full[:, r0:r1], 1e-12, what="merged output")
+            _close(lse, l_full[:, :, r0:r1], 1e-12, what="merged lse")
+
+
+def pin_chunk_global_offsets(mod):
+    """Causal chunks at global positions: keys wholly before the queries are
+    all visible (the non-causal result), keys wholly after are invisible
+    (O = 0, L = -inf), and moving both chunks by the same amount changes
+    nothing."""
+    q = _rand((1, 6, 2, 4), 320)
+    k = _rand((1, 9, 2, 4), 321)
+    v = _rand((1, 9, 2, 4), 322)
+    o_nc, l_nc = mod.attention_forward_chunk(q, k, v, False, 0.8, 0, 0)
+    o_past, l_past = mod.attention_forward_chunk(q, k, v, True, 0.8, 100, 91)
+    _close(o_past, o_nc, what="past chunk output")
+    _close(l_past, l_nc, what="past chunk lse")
+    o_fut, l_fut = mod.attention_forward_chunk(q, k, v, True, 0.8, 0, 6)
+    assert np.all(o_fut == 0.0) and np.all(np.isneginf(l_fut)), "future chunk must be empty"
+    o_a, l_a = mod.attention_forward_chunk(q, k, v, True, 0.8, 4, 2)
+    o_b, l_b = mod.attention_forward_chunk(q, k, v, True, 0.8, 1004, 1002)
+    _close(o_a, o_b, what="shifted output")
+    _close(l_a, l_b, what="shifted lse")
+    # Query row i sees keys 0 .. i + 2 here: row 0 equals the first three keys alone.
+    o_3, l_3 = mod.attention_forward_chunk(q[:, :1], k[:, :3], v[:, :3], False, 0.8, 0, 0)
+    _close(o_a[:, :1], o_3, what="partial row output")
+    _close(l_a[:, :, :1], l_3, what="partial row lse")
+
+
+def pin_merge_closed_forms(mod):
+    """Merge identities: one chunk passes through; two chunks with equal L
+    average their outputs and add ln 2; a chunk with L = -inf carries no
+    weight; chunk order does not matter; rows empty in every chunk give
+    O = 0 and L = -inf."""
+    C, B, Nq, H, d = 3, 2, 4, 2, 3
+    o = _rand((C, B, Nq, H, d), 330)
+    lse = _rand((C, B, H, Nq), 331) * 3.0
+    m1, l1 = mod.merge_chunks(o[:1], lse[:1])
+    _close(m1, o[0], what="single chunk output")
+    _close(l1, lse[0], what="single chunk lse")
+    eq = np.stack([lse[0], lse[0]])
+    m2, l2 = mod.merge_chunks(o[:2], eq)
+    _close(m2, 0.5 * (o[0] + o[1]), what="equal-weight output")
+    _close(l2, lse[0] + math.log(2.0), what="equal-weight lse")
+    dead = lse.copy()
+    dead[1] = -np.inf
+    m3, l3 = mod.merge_chunks(o, dead)
+    m3b, l3b = mod.merge_chunks(o[[0, 2]], dead[[0, 2]])
+    _close(m3, m3b, what="empty chunk ignored (output)")
+    _close(l3, l3b, what="empty chunk ignored (lse)")
+    perm = [2, 0, 1]
+    m4, l4 = mod.merge_chunks(o[perm], lse[perm])
+    m5, l5 = mod.merge_chunks(o, lse)
+    _close(m4, m5, what="chunk order (output)")
+    _close(l4, l5, what="chunk order (lse)")
+    # Closed form for two chunks: weights are logistic in the lse difference.
+    w0 = 1.0 / (1.0 + np.exp(lse[1] - lse[0]))                     # [B, H, Nq]
+    want = w0.transpose(0, 2, 1)[..., None] * o[0] + (1 - w0).transpose(0, 2, 1)[..., None] * o[1]
+    m6, l6 = mod.merge_chunks(o[:2], lse[:2])
+    _close(m6, want, what="two-chunk weights")
+    _close(l6, np.logaddexp(lse[0], lse[1]), what="two-chunk lse")
+    allneg = np.full((C, B, H, Nq), -np.inf)
+    m7, l7 = mod.merge_chunks(o, allneg)
+    assert np.all(m7 == 0.0) and np.all(np.isneginf(l7)), "all-empty rows"
+
+
 FORWARD_PINS = [
     pin_rows_sum_to_one,
     pin_q_zero,
@@ -370,6 +501,12 @@ FORWARD_PINS = [
     pin_brute_force,
     pin_sampled_rows,
 ]
+CHUNK_PINS = [
+    pin_chunk_brute_force,
+    pin_chunk_merge_is_full_attention,
+    pin_chunk_global_offsets,
+    pin_merge_closed_forms,
+]
 BACKWARD_PINS = [
     pin_constant_v,
     pin_backward_invariants,
@@ -378,4 +515,4 @@ BACKWARD_PINS = [
     pin_worked_examples,
     pin_backward_head,
 ]
-ALL_PINS = FORWARD_PINS + BACKWARD_PINS
+ALL_PINS = FORWARD_PINS + CHUNK_PINS + BACKWARD_PINS

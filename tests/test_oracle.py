@@ -55,7 +55,8 @@ MUTATIONS = [
     ("scores transposed", "(qh @ kh.T)", "(kh @ qh.T)"),
     ("max over columns", "m = s.max(axis=1, keepdims=True)", "m = s.max(axis=0, keepdims=True)"),
     ("sum over columns", "l = e.sum(axis=1, keepdims=True)", "l = e.sum(axis=0, keepdims=True)"),
-    ("P transposed in PV", "o[b, r0:r1, h, :] = p @ vh", "o[b, r0:r1, h, :] = p.T @ vh"),
+    ("P transposed in PV", "o[b, r0:r1, h, :] = p @ vh\n                with np.errstate(divide=\"ignore\"):\n                    lse[b, h, r0:r1] = m + np.log(l)",
+     "o[b, r0:r1, h, :] = p.T @ vh\n                with np.errstate(divide=\"ignore\"):\n                    lse[b, h, r0:r1] = m + np.log(l)"),
     ("lse without max", "lse[b, h, r0:r1] = m + np.log(l)\n    return o, lse",
      "lse[b, h, r0:r1] = np.log(l)\n    return o, lse"),
     ("lse base 2", "lse[b, h, r0:r1] = m + np.log(l)\n    return o, lse",
@@ -72,6 +73,21 @@ MUTATIONS = [
     ("dV not transposed", "dv[b, :, h, :] += p.T @ doh[r0:r1]", "dv[b, :, h, :] += p @ doh[r0:r1]"),
     ("dV overwritten per chunk", "dv[b, :, h, :] += p.T @ doh[r0:r1]", "dv[b, :, h, :] = p.T @ doh[r0:r1]"),
     ("sampled row offset", "s = _scores(qi, kh, int(i), causal, scale)", "s = _scores(qi, kh, 0, causal, scale)"),
+    ("chunk mask includes the diagonal", "s = np.where(kpos > qpos, -np.inf, s)", "s = np.where(kpos >= qpos, -np.inf, s)"),
+    ("chunk mask flipped", "s = np.where(kpos > qpos, -np.inf, s)", "s = np.where(kpos < qpos, -np.inf, s)"),
+    ("chunk query offset from keys", "qpos = (q_start + np.arange(r0, r1))[:, None]",
+     "qpos = (k_start + np.arange(r0, r1))[:, None]"),
+    ("chunk row offset lost", "qpos = (q_start + np.arange(r0, r1))[:, None]",
+     "qpos = (q_start + np.arange(0, r1 - r0))[:, None]"),
+    ("chunk key offset ignored", "kpos = (k_start + np.arange(Nk))[None, :]", "kpos = np.arange(Nk)[None, :]"),
+    ("chunk P transposed", "o[b, r0:r1, h, :] = p @ vh\n                with np.errstate(divide=\"ignore\"):\n                    lse[b, h, r0:r1] = np.where(",
+     "o[b, r0:r1, h, :] = p[::-1] @ vh\n                with np.errstate(divide=\"ignore\"):\n                    lse[b, h, r0:r1] = np.where("),
+    ("empty chunk lse zero", "lse = np.full((B, H, Nq), -np.inf)", "lse = np.zeros((B, H, Nq))"),
+    ("merge lse without max", "lse = np.where(tot > 0, mx_safe + np.log(", "lse = np.where(tot > 0, np.log("),
+    ("merge weights unnormalised", "frac = np.where(tot[None] > 0, w / np.where(tot > 0, tot, 1.0)[None], 0.0)",
+     "frac = np.where(tot[None] > 0, w, 0.0)"),
+    ("merge weights not shifted", "w = np.exp(lse_parts - mx_safe[None])", "w = np.exp(lse_parts)"),
+    ("merge output layout", 'o = np.einsum("cbhn,cbnhd->bnhd", frac, o_parts)', 'o = np.einsum("cbhn,cbnhd->bnhd", frac[::-1], o_parts)'),
     ("head slice swapped", "sl = (slice(b, b + 1), slice(None), slice(h, h + 1), slice(None))",
      "sl = (slice(h, h + 1), slice(None), slice(b, b + 1), slice(None))"),
 ]
