@@ -8,7 +8,8 @@ raises.
 
 Tensors use the library's layouts: q, k, v, o, do, dq, dk, dv are
 torch.bfloat16 [B, N, H, d] contiguous CUDA (HIP) tensors; lse is
-torch.float32 [B, H, N].
+torch.float32 [B, H, N]. Chunk outputs (fa_fwd_chunk) are torch.float32
+[B, Nq, H, d]; fa_merge takes C of them stacked as [C, B, N, H, d].
 """
 
 from __future__ import annotations
@@ -25,6 +26,8 @@ __all__ = [
     "fa_fwd",
     "fa_bwd",
     "fa_bwd_workspace_bytes",
+    "fa_fwd_chunk",
+    "fa_merge",
     "fa_status_string",
     "fa_version",
     "EXPORTED_SYMBOLS",
@@ -32,7 +35,8 @@ __all__ = [
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libfa_mi355x.so"
-EXPORTED_SYMBOLS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_string", "fa_version")
+EXPORTED_SYMBOLS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd_chunk", "fa_merge",
+                    "fa_status_string", "fa_version")
 
 _lib = None
 
@@ -66,6 +70,11 @@ def load_library():
     lib.fa_fwd.restype = i
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, vp]
     lib.fa_bwd.restype = i
+    ll = ctypes.c_longlong
+    lib.fa_fwd_chunk.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, ll, ll, f, vp]
+    lib.fa_fwd_chunk.restype = i
+    lib.fa_merge.argtypes = [vp, vp, i, vp, vp, i, i, i, i, vp]
+    lib.fa_merge.restype = i
     lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i]
     lib.fa_bwd_workspace_bytes.restype = sz
     lib.fa_status_string.argtypes = [i]
@@ -167,3 +176,63 @@ def fa_bwd(q, k, v, o, lse, do, causal: bool, softmax_scale: Optional[float] = N
     if st != 0:
         raise FaError(st, "fa_bwd")
     return dq, dk, dv
+
+
+def fa_fwd_chunk(q, k, v, causal: bool, q_start: int = 0, k_start: int = 0,
+                 softmax_scale: Optional[float] = None, out=None, lse=None):
+    """Attention of the query chunk q (rows at global positions q_start..)
+    over the key chunk k, v (positions k_start..). Returns (o float32
+    [B, Nq, H, d], lse float32 [B, H, Nq]); rows that see no key get o = 0
+    and lse = -inf."""
+    import torch
+
+    _check_bnhd("q", q)
+    B, Nq, H, d = q.shape
+    _check_bnhd("k", k)
+    Nk = k.shape[1]
+    if k.shape[0] != B or tuple(k.shape[2:]) != (H, d):
+        raise ValueError(f"k has shape {tuple(k.shape)}, expected [{B}, Nk, {H}, {d}]")
+    _check_bnhd("v", v, k.shape)
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        out = torch.empty((B, Nq, H, d), dtype=torch.float32, device=q.device)
+    if out.dtype != torch.float32 or tuple(out.shape) != (B, Nq, H, d) or not out.is_cuda or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous float32 device tensor of shape {(B, Nq, H, d)}")
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    _check_lse(lse, B, Nq, H)
+    kp = k.data_ptr() if Nk > 0 else q.data_ptr()  # an empty chunk is not read
+    vp = v.data_ptr() if Nk > 0 else q.data_ptr()
+    st = load_library().fa_fwd_chunk(
+        q.data_ptr(), kp, vp, out.data_ptr(), lse.data_ptr(), B, Nq, Nk, H, d, int(bool(causal)),
+        int(q_start), int(k_start), scale, _stream_handle(q.device),
+    )
+    if st != 0:
+        raise FaError(st, "fa_fwd_chunk")
+    return out, lse
+
+
+def fa_merge(o_parts, lse_parts, out=None, lse=None):
+    """Combine C chunk results (o_parts float32 [C, B, N, H, d], lse_parts
+    float32 [C, B, H, N]) into (o bf16 [B, N, H, d], lse float32 [B, H, N])."""
+    import torch
+
+    if o_parts.dtype != torch.float32 or o_parts.dim() != 5 or not o_parts.is_cuda or not o_parts.is_contiguous():
+        raise ValueError("o_parts must be a contiguous float32 device tensor [C, B, N, H, d]")
+    C, B, N, H, d = o_parts.shape
+    if (lse_parts.dtype != torch.float32 or tuple(lse_parts.shape) != (C, B, H, N) or not lse_parts.is_cuda
+            or not lse_parts.is_contiguous()):
+        raise ValueError(f"lse_parts must be a contiguous float32 device tensor of shape {(C, B, H, N)}")
+    if out is None:
+        out = torch.empty((B, N, H, d), dtype=torch.bfloat16, device=o_parts.device)
+    _check_bnhd("out", out, (B, N, H, d))
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=o_parts.device)
+    _check_lse(lse, B, N, H)
+    st = load_library().fa_merge(
+        o_parts.data_ptr(), lse_parts.data_ptr(), C, out.data_ptr(), lse.data_ptr(), B, N, H, d,
+        _stream_handle(o_parts.device),
+    )
+    if st != 0:
+        raise FaError(st, "fa_merge")
+    return out, lse

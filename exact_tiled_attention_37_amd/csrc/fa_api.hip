@@ -14,6 +14,7 @@ namespace {
 constexpr int kVersion = 100;  // 0.1.0
 constexpr int kMaxDevices = 64;
 constexpr long long kMaxElems = (1LL << 31) - (1LL << 16);
+constexpr int kMaxMergeChunks = 65536;
 
 // 0 = not checked yet, 1 = gfx950, 2 = something else.
 std::atomic<int> g_device_state[kMaxDevices];
@@ -71,8 +72,54 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   st = check_device();
   if (st != FA_OK) return st;
   (void)hipGetLastError();  // do not report an earlier, unrelated error as ours
-  const fa::FwdArgs a{q, k, v, o, lse, B, N, H, softmax_scale, stream};
+  const fa::FwdArgs a{q, k, v, o, lse, B, N, N, H, 0, false, softmax_scale, stream};
   return dispatch(d, causal, [&](auto D, auto C) { return fa::launch_fwd<decltype(D)::value, decltype(C)::value>(a); });
+}
+
+fa_status fa_fwd_chunk(const void* q, const void* k, const void* v, float* o, float* lse, int B, int Nq,
+                       int Nk, int H, int d, int causal, long long q_start, long long k_start,
+                       float softmax_scale, hipStream_t stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if (B < 1 || Nq < 1 || Nk < 0 || H < 1) return FA_ERR_SHAPE;
+  fa_status st = check_shape(B, Nq, H, d);
+  if (st != FA_OK) return st;
+  if (Nk > 0 && (st = check_shape(B, Nk, H, d)) != FA_OK) return st;
+  if (!std::isfinite(softmax_scale)) return FA_ERR_SCALE;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
+    return FA_ERR_ALIGN;
+  st = check_device();
+  if (st != FA_OK) return st;
+  (void)hipGetLastError();
+  // Causal: key j is visible to query i iff j <= i + delta. Clamping delta to
+  // [-Nq, Nk - 1] keeps the same visible sets (below -Nq + 1 no row sees a
+  // key; from Nk - 1 on every row sees every key, which is the unmasked case).
+  int delta = 0;
+  if (causal) {
+    const long long dl = q_start - k_start;
+    if (dl >= (long long)Nk - 1) {
+      causal = 0;
+    } else {
+      delta = (int)(dl < -(long long)Nq ? -(long long)Nq : dl);
+    }
+  }
+  const fa::FwdArgs a{q, k, v, o, lse, B, Nq, Nk, H, delta, true, softmax_scale, stream};
+  return dispatch(d, causal, [&](auto D, auto C) { return fa::launch_fwd<decltype(D)::value, decltype(C)::value>(a); });
+}
+
+fa_status fa_merge(const float* o_parts, const float* lse_parts, int C, void* o, float* lse, int B, int N,
+                   int H, int d, hipStream_t stream) {
+  if (!o_parts || !lse_parts || !o || !lse) return FA_ERR_NULL;
+  fa_status st = check_shape(B, N, H, d);
+  if (st != FA_OK) return st;
+  if (C < 1 || C > kMaxMergeChunks) return FA_ERR_SHAPE;
+  if (!aligned(o_parts, 16) || !aligned(o, 16) || !aligned(lse_parts, 4) || !aligned(lse, 4)) return FA_ERR_ALIGN;
+  st = check_device();
+  if (st != FA_OK) return st;
+  (void)hipGetLastError();
+  const fa::MergeArgs a{o_parts, lse_parts, C, o, lse, B, N, H, stream};
+  const hipError_t e = d == 64 ? fa::launch_merge<64>(a) : fa::launch_merge<128>(a);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 size_t fa_bwd_workspace_bytes(int B, int N, int H, int d) {

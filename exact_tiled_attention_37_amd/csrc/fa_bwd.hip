@@ -124,10 +124,10 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   const long hoff = ((long)b * N * H + h) * D;
   const uint32_t tokb = (uint32_t)H * D * 2;
   const uint32_t nrec = (uint32_t)(N - 1) * tokb + D * 2;
-  const auto rq = make_rsrc(Q + hoff, nrec);
-  const auto rdo = make_rsrc(dO + hoff, nrec);
-  const auto rl = make_rsrc(lse2 + (long)head * N, (uint32_t)N * 4);
-  const auto rd = make_rsrc(dsum + (long)head * N, (uint32_t)N * 4);
+  const u32x4 rq = make_raw_rsrc(Q + hoff, nrec);
+  const u32x4 rdo = make_raw_rsrc(dO + hoff, nrec);
+  const u32x4 rl = make_raw_rsrc(lse2 + (long)head * N, (uint32_t)N * 4);
+  const u32x4 rd = make_raw_rsrc(dsum + (long)head * N, (uint32_t)N * 4);
 
   const int kb0 = kblk * kKvBlock;
   const int kw0 = kb0 + 32 * wave;
@@ -141,12 +141,12 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
     const uint32_t koff = row_off(mykey, N, tokb, 16 * g);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) kf[ks] = __builtin_bit_cast(bf16x8, buf_load16(rk, koff + 32 * ks) ^ k_sign);
-    const auto rv = make_rsrc(V + hoff, nrec);
+    const u32x4 rv = make_raw_rsrc(V + hoff, nrec);
 #pragma unroll
     for (int t = 0; t < TV::LOADS / 4; ++t) {
       const int u = wave + 4 * t;
       const uint32_t off = row_off(kb0 + TV::dma_row(u, lane), N, tokb, 16u * TV::dma_chunk(u, lane));
-      buf_load16_lds(rv, vblk + TV::dma_dst(u), off);
+      dma16(rv, vblk + TV::dma_dst(u), off);
     }
   }
 
@@ -157,13 +157,13 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
       const int u = wave + 4 * t;
       const uint32_t off = row_off(q0 + TQ::dma_row(u, lane), N, tokb, 16u * TQ::dma_chunk(u, lane));
       char* l = dst + TQ::dma_dst(u);
-      buf_load16_lds(rq, l, off);
-      buf_load16_lds(rdo, l + QT, off);
+      dma16(rq, l, off);
+      dma16(rdo, l + QT, off);
     }
     if (wave == 0) {  // 64 row terms per load; the 32 past this step are unused
       const uint32_t off = (uint32_t)(q0 + lane) * 4;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (FA_LDS void*)rows, 4, (int)off, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (FA_LDS void*)(rows + 64), 4, (int)off, 0, 0, 0);
+      dma4(rl, rows, off);
+      dma4(rd, rows + 64, off);
     }
   };
 
@@ -294,8 +294,8 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   const long hoff = ((long)b * N * H + h) * D;
   const uint32_t tokb = (uint32_t)H * D * 2;
   const uint32_t nrec = (uint32_t)(N - 1) * tokb + D * 2;
-  const auto rk = make_rsrc(K + hoff, nrec);
-  const auto rv = make_rsrc(V + hoff, nrec);
+  const u32x4 rk = make_raw_rsrc(K + hoff, nrec);
+  const u32x4 rv = make_raw_rsrc(V + hoff, nrec);
 
   const int qw0 = qblk * kQBlock + wave * 32;
   const int myq = qw0 + l32;
@@ -324,8 +324,8 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
       const int u = wave + 4 * t;
       const uint32_t off = row_off(tile * kKTile + T::dma_row(u, lane), N, tokb, 16u * T::dma_chunk(u, lane));
       char* l = dst + T::dma_dst(u);
-      buf_load16_lds(rk, l, off);
-      buf_load16_lds(rv, l + TILE, off);
+      dma16(rk, l, off);
+      dma16(rv, l + TILE, off);
     }
   };
 

@@ -163,16 +163,50 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t o
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
 }
 
-// 16 bytes per lane straight from memory into LDS (no registers): lane i of
-// the wave writes LDS bytes [lds + 16 i, lds + 16 i + 16). `lds` must be the
-// same for the whole wave.
-__device__ __forceinline__ void buf_load16_lds(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t off) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (FA_LDS void*)lds, 16, (int)off, 0, 0, 0);
+// The four descriptor words of the same resource, held in scalar registers,
+// for the loads below that are written as inline assembly.
+__device__ __forceinline__ u32x4 make_raw_rsrc(const void* base, uint32_t nbytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  u32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));  // stride 0
+  r[2] = __builtin_amdgcn_readfirstlane(nbytes);
+  r[3] = 0x00020000u;
+  return r;
+}
+
+// Loads straight from memory into LDS (no registers): lane i of the wave
+// writes LDS bytes [lds + W i, lds + W i + W) for W = 16 (dma16) or 4
+// (dma4); `lds` must be the same for the whole wave (it goes to M0).
+//
+// They are written as inline assembly on purpose. For the intrinsic form the
+// compiler tracks only a few LDS-DMA writes individually and otherwise
+// assumes that any pending one may alias a later LDS read, so it waits for
+// the prefetch of the next tile before reading the current one, which
+// serialises the pipeline. Here the loads are ordered only by the explicit
+// vmcnt waits placed before each barrier (wait_vmem / wait_vmem_leave); the
+// compiler's own vmcnt waits for register loads stay correct, because extra
+// loads only make a "at most n outstanding" wait stricter.
+__device__ __forceinline__ uint32_t lds_base(const void* lds) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const FA_LDS void*)lds);
+}
+__device__ __forceinline__ void dma16(const u32x4& r, const void* lds, uint32_t off) {
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(r), "{m0}"(lds_base(lds)) : "memory");
+}
+__device__ __forceinline__ void dma4(const u32x4& r, const void* lds, uint32_t off) {
+  asm volatile("buffer_load_dword %0, %1, 0 offen lds" ::"v"(off), "s"(r), "{m0}"(lds_base(lds)) : "memory");
 }
 
 // s_waitcnt vmcnt(0): all of this wave's vector memory loads (including the
 // ones that write LDS directly) have completed.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// s_waitcnt vmcnt(N): all but this wave's N most recent vector memory loads
+// have completed (loads complete in issue order for this counter).
+template <int N>
+__device__ __forceinline__ void wait_vmem_leave() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
 
 // Blocks are dispatched round-robin over the XCDs (block i goes to XCD i % 8).
 // Remap so that each XCD receives one contiguous range of logical blocks:

@@ -46,32 +46,43 @@ namespace fa {
 
 namespace {
 
-constexpr int kFwdBR = 128;     // query rows per workgroup
-constexpr int kFwdThreads = 256;
-
-// Per head dimension: keys per K/V tile and waves per SIMD. d = 64 uses
-// 32-key tiles so that three workgroups fit per CU (fewer registers and LDS
-// per workgroup); d = 128 uses 64-key tiles at two workgroups per CU.
+// Per head dimension: query rows per workgroup (32 per wave), keys per K/V
+// tile, LDS stages of the K/V ring and waves per SIMD. Both use 128 rows
+// (4 waves) per workgroup and a double-buffered ring; d = 128 takes 64-key
+// tiles at two workgroups per CU, d = 64 32-key tiles at three. (256-row
+// workgroups and deeper rings were measured slower: one workgroup per CU
+// leaves each workgroup's start and end exposed.)
 template <int D> struct FwdCfg;
-template <> struct FwdCfg<64> { static constexpr int BC = 32, WAVES_PER_SIMD = 3; };
-template <> struct FwdCfg<128> { static constexpr int BC = 64, WAVES_PER_SIMD = 2; };
+template <> struct FwdCfg<64> {
+  static constexpr int BR = 128, BC = 32, STAGES = 2, WAVES_PER_SIMD = 3;
+};
+template <> struct FwdCfg<128> {
+  static constexpr int BR = 128, BC = 64, STAGES = 2, WAVES_PER_SIMD = 2;
+};
 constexpr float kRescaleSlack = 8.f;  // log2 units a row max may exceed the running max
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kFwdThreads)
+// Nq query rows attend to Nk key rows. With the causal mask key j is visible
+// to query i iff j <= i + delta (delta = global position of query row 0 minus
+// that of key row 0; 0 for plain self-attention). F32OUT: O is written as
+// float32 (a chunk result that a merge combines later), otherwise bfloat16.
+template <int D, bool CAUSAL, bool F32OUT>
+__global__ __launch_bounds__(FwdCfg<D>::BR * 2)
 __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_PER_SIMD))) void fwd_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    bf16* __restrict__ O, float* __restrict__ LSE, int N, int H, int nqb, int total_blocks,
-    float c2, uint32_t q_sign) {
+    void* __restrict__ O, float* __restrict__ LSE, int Nq, int Nk, int delta, int H, int nqb,
+    int total_blocks, float c2, uint32_t q_sign) {
+  constexpr int kFwdBR = FwdCfg<D>::BR;            // query rows per workgroup
   constexpr int kFwdBC = FwdCfg<D>::BC;            // keys per K/V tile
+  constexpr int STAGES = FwdCfg<D>::STAGES;        // K/V tiles in the LDS ring
+  constexpr int NW = kFwdBR / 32;                  // waves per workgroup
   constexpr int KB = kFwdBC / 32;                  // 32-key score blocks per tile
   using T = Tile<kFwdBC, D>;                       // one K or V tile in LDS
   constexpr int TILE = T::BYTES;
-  constexpr int DMA_PER_WAVE = T::LOADS / 4;       // 1 KiB wave loads per tile per wave
+  static_assert(T::LOADS % NW == 0 || NW % T::LOADS == 0, "tile loads split evenly over the waves");
+  constexpr int DMA_PER_WAVE = (T::LOADS + NW - 1) / NW;  // 1 KiB wave loads per tile per wave and tensor
   constexpr int KS = D / 16;                       // MFMA k-steps over d
   constexpr int DB = D / 32;                       // 32-wide output column blocks
-  __shared__ __attribute__((aligned(1024))) char kv0[2 * TILE];  // K tile, then V tile
-  __shared__ __attribute__((aligned(1024))) char kv1[2 * TILE];
+  __shared__ __attribute__((aligned(1024))) char ring[STAGES * 2 * TILE];  // per stage: K tile, V tile
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -81,12 +92,13 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
   const int head = logical / nqb;                  // b * H + h
   const int qblk = nqb - 1 - (logical - head * nqb);  // longest causal rows first
   const int b = head / H, h = head - b * H;
-  const long hoff = ((long)b * N * H + h) * D;     // element offset of token 0
+  const long hq = ((long)b * Nq * H + h) * D;      // element offset of query / output token 0
+  const long hk = ((long)b * Nk * H + h) * D;      // element offset of key / value token 0
   const uint32_t tokb = (uint32_t)H * D * 2;       // bytes between tokens
-  const uint32_t nrec = (uint32_t)(N - 1) * tokb + D * 2;
-  const auto rq = make_rsrc(Q + hoff, nrec);
-  const auto rk = make_rsrc(K + hoff, nrec);
-  const auto rv = make_rsrc(V + hoff, nrec);
+  const auto rq = make_rsrc(Q + hq, (uint32_t)(Nq - 1) * tokb + D * 2);
+  const uint32_t nrec_k = Nk > 0 ? (uint32_t)(Nk - 1) * tokb + D * 2 : 0u;
+  const u32x4 rk = make_raw_rsrc(K + hk, nrec_k);
+  const u32x4 rv = make_raw_rsrc(V + hk, nrec_k);
 
   const int qw0 = qblk * kFwdBR + wave * 32;       // first query row of this wave
   const int myq = qw0 + l32;
@@ -94,25 +106,27 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
   // Q as the B operand of S^T = K Q^T: row myq, d = 16*ks + 8*g .. +7.
   bf16x8 qf[KS];
   {
-    const uint32_t qoff = row_off(myq, N, tokb, 16 * g);
+    const uint32_t qoff = row_off(myq, Nq, tokb, 16 * g);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, buf_load16(rq, qoff + 32 * ks) ^ q_sign);
   }
 
-  // LDS-DMA: wave load u = wave + 4 t of a tile; lane i fills the chunk
+  // LDS-DMA: wave load u = wave + NW t of a tile; lane i fills the chunk
   // (row, column) the layout assigns to it. A tile row is a key.
   auto issue = [&](int tile, char* dst) __attribute__((always_inline)) {
 #pragma unroll
     for (int t = 0; t < DMA_PER_WAVE; ++t) {
-      const int u = wave + 4 * t;
-      const uint32_t off = row_off(tile * kFwdBC + T::dma_row(u, lane), N, tokb, 16u * T::dma_chunk(u, lane));
+      const int u = wave + NW * t;
+      if (T::LOADS < NW && u >= T::LOADS) break;  // fewer loads than waves: the rest issue none
+      const uint32_t off = row_off(tile * kFwdBC + T::dma_row(u, lane), Nk, tokb, 16u * T::dma_chunk(u, lane));
       char* l = dst + T::dma_dst(u);
-      buf_load16_lds(rk, l, off);
-      buf_load16_lds(rv, l + TILE, off);
+      dma16(rk, l, off);
+      dma16(rv, l + TILE, off);
     }
   };
 
-  const int kv_len = CAUSAL ? min(N, (qblk + 1) * kFwdBR) : N;
+  // Keys up to the last one visible to the block's last row.
+  const int kv_len = CAUSAL ? max(0, min(Nk, (qblk + 1) * kFwdBR + delta)) : Nk;
   const int ntiles = (kv_len + kFwdBC - 1) / kFwdBC;
 
   f32x16 oacc[DB];
@@ -142,7 +156,7 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-          if ((CAUSAL && key > myq) || key >= N) s[kb][r] = -INFINITY;
+          if ((CAUSAL && key > myq + delta) || key >= Nk) s[kb][r] = -INFINITY;
         }
     }
     float mx = max16(s[0], -INFINITY);
@@ -188,49 +202,72 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
         oacc[db] = mfma32(a, pf[ks], oacc[db]);
       }
   };
+  // Tile j lives in stage j % STAGES. Iteration j first refills the stage
+  // that tile j - 1 used (every wave finished it before the last barrier)
+  // with tile j + STAGES - 1, computes tile j, then waits for its own loads
+  // of tile j + 1 (the loads of later tiles may stay in flight) and meets the
+  // other waves at the barrier, after which tile j + 1 is complete in LDS.
+  auto stage = [&](int j) __attribute__((always_inline)) { return ring + (j % STAGES) * (2 * TILE); };
+  static_assert(STAGES >= 2 && STAGES <= 4, "K/V ring depth");
+  auto wait_next = [&](int j) __attribute__((always_inline)) {
+    if constexpr (STAGES >= 4) {
+      if (j + 3 < ntiles) {  // tiles j + 2 and j + 3 may stay in flight
+        wait_vmem_leave<4 * DMA_PER_WAVE>();
+        return;
+      }
+    }
+    if constexpr (STAGES >= 3) {
+      if (j + 2 < ntiles) {  // tile j + 2 may stay in flight
+        wait_vmem_leave<2 * DMA_PER_WAVE>();
+        return;
+      }
+    }
+    wait_vmem();
+  };
+#pragma unroll
+  for (int t = 0; t < STAGES - 1; ++t)
+    if (t < ntiles) issue(t, stage(t));
+  wait_next(-1);
+  __syncthreads();
   // Tiles before jm need no mask for any wave of this workgroup; they run in
   // a loop of their own so that the masked variant never joins the hot loop.
-  // Both loops go through the tiles in pairs so that each LDS buffer is named
-  // statically (tile j lives in buffer j % 2).
-  const int jm = CAUSAL ? min(qblk * (kFwdBR / kFwdBC), N / kFwdBC) : N / kFwdBC;
-  issue(0, kv0);
-  wait_vmem();
-  __syncthreads();
+  // (causal: the tiles whose last key is visible to the block's first row)
+  const int jm = CAUSAL ? min(max(0, qblk * kFwdBR + delta + 1) / kFwdBC, Nk / kFwdBC) : Nk / kFwdBC;
   int j = 0;
-  for (; j + 1 < jm; j += 2) {
-    issue(j + 1, kv1);
-    compute(j, kv0, std::false_type{});
-    wait_vmem();
-    __syncthreads();
-    if (j + 2 < ntiles) issue(j + 2, kv0);
-    compute(j + 1, kv1, std::false_type{});
-    wait_vmem();
+  for (; j < jm; ++j) {
+    if (j + STAGES - 1 < ntiles) issue(j + STAGES - 1, stage(j + STAGES - 1));
+    compute(j, stage(j), std::false_type{});
+    wait_next(j);
     __syncthreads();
   }
-  for (; j < ntiles; j += 2) {
-    if (j + 1 < ntiles) issue(j + 1, kv1);
-    compute(j, kv0, std::true_type{});
-    wait_vmem();
-    __syncthreads();
-    if (j + 1 >= ntiles) break;
-    if (j + 2 < ntiles) issue(j + 2, kv0);
-    compute(j + 1, kv1, std::true_type{});
-    wait_vmem();
+  for (; j < ntiles; ++j) {
+    if (j + STAGES - 1 < ntiles) issue(j + STAGES - 1, stage(j + STAGES - 1));
+    // A tile whose first key lies past this wave's last row is fully masked
+    // for it and contributes nothing.
+    if (!CAUSAL || j * kFwdBC <= qw0 + 31 + delta) compute(j, stage(j), std::true_type{});
+    wait_next(j);
     __syncthreads();
   }
 
+  // A row that saw no key (possible only with a causal offset that puts every
+  // key after it) has l = 0: its output is 0 and its logsumexp -inf.
   const float l_tot = xhalf_sum(l_run);
-  const float inv = 1.f / l_tot;
-  if (myq < N) {
-    if (g == 0) LSE[(long)head * N + myq] = (m_run + log2f(l_tot)) * kLn2;
-    bf16* orow = O + hoff + (long)myq * H * D;
+  const bool seen = l_tot > 0.f;
+  const float inv = seen ? 1.f / l_tot : 0.f;
+  if (myq < Nq) {
+    if (g == 0) LSE[(long)head * Nq + myq] = seen ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+    const long row = hq + (long)myq * H * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int rq4 = 0; rq4 < 4; ++rq4) {
         f32x4 x = {oacc[db][4 * rq4] * inv, oacc[db][4 * rq4 + 1] * inv, oacc[db][4 * rq4 + 2] * inv,
                    oacc[db][4 * rq4 + 3] * inv};
-        *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * rq4 + 4 * g) = to_bf16x4(x);
+        const int col = 32 * db + 8 * rq4 + 4 * g;
+        if constexpr (F32OUT)
+          *reinterpret_cast<f32x4*>(static_cast<float*>(O) + row + col) = x;
+        else
+          *reinterpret_cast<bf16x4*>(static_cast<bf16*>(O) + row + col) = to_bf16x4(x);
       }
   }
 }
@@ -239,14 +276,20 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
 
 template <int D, bool CAUSAL>
 hipError_t launch_fwd(const FwdArgs& a) {
-  const int nqb = (a.N + kFwdBR - 1) / kFwdBR;
+  constexpr int BR = FwdCfg<D>::BR;
+  const int nqb = (a.Nq + BR - 1) / BR;
   const int total = a.B * a.H * nqb;
   const float c2 = fabsf(a.scale) * kLog2e;
   const uint32_t q_sign = a.scale < 0.f ? 0x80008000u : 0u;
-  hipLaunchKernelGGL((fwd_kernel<D, CAUSAL>), dim3(total), dim3(kFwdThreads), 0, a.stream,
-                     static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k),
-                     static_cast<const bf16*>(a.v), static_cast<bf16*>(a.o), a.lse, a.N, a.H, nqb,
-                     total, c2, q_sign);
+  const auto* q = static_cast<const bf16*>(a.q);
+  const auto* k = static_cast<const bf16*>(a.k);
+  const auto* v = static_cast<const bf16*>(a.v);
+  if (a.f32_out)
+    hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, true>), dim3(total), dim3(BR * 2), 0, a.stream, q, k, v, a.o,
+                       a.lse, a.Nq, a.Nk, a.delta, a.H, nqb, total, c2, q_sign);
+  else
+    hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, false>), dim3(total), dim3(BR * 2), 0, a.stream, q, k, v, a.o,
+                       a.lse, a.Nq, a.Nk, a.delta, a.H, nqb, total, c2, q_sign);
   return hipGetLastError();
 }
 

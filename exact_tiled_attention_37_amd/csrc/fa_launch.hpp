@@ -6,14 +6,28 @@
 
 namespace fa {
 
+// Nq query rows against Nk key rows; with the causal mask key j is visible
+// to query i iff j <= i + delta. f32_out selects a float32 output.
 struct FwdArgs {
   const void* q;
   const void* k;
   const void* v;
   void* o;
   float* lse;
-  int B, N, H;
+  int B, Nq, Nk, H;
+  int delta;
+  bool f32_out;
   float scale;
+  hipStream_t stream;
+};
+
+struct MergeArgs {
+  const float* o_parts;   // [C, B, N, H, d] float32
+  const float* lse_parts; // [C, B, H, N] float32
+  int C;
+  void* o;                // [B, N, H, d] bfloat16
+  float* lse;             // [B, H, N] float32
+  int B, N, H;
   hipStream_t stream;
 };
 
@@ -39,6 +53,9 @@ hipError_t launch_fwd(const FwdArgs& a);
 
 template <int D, bool CAUSAL>
 hipError_t launch_bwd(const BwdArgs& a);
+
+template <int D>
+hipError_t launch_merge(const MergeArgs& a);
 
 // Workspace layout of the backward pass: L * log2(e), then D; each part is a
 // float32 [B, H, N] array starting on a 256-byte boundary.

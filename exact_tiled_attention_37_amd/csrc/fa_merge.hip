@@ -1,0 +1,81 @@
+// Merge of attention results computed over disjoint key chunks.
+//
+// The Ring Attention entry on the "High-Bandwidth Memory" keyword page
+// computes attention block by block, each device's queries meeting one
+// key/value block per pass; the IPLEX post on FlashAttention-2 work
+// partitioning (section "Tiling preserves the attention calculation")
+// requires blocks to combine into the globally normalised result. Each chunk
+// c supplies its normalised output O_c and the natural-log logsumexp L_c of
+// its scaled scores; the combination is
+//     L = ln sum_c exp(L_c),   O = sum_c exp(L_c - L) O_c,
+// computed with the largest L_c as the shift so no exponent is positive.
+// Rows with L_c = -inf for every chunk saw no key: O = 0 and L = -inf.
+//
+// Memory-bound: per output row it reads C rows of d float32 plus C logsumexp
+// values and writes d bfloat16 plus one float. Rows are laid out [B, N, H]
+// in the outputs and in every chunk, so a wave reads whole contiguous rows;
+// D / 4 lanes cover one row with 16-byte loads.
+
+#include "fa_common.hpp"
+#include "fa_launch.hpp"
+
+namespace fa {
+
+namespace {
+
+constexpr int kMergeThreads = 256;
+
+template <int D>
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __restrict__ Op,
+                                                               const float* __restrict__ Lp, int C,
+                                                               bf16* __restrict__ O, float* __restrict__ L,
+                                                               int N, int H, long rows) {
+  constexpr int LPR = D / 4;                     // lanes per row
+  constexpr int RPB = kMergeThreads / LPR;       // rows per block
+  const long r = (long)blockIdx.x * RPB + threadIdx.x / LPR;
+  const int c4 = threadIdx.x % LPR;
+  if (r >= rows) return;
+  const int h = (int)(r % H);
+  const long bn = r / H;
+  const int n = (int)(bn % N);
+  const long b = bn / N;
+  const long lrow = (b * H + h) * N + n;         // index in a [B, H, N] array
+  const long lstride = rows;                     // B * H * N = B * N * H
+  const long ostride = rows * D;                 // elements per chunk of O
+
+  float m = -INFINITY;
+  for (int c = 0; c < C; ++c) m = fmaxf(m, Lp[c * lstride + lrow]);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float tot = 0.f;
+  if (m != -INFINITY) {
+    const float* op = Op + r * D + 4 * c4;
+#pragma unroll 4
+    for (int c = 0; c < C; ++c) {
+      const float w = fast_exp2((Lp[c * lstride + lrow] - m) * kLog2e);  // exp2(-inf) = 0
+      const f32x4 x = *reinterpret_cast<const f32x4*>(op + c * ostride);
+      tot += w;
+      acc += w * x;
+    }
+  }
+  const bool seen = tot > 0.f;
+  const float inv = seen ? 1.f / tot : 0.f;
+  *reinterpret_cast<bf16x4*>(O + r * D + 4 * c4) = to_bf16x4(acc * inv);
+  if (c4 == 0) L[lrow] = seen ? m + logf(tot) : -INFINITY;
+}
+
+}  // namespace
+
+template <int D>
+hipError_t launch_merge(const MergeArgs& a) {
+  constexpr int RPB = kMergeThreads / (D / 4);
+  const long rows = (long)a.B * a.N * a.H;
+  const unsigned grid = (unsigned)((rows + RPB - 1) / RPB);
+  hipLaunchKernelGGL((merge_kernel<D>), dim3(grid), dim3(kMergeThreads), 0, a.stream, a.o_parts, a.lse_parts,
+                     a.C, static_cast<bf16*>(a.o), a.lse, a.N, a.H, rows);
+  return hipGetLastError();
+}
+
+template hipError_t launch_merge<64>(const MergeArgs&);
+template hipError_t launch_merge<128>(const MergeArgs&);
+
+}  // namespace fa

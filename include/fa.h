@@ -104,6 +104,51 @@ FA_API fa_status fa_bwd(const void* q, const void* k, const void* v, const void*
                  int B, int N, int H, int d, int causal, float softmax_scale,
                  hipStream_t stream);
 
+/*
+ * Attention of a query chunk over a key chunk: the unit of blockwise
+ * attention in which a device keeps its queries and meets one key/value
+ * block at a time (Ring Attention entry on the "High-Bandwidth Memory"
+ * keyword page). Chunk results over disjoint key sets combine exactly with
+ * fa_merge into the globally normalised result (IPLEX post, section "Tiling
+ * preserves the attention calculation").
+ *
+ *   q          [B, Nq, H, d] bf16, query rows at global positions q_start ..
+ *   k, v       [B, Nk, H, d] bf16, key rows at global positions k_start ..
+ *   o          [B, Nq, H, d] float32 output: each row's attention output over
+ *              the keys of this chunk it can see, normalised over those keys
+ *              (16-byte aligned)
+ *   lse        [B, H, Nq] float32 output: natural-log logsumexp over the same
+ *              keys
+ *   causal     key j is visible to query i iff k_start + j <= q_start + i;
+ *              a row that sees no key of the chunk gets o = 0, lse = -inf.
+ *              Non-causal: every key of the chunk is visible (the starts are
+ *              then ignored).
+ *   Nq >= 1, Nk >= 0 (Nk = 0 is an empty chunk: o = 0, lse = -inf, and k, v
+ *   are not read). B*Nq*H*d and B*Nk*H*d must each be <= 2^31 - 2^16.
+ *   Errors as for fa_fwd (FA_ERR_SHAPE also for Nq < 1 or Nk < 0).
+ */
+FA_API fa_status fa_fwd_chunk(const void* q, const void* k, const void* v, float* o, float* lse,
+                       int B, int Nq, int Nk, int H, int d, int causal,
+                       long long q_start, long long k_start, float softmax_scale,
+                       hipStream_t stream);
+
+/*
+ * Exact combination of C chunk results over disjoint key sets (same
+ * sources as fa_fwd_chunk):
+ *   L = ln sum_c exp(L_c),   O = sum_c exp(L_c - L) O_c
+ * Rows whose L_c is -inf in every chunk get O = 0 and L = -inf.
+ *
+ *   o_parts    [C, B, N, H, d] float32 (C fa_fwd_chunk outputs back to back),
+ *              16-byte aligned
+ *   lse_parts  [C, B, H, N] float32 (the matching logsumexp arrays)
+ *   o          [B, N, H, d] bf16 output, rounded to nearest even
+ *   lse        [B, H, N] float32 output, natural log
+ *   1 <= C <= 65536; B, N, H >= 1; B*N*H*d <= 2^31 - 2^16; d = 64 or 128.
+ *   FA_ERR_SHAPE for a C, B, N or H out of range.
+ */
+FA_API fa_status fa_merge(const float* o_parts, const float* lse_parts, int C, void* o, float* lse,
+                   int B, int N, int H, int d, hipStream_t stream);
+
 /* Human-readable text of a status code (a static string; never NULL). */
 FA_API const char* fa_status_string(fa_status status);
 

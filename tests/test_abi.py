@@ -132,3 +132,56 @@ def test_binding_rejects_wrong_tensors(lib):
         fa.fa_fwd(q.float(), q, q, causal=False)
     with pytest.raises(ValueError):
         fa.fa_fwd(q[0], q, q, causal=False)
+
+
+def chunk(lib, q=P, k=P, v=P, o=P, lse=P, B=1, Nq=8, Nk=8, H=2, d=64, causal=1, qs=0, ks=0, scale=0.125):
+    return lib.fa_fwd_chunk(q, k, v, o, lse, B, Nq, Nk, H, d, causal, qs, ks, scale, None)
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "o", "lse"])
+def test_chunk_null_pointer(lib, which):
+    assert chunk(lib, **{which: None}) == FA_ERR_NULL
+
+
+@pytest.mark.parametrize("B,Nq,Nk,H", [(0, 8, 8, 2), (1, 0, 8, 2), (1, 8, -1, 2), (1, 8, 8, 0),
+                                       (4096, 65536, 8, 16), (1, 8, 1 << 28, 16)])
+def test_chunk_shape(lib, B, Nq, Nk, H):
+    assert chunk(lib, B=B, Nq=Nq, Nk=Nk, H=H) == FA_ERR_SHAPE
+
+
+def test_chunk_headdim_scale_alignment(lib):
+    assert chunk(lib, d=96) == FA_ERR_HEADDIM
+    assert chunk(lib, scale=float("nan")) == FA_ERR_SCALE
+    assert chunk(lib, o=P + 8) == FA_ERR_ALIGN  # float32 rows still need 16 bytes
+    assert chunk(lib, lse=P + 2) == FA_ERR_ALIGN
+
+
+def merge(lib, op=P, lp=P, C=3, o=P, lse=P, B=1, N=8, H=2, d=64):
+    return lib.fa_merge(op, lp, C, o, lse, B, N, H, d, None)
+
+
+@pytest.mark.parametrize("which", ["op", "lp", "o", "lse"])
+def test_merge_null_pointer(lib, which):
+    assert merge(lib, **{which: None}) == FA_ERR_NULL
+
+
+@pytest.mark.parametrize("C,B,N,H", [(0, 1, 8, 2), (65537, 1, 8, 2), (3, 0, 8, 2), (3, 1, 0, 2), (3, 1, 8, 0)])
+def test_merge_shape(lib, C, B, N, H):
+    assert merge(lib, C=C, B=B, N=N, H=H) == FA_ERR_SHAPE
+
+
+def test_merge_headdim_alignment(lib):
+    assert merge(lib, d=32) == FA_ERR_HEADDIM
+    assert merge(lib, op=P + 4) == FA_ERR_ALIGN
+    assert merge(lib, o=P + 8) == FA_ERR_ALIGN
+    assert merge(lib, lp=P + 1) == FA_ERR_ALIGN
+
+
+def test_binding_rejects_wrong_chunk_tensors(lib):
+    import torch
+
+    q = torch.zeros(1, 8, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):  # host tensors
+        fa.fa_fwd_chunk(q, q, q, causal=True)
+    with pytest.raises(ValueError):
+        fa.fa_merge(torch.zeros(2, 1, 8, 2, 64), torch.zeros(2, 1, 2, 8))

@@ -1,0 +1,201 @@
+"""GPU parity of the key-chunk entry points (fa_fwd_chunk, fa_merge) against
+the fp64 oracle, through the C ABI.
+
+A chunk result is float32, so its only rounding is that of the bf16
+probabilities inside the kernel; the same tolerances as the core path apply
+(max-abs 2e-2, mean-abs 2e-3 on outputs, 1e-3 on logsumexp). Rows that see no
+key must come back exactly as o = 0 and lse = -inf.
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import exact_tiled_attention_37_amd as fa
+import oracle
+import seeded_inputs as si
+
+pytestmark = pytest.mark.gpu
+
+MAX_TOL, MEAN_TOL, LSE_TOL = 2e-2, 2e-3, 1e-3
+
+
+def announce(msg):
+    sys.__stderr__.write(f"[gpu-case] {msg}\n")
+    sys.__stderr__.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible: GPU tests need an MI355X")
+    fa.load_library()
+
+
+def dev(bits):
+    return si.bits_to_torch(bits, "cuda")
+
+
+def f64(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def check(name, got, ref, max_tol=MAX_TOL, mean_tol=MEAN_TOL):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, f"{name}: shape {got.shape} vs {ref.shape}"
+    assert np.all(np.isfinite(got)), f"{name}: non-finite values"
+    if got.size == 0:
+        return
+    err = np.abs(got - ref)
+    mx, mn = float(err.max()), float(err.mean())
+    assert mx <= max_tol and mn <= mean_tol, (
+        f"{name}: max-abs {mx:.3e} (tol {max_tol}), mean-abs {mn:.3e} (tol {mean_tol}), "
+        f"at {np.unravel_index(int(err.argmax()), err.shape)}"
+    )
+
+
+def check_chunk(o, lse, ro, rl):
+    """Empty rows exactly (o = 0, lse = -inf); the rest within tolerance."""
+    empty = np.isneginf(rl)                                   # [B, H, Nq]
+    assert np.array_equal(np.isneginf(lse), empty), "rows without a visible key differ"
+    empty_rows = empty.transpose(0, 2, 1)                     # [B, Nq, H]
+    assert np.all(o[empty_rows] == 0.0), "rows without a visible key must be zero"
+    check("O_c", o, ro)
+    check("L_c", lse[~empty], rl[~empty], LSE_TOL, LSE_TOL)
+
+
+def draw_chunk(B, Nq, Nk, H, d, seed):
+    bits = si.draw(B, max(Nq, Nk), H, d, seed)
+    return bits["q"][:, :Nq].copy(), bits["k"][:, :Nk].copy(), bits["v"][:, :Nk].copy()
+
+
+CHUNKS = [
+    # (B, Nq, Nk, H, d, q_start, k_start)
+    (1, 130, 200, 2, 128, 0, 0),
+    (2, 70, 333, 1, 64, 300, 0),       # causal: early rows see part of the chunk
+    (1, 100, 64, 2, 128, 0, 50),       # causal: rows 0..49 see no key
+    (1, 64, 96, 2, 64, 1000, 0),       # causal: chunk wholly in the past
+    (1, 64, 96, 2, 64, 0, 1000),       # causal: chunk wholly in the future
+    (1, 257, 129, 3, 128, 129, 64),
+    (1, 33, 1, 1, 64, 5, 5),
+    (2, 300, 700, 2, 128, 520, 17),
+]
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+@pytest.mark.parametrize("case", CHUNKS, ids=lambda c: "B%dNq%dNk%dH%dd%d_q%d_k%d" % c)
+def test_chunk_small(case, causal):
+    import torch
+
+    B, Nq, Nk, H, d, qs, ks = case
+    seed = 5000 + Nq + 3 * Nk + d
+    scale = 1.0 / math.sqrt(d)
+    announce(f"chunk case={case} causal={causal} seed={seed}")
+    qb, kb, vb = draw_chunk(B, Nq, Nk, H, d, seed)
+    ro, rl = oracle.attention_forward_chunk(si.bf16_bits_to_f64(qb), si.bf16_bits_to_f64(kb),
+                                            si.bf16_bits_to_f64(vb), causal, scale, qs, ks)
+    o, lse = fa.fa_fwd_chunk(dev(qb), dev(kb), dev(vb), causal, qs, ks, scale)
+    torch.cuda.synchronize()
+    check_chunk(f64(o), f64(lse), ro, rl)
+
+
+def test_empty_chunk():
+    import torch
+
+    announce("chunk Nk=0")
+    qb, _, _ = draw_chunk(1, 40, 1, 2, 64, 77)
+    q = dev(qb)
+    k = torch.empty((1, 0, 2, 64), dtype=torch.bfloat16, device="cuda")
+    o = torch.full((1, 40, 2, 64), 7.0, device="cuda")
+    lse = torch.full((1, 2, 40), 7.0, device="cuda")
+    fa.fa_fwd_chunk(q, k, k, True, 0, 0, 0.125, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.all(o == 0).item() and torch.all(torch.isneginf(lse)).item()
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_chunks_merge_to_full_attention(d, causal):
+    """Keys split into chunks, each attended with its global offset, merged:
+    the result is full attention (compared with the oracle's)."""
+    import torch
+
+    B, N, H = 1, 700, 2
+    seed = 6100 + d + int(causal)
+    scale = 1.0 / math.sqrt(d)
+    announce(f"chunks->merge N={N} d={d} causal={causal} seed={seed}")
+    bits = si.draw(B, N, H, d, seed)
+    q, k, v = dev(bits["q"]), dev(bits["k"]), dev(bits["v"])
+    bounds = [0, 100, 356, 357, 700]
+    parts = [fa.fa_fwd_chunk(q, k[:, a:b].contiguous(), v[:, a:b].contiguous(), causal, 0, a, scale)
+             for a, b in zip(bounds[:-1], bounds[1:])]
+    o, lse = fa.fa_merge(torch.stack([p[0] for p in parts]).contiguous(),
+                         torch.stack([p[1] for p in parts]).contiguous())
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention_forward(*(si.bf16_bits_to_f64(bits[n]) for n in ("q", "k", "v")), causal, scale)
+    check("merged O", f64(o), ro)
+    check("merged LSE", f64(lse), rl, LSE_TOL, LSE_TOL)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_merge_against_oracle(d):
+    """Random chunk results, including chunks and rows with lse = -inf."""
+    import torch
+
+    C, B, N, H = 5, 2, 37, 3
+    announce(f"merge C={C} d={d}")
+    rng = np.random.Generator(np.random.PCG64(8800 + d))
+    o_parts = rng.standard_normal((C, B, N, H, d)).astype(np.float32)
+    lse_parts = (rng.standard_normal((C, B, H, N)) * 4.0).astype(np.float32)
+    lse_parts[1] = -np.inf                 # an empty chunk
+    lse_parts[:, 0, 1, 5] = -np.inf        # a row empty in every chunk
+    lse_parts[2:, 1, 2, 7] = -np.inf       # a row only the first chunks see
+    o_parts[lse_parts.transpose(0, 1, 3, 2) == -np.inf] = 0.0
+    ro, rl = oracle.merge_chunks(o_parts.astype(np.float64), lse_parts.astype(np.float64))
+    o, lse = fa.fa_merge(torch.from_numpy(o_parts).cuda(), torch.from_numpy(lse_parts).cuda())
+    torch.cuda.synchronize()
+    got_l = f64(lse)
+    empty = np.isneginf(rl)
+    assert np.array_equal(np.isneginf(got_l), empty)
+    check("merge O", f64(o), ro)
+    check("merge LSE", got_l[~empty], rl[~empty], LSE_TOL, LSE_TOL)
+
+
+# One rank's share of the long sequence split over 8 ranks: 2048 query rows
+# at global position r * 2048 against the 2048-key chunks 0..r (causal),
+# merged. Sampled rows are compared with full causal attention over all
+# 16384 keys.
+RING_RANKS = 8
+
+
+@pytest.mark.parametrize("rank", [7, 2])
+def test_ring_rank_workload(rank):
+    import torch
+
+    w = si.WORKLOADS["long_causal"]
+    n = w.N // RING_RANKS
+    announce(f"ring rank={rank} of {RING_RANKS} on {w.name}")
+    bits = si.draw_workload(w)
+    q, k, v = dev(bits["q"]), dev(bits["k"]), dev(bits["v"])
+    qc = q[:, rank * n:(rank + 1) * n].contiguous()
+    parts = []
+    for c in range(rank + 1):
+        kc = k[:, c * n:(c + 1) * n].contiguous()
+        vc = v[:, c * n:(c + 1) * n].contiguous()
+        parts.append(fa.fa_fwd_chunk(qc, kc, vc, True, rank * n, c * n, w.scale))
+    o, lse = fa.fa_merge(torch.stack([p[0] for p in parts]).contiguous(),
+                         torch.stack([p[1] for p in parts]).contiguous())
+    torch.cuda.synchronize()
+    rng = np.random.Generator(np.random.PCG64(9000 + rank))
+    rows = np.sort(rng.choice(n, size=12, replace=False))
+    rows[0] = 0
+    for h in (0, 9):
+        qh, kh, vh = (si.bf16_bits_to_f64(bits[t][:, :, h:h + 1]) for t in ("q", "k", "v"))
+        ro, rl = oracle.attention_forward_rows(qh, kh, vh, True, w.scale, 0, 0, rank * n + rows)
+        check(f"ring O h={h}", f64(o[0, rows, h]), ro)
+        check(f"ring LSE h={h}", f64(lse[0, h, rows]), rl, LSE_TOL, LSE_TOL)
