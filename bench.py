@@ -75,6 +75,8 @@ def parse():
     ap.add_argument("--cpu-heads", type=int, default=8,
                     help="heads of the workload the CPU oracle baseline runs (0 = skip)")
     ap.add_argument("--no-sweep", action="store_true", help="skip the forward sweep over the other workloads")
+    ap.add_argument("--no-ring", action="store_true",
+                    help="skip the key-chunk leg (one rank's share of the 16384-token sequence over 8 ranks)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (3 times) so that profiler byte "
                          "counters can be scaled against a transfer of known size")
@@ -93,6 +95,61 @@ def time_calls(fn, n, stream):
     stop.record(stream)
     stop.synchronize()
     return start.elapsed_time(stop) / 1e3 / n
+
+
+RING_RANKS = 8
+
+
+def ring_rank_leg(fa, si, torch, dev, stream):
+    """One rank's share of the 16384-token causal workload split over 8
+    ranks (rank 7, the busiest): its 2048 query rows attend to the 2048-key
+    chunks 0..7 with their global positions (fa_fwd_chunk, written straight
+    into the stacked chunk buffer), then fa_merge combines the 8 results.
+    FLOPs count 4*B*H*n^2*d per chunk, halved for the diagonal one; the merge
+    is priced by its algorithmic bytes against HBM bandwidth."""
+    w = si.WORKLOADS["long_causal"]
+    n = w.N // RING_RANKS
+    r = RING_RANKS - 1
+    C = r + 1
+    b = si.draw_workload(w)
+    q, k, v = (si.bits_to_torch(b[t], dev) for t in ("q", "k", "v"))
+    qc = q[:, r * n:(r + 1) * n].contiguous()
+    kcs = [k[:, c * n:(c + 1) * n].contiguous() for c in range(C)]
+    vcs = [v[:, c * n:(c + 1) * n].contiguous() for c in range(C)]
+    del q, k, v
+    o_parts = torch.empty((C, w.B, n, w.H, w.d), dtype=torch.float32, device=dev)
+    l_parts = torch.empty((C, w.B, w.H, n), dtype=torch.float32, device=dev)
+    o = torch.empty((w.B, n, w.H, w.d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.B, w.H, n), dtype=torch.float32, device=dev)
+
+    def chunks():
+        for c in range(C):
+            fa.fa_fwd_chunk(qc, kcs[c], vcs[c], True, r * n, c * n, w.scale, out=o_parts[c], lse=l_parts[c])
+
+    def merge():
+        fa.fa_merge(o_parts, l_parts, out=o, lse=lse)
+
+    for _ in range(3):
+        chunks()
+        merge()
+    torch.cuda.synchronize()
+    t_chunks = time_calls(chunks, 10, stream)
+    t_merge = time_calls(merge, 20, stream)
+    flops = 4.0 * w.B * w.H * n * n * w.d * (C - 0.5)
+    rows = w.B * n * w.H
+    mbytes = C * rows * (w.d * 4 + 4) + rows * (w.d * 2 + 4)
+    tf = flops / t_chunks / 1e12
+    gbs = mbytes / t_merge / 1e9
+    return {
+        "config": f"rank {r} of {RING_RANKS}: B={w.B} H={w.H} d={w.d}, {n} query rows at position {r * n}, "
+                  f"{C} causal key chunks of {n}",
+        "chunks_ms": round(t_chunks * 1e3, 4), "chunks_tflops": round(tf, 2),
+        "chunks_frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+        "merge_ms": round(t_merge * 1e3, 4),
+        "merge_roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                           "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes_per_launch": int(mbytes)},
+        "total_ms": round((t_chunks + t_merge) * 1e3, 4),
+    }
 
 
 def main():
@@ -215,6 +272,9 @@ def main():
                            "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
             del q2, k2, v2, o2, l2
         detail["fwd_sweep"] = sweep
+
+    if not args.no_ring:
+        detail["ring_rank"] = ring_rank_leg(fa, si, torch, dev, stream)
 
     cpu = None
     if args.cpu_heads > 0:
