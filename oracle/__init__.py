@@ -7,6 +7,7 @@ import this package; the HIP library and its Python binding never do.
 from .attention import (
     attention_backward,
     attention_backward_head,
+    attention_decode,
     attention_forward,
     attention_forward_chunk,
     attention_forward_rows,
@@ -18,6 +19,7 @@ __all__ = [
     "attention_forward_chunk",
     "attention_forward_rows",
     "merge_chunks",
+    "attention_decode",
     "attention_backward",
     "attention_backward_head",
 ]

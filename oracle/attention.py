@@ -252,3 +252,24 @@ def merge_chunks(o_parts, lse_parts):
         frac = np.where(tot[None] > 0, w / np.where(tot > 0, tot, 1.0)[None], 0.0)  # [C, B, H, Nq]
     o = np.einsum("cbhn,cbnhd->bnhd", frac, o_parts)
     return o, lse
+
+
+# ---------------------------------------------------------------------------
+# Decode-shaped attention: a few new query rows against a long key/value
+# history. The IPLEX post (section "Document the implementation
+# difference") separates prefill from decoding as workloads with different
+# bottlenecks but fixes no convention for the causal mask when the query and
+# key lengths differ. The plain reading, used here, is that the Nq queries
+# are the last Nq positions of the sequence the Nk keys cover (bottom-right
+# alignment): query row i sits at position Nk - Nq + i and sees key j iff
+# j <= Nk - Nq + i. That is the key-chunk definition above with
+# q_start = Nk - Nq and k_start = 0.
+
+
+def attention_decode(q, k, v, causal: bool, scale: float):
+    """Decode-shaped attention: q [B, Nq, H, d] as the last Nq positions of
+    the sequence of k, v [B, Nk, H, d]. Returns (O [B, Nq, H, d],
+    L [B, H, Nq]) in float64; with Nq > Nk the first Nq - Nk rows see no key
+    (O = 0, L = -inf)."""
+    nq, nk = np.shape(q)[1], np.shape(k)[1]
+    return attention_forward_chunk(q, k, v, causal, scale, q_start=nk - nq, k_start=0)

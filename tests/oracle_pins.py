@@ -489,6 +489,33 @@ def pin_merge_closed_forms(mod):
     assert np.all(m7 == 0.0) and np.all(np.isneginf(l7)), "all-empty rows"
 
 
+def pin_decode_alignment(mod):
+    """Decode-shaped attention (queries are the last Nq positions): with
+    Nq = Nk it is ordinary causal attention; a single causal query sees every
+    key (the non-causal result); each decode row equals the matching row of
+    causal attention over the whole sequence; and extra leading rows beyond
+    Nk see nothing."""
+    B, N, H, d = 1, 19, 2, 4
+    q, k, v = (_rand((B, N, H, d), 340 + t) for t in range(3))
+    o_full, l_full = mod.attention_forward(q, k, v, True, 0.7)
+    o_sq, l_sq = mod.attention_decode(q, k, v, True, 0.7)
+    _close(o_sq, o_full, what="square decode output")
+    _close(l_sq, l_full, what="square decode lse")
+    for nq in (1, 5):
+        o_dec, l_dec = mod.attention_decode(q[:, N - nq:], k, v, True, 0.7)
+        _close(o_dec, o_full[:, N - nq:], what="decode rows output")
+        _close(l_dec, l_full[:, :, N - nq:], what="decode rows lse")
+    o1, l1 = mod.attention_decode(q[:, :1], k, v, True, 0.7)
+    o1n, l1n = mod.attention_decode(q[:, :1], k, v, False, 0.7)
+    _close(o1, o1n, what="single query output")
+    _close(l1, l1n, what="single query lse")
+    o_long, l_long = mod.attention_decode(q[:, :7], k[:, :4], v[:, :4], True, 0.7)
+    assert np.all(o_long[:, :3] == 0.0) and np.all(np.isneginf(l_long[:, :, :3])), "rows before the first key"
+    o_tail, l_tail = mod.attention_forward_chunk(q[:, 3:7], k[:, :4], v[:, :4], True, 0.7, 0, 0)
+    _close(o_long[:, 3:], o_tail, what="rows from the first key on")
+    _close(l_long[:, :, 3:], l_tail, what="rows from the first key on (lse)")
+
+
 FORWARD_PINS = [
     pin_rows_sum_to_one,
     pin_q_zero,
@@ -506,6 +533,7 @@ CHUNK_PINS = [
     pin_chunk_merge_is_full_attention,
     pin_chunk_global_offsets,
     pin_merge_closed_forms,
+    pin_decode_alignment,
 ]
 BACKWARD_PINS = [
     pin_constant_v,

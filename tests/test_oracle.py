@@ -88,6 +88,10 @@ MUTATIONS = [
      "frac = np.where(tot[None] > 0, w, 0.0)"),
     ("merge weights not shifted", "w = np.exp(lse_parts - mx_safe[None])", "w = np.exp(lse_parts)"),
     ("merge output layout", 'o = np.einsum("cbhn,cbnhd->bnhd", frac, o_parts)', 'o = np.einsum("cbhn,cbnhd->bnhd", frac[::-1], o_parts)'),
+    ("decode top-left alignment", "return attention_forward_chunk(q, k, v, causal, scale, q_start=nk - nq, k_start=0)",
+     "return attention_forward_chunk(q, k, v, causal, scale, q_start=0, k_start=0)"),
+    ("decode offset off by one", "return attention_forward_chunk(q, k, v, causal, scale, q_start=nk - nq, k_start=0)",
+     "return attention_forward_chunk(q, k, v, causal, scale, q_start=nk - nq - 1, k_start=0)"),
     ("head slice swapped", "sl = (slice(b, b + 1), slice(None), slice(h, h + 1), slice(None))",
      "sl = (slice(h, h + 1), slice(None), slice(b, b + 1), slice(None))"),
 ]
