@@ -28,6 +28,8 @@ __all__ = [
     "fa_bwd_workspace_bytes",
     "fa_fwd_chunk",
     "fa_merge",
+    "fa_decode",
+    "fa_decode_workspace_bytes",
     "fa_status_string",
     "fa_version",
     "EXPORTED_SYMBOLS",
@@ -35,8 +37,8 @@ __all__ = [
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libfa_mi355x.so"
-EXPORTED_SYMBOLS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd_chunk", "fa_merge",
-                    "fa_status_string", "fa_version")
+EXPORTED_SYMBOLS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd_chunk", "fa_merge", "fa_decode",
+                    "fa_decode_workspace_bytes", "fa_status_string", "fa_version")
 
 _lib = None
 
@@ -75,6 +77,10 @@ def load_library():
     lib.fa_fwd_chunk.restype = i
     lib.fa_merge.argtypes = [vp, vp, i, vp, vp, i, i, i, i, vp]
     lib.fa_merge.restype = i
+    lib.fa_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
+    lib.fa_decode.restype = i
+    lib.fa_decode_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.fa_decode_workspace_bytes.restype = sz
     lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i]
     lib.fa_bwd_workspace_bytes.restype = sz
     lib.fa_status_string.argtypes = [i]
@@ -235,4 +241,43 @@ def fa_merge(o_parts, lse_parts, out=None, lse=None):
     )
     if st != 0:
         raise FaError(st, "fa_merge")
+    return out, lse
+
+
+def fa_decode_workspace_bytes(B: int, Nq: int, Nk: int, H: int, d: int) -> int:
+    return int(load_library().fa_decode_workspace_bytes(B, Nq, Nk, H, d))
+
+
+def fa_decode(q, k, v, causal: bool, softmax_scale: Optional[float] = None, out=None, lse=None,
+              workspace=None):
+    """Decode-shaped attention: q [B, Nq, H, d] holds the last Nq positions
+    of the sequence whose keys and values are k, v [B, Nk, H, d]. Returns
+    (o bf16 [B, Nq, H, d], lse float32 [B, H, Nq])."""
+    import torch
+
+    _check_bnhd("q", q)
+    B, Nq, H, d = q.shape
+    _check_bnhd("k", k)
+    Nk = k.shape[1]
+    if k.shape[0] != B or tuple(k.shape[2:]) != (H, d):
+        raise ValueError(f"k has shape {tuple(k.shape)}, expected [{B}, Nk, {H}, {d}]")
+    _check_bnhd("v", v, k.shape)
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        out = torch.empty_like(q)
+    _check_bnhd("out", out, q.shape)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    _check_lse(lse, B, Nq, H)
+    need = fa_decode_workspace_bytes(B, Nq, Nk, H, d)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = load_library().fa_decode(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, Nq, Nk, H, d,
+        int(bool(causal)), scale, ws_ptr, ws_len, _stream_handle(q.device),
+    )
+    if st != 0:
+        raise FaError(st, "fa_decode")
     return out, lse

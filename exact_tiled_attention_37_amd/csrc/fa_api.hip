@@ -107,6 +107,42 @@ fa_status fa_fwd_chunk(const void* q, const void* k, const void* v, float* o, fl
   return dispatch(d, causal, [&](auto D, auto C) { return fa::launch_fwd<decltype(D)::value, decltype(C)::value>(a); });
 }
 
+size_t fa_decode_workspace_bytes(int B, int Nq, int Nk, int H, int d) {
+  if (check_shape(B, Nq, H, d) != FA_OK || check_shape(B, Nk, H, d) != FA_OK) return 0;
+  return fa::decode_workspace_bytes(B, Nq, Nk, H, d);
+}
+
+fa_status fa_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Nq, int Nk,
+                    int H, int d, int causal, float softmax_scale, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if (B < 1 || Nq < 1 || Nk < 1 || H < 1) return FA_ERR_SHAPE;
+  fa_status st = check_shape(B, Nq, H, d);
+  if (st != FA_OK || (st = check_shape(B, Nk, H, d)) != FA_OK) return st;
+  if (!std::isfinite(softmax_scale)) return FA_ERR_SCALE;
+  const size_t need = fa::decode_workspace_bytes(B, Nq, Nk, H, d);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return FA_ERR_WORKSPACE;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4) ||
+      (need > 0 && !aligned(workspace, 256)))
+    return FA_ERR_ALIGN;
+  st = check_device();
+  if (st != FA_OK) return st;
+  (void)hipGetLastError();
+  // The queries are the last Nq positions: key j is visible to query i iff
+  // j <= i + Nk - Nq (clamped as in fa_fwd_chunk; a single query sees all).
+  int delta = 0;
+  if (causal) {
+    const long long dl = (long long)Nk - Nq;
+    if (dl >= (long long)Nk - 1)
+      causal = 0;
+    else
+      delta = (int)(dl < -(long long)Nq ? -(long long)Nq : dl);
+  }
+  const fa::DecodeArgs a{q, k, v, o, lse, static_cast<float*>(workspace), B, Nq, Nk, H, delta, softmax_scale, stream};
+  return dispatch(d, causal, [&](auto D, auto C) { return fa::launch_decode<decltype(D)::value, decltype(C)::value>(a); });
+}
+
 fa_status fa_merge(const float* o_parts, const float* lse_parts, int C, void* o, float* lse, int B, int N,
                    int H, int d, hipStream_t stream) {
   if (!o_parts || !lse_parts || !o || !lse) return FA_ERR_NULL;

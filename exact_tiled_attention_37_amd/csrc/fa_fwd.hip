@@ -52,28 +52,37 @@ namespace {
 // tiles at two workgroups per CU, d = 64 32-key tiles at three. (256-row
 // workgroups and deeper rings were measured slower: one workgroup per CU
 // leaves each workgroup's start and end exposed.)
+template <int D_, int BR_, int BC_, int STAGES_, int WAVES_PER_SIMD_>
+struct KernelCfg {
+  static constexpr int D = D_, BR = BR_, BC = BC_, STAGES = STAGES_, WAVES_PER_SIMD = WAVES_PER_SIMD_;
+};
 template <int D> struct FwdCfg;
-template <> struct FwdCfg<64> {
-  static constexpr int BR = 128, BC = 32, STAGES = 2, WAVES_PER_SIMD = 3;
-};
-template <> struct FwdCfg<128> {
-  static constexpr int BR = 128, BC = 64, STAGES = 2, WAVES_PER_SIMD = 2;
-};
+template <> struct FwdCfg<64> : KernelCfg<64, 128, 32, 2, 3> {};
+template <> struct FwdCfg<128> : KernelCfg<128, 128, 64, 2, 2> {};
+// Decode-shaped calls (a few query rows against a long key history) are
+// bound by streaming K and V from memory, and their parallelism comes from
+// splitting the keys, not from query blocks: one wave per workgroup holds
+// all (up to 32) query rows of a (batch, head) and streams one key range.
+template <int D> struct DecCfg : KernelCfg<D, 32, kDecodeBC, 2, 2> {};
 constexpr float kRescaleSlack = 8.f;  // log2 units a row max may exceed the running max
 
 // Nq query rows attend to Nk key rows. With the causal mask key j is visible
 // to query i iff j <= i + delta (delta = global position of query row 0 minus
 // that of key row 0; 0 for plain self-attention). F32OUT: O is written as
 // float32 (a chunk result that a merge combines later), otherwise bfloat16.
-template <int D, bool CAUSAL, bool F32OUT>
-__global__ __launch_bounds__(FwdCfg<D>::BR * 2)
-__attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_PER_SIMD))) void fwd_kernel(
+// The keys may be split into nsplit ranges of split_len keys (a multiple of
+// the tile width), one workgroup each; split s writes its result at
+// O + s * o_split and LSE + s * l_split (elements).
+template <typename Cfg, bool CAUSAL, bool F32OUT>
+__global__ __launch_bounds__(Cfg::BR * 2)
+__attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD))) void fwd_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     void* __restrict__ O, float* __restrict__ LSE, int Nq, int Nk, int delta, int H, int nqb,
-    int total_blocks, float c2, uint32_t q_sign) {
-  constexpr int kFwdBR = FwdCfg<D>::BR;            // query rows per workgroup
-  constexpr int kFwdBC = FwdCfg<D>::BC;            // keys per K/V tile
-  constexpr int STAGES = FwdCfg<D>::STAGES;        // K/V tiles in the LDS ring
+    int nsplit, int split_len, long o_split, long l_split, int total_blocks, float c2, uint32_t q_sign) {
+  constexpr int D = Cfg::D;                        // head dimension
+  constexpr int kFwdBR = Cfg::BR;                  // query rows per workgroup
+  constexpr int kFwdBC = Cfg::BC;                  // keys per K/V tile
+  constexpr int STAGES = Cfg::STAGES;              // K/V tiles in the LDS ring
   constexpr int NW = kFwdBR / 32;                  // waves per workgroup
   constexpr int KB = kFwdBC / 32;                  // 32-key score blocks per tile
   using T = Tile<kFwdBC, D>;                       // one K or V tile in LDS
@@ -89,8 +98,11 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
   const int g = lane >> 5, l32 = lane & 31, G = lane >> 4;
 
   const int logical = xcd_remap(blockIdx.x, total_blocks);
-  const int head = logical / nqb;                  // b * H + h
-  const int qblk = nqb - 1 - (logical - head * nqb);  // longest causal rows first
+  const int per_head = nqb * nsplit;
+  const int head = logical / per_head;             // b * H + h
+  const int rest = logical - head * per_head;
+  const int qblk = nqb - 1 - rest / nsplit;        // longest causal rows first
+  const int split = rest - (rest / nsplit) * nsplit;
   const int b = head / H, h = head - b * H;
   const long hq = ((long)b * Nq * H + h) * D;      // element offset of query / output token 0
   const long hk = ((long)b * Nk * H + h) * D;      // element offset of key / value token 0
@@ -125,9 +137,14 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
     }
   };
 
-  // Keys up to the last one visible to the block's last row.
+  // Keys up to the last one visible to the block's last row, within this
+  // workgroup's key range [k_lo, k_lo + split_len): tiles j0 .. j1 - 1.
   const int kv_len = CAUSAL ? max(0, min(Nk, (qblk + 1) * kFwdBR + delta)) : Nk;
-  const int ntiles = (kv_len + kFwdBC - 1) / kFwdBC;
+  const int k_lo = split * split_len;
+  const int k_end = min(kv_len, k_lo + split_len);
+  const int j0 = k_lo / kFwdBC;
+  const int j1 = k_end > k_lo ? (k_end + kFwdBC - 1) / kFwdBC : j0;
+  const int ntiles = j1 - j0;
 
   f32x16 oacc[DB];
 #pragma unroll
@@ -202,22 +219,23 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
         oacc[db] = mfma32(a, pf[ks], oacc[db]);
       }
   };
-  // Tile j lives in stage j % STAGES. Iteration j first refills the stage
-  // that tile j - 1 used (every wave finished it before the last barrier)
-  // with tile j + STAGES - 1, computes tile j, then waits for its own loads
-  // of tile j + 1 (the loads of later tiles may stay in flight) and meets the
-  // other waves at the barrier, after which tile j + 1 is complete in LDS.
-  auto stage = [&](int j) __attribute__((always_inline)) { return ring + (j % STAGES) * (2 * TILE); };
+  // The t-th tile of the range (tile j0 + t) lives in stage t % STAGES.
+  // Iteration t first refills the stage that tile t - 1 used (every wave
+  // finished it before the last barrier) with tile t + STAGES - 1, computes
+  // tile t, then waits for its own loads of tile t + 1 (the loads of later
+  // tiles may stay in flight) and meets the other waves at the barrier,
+  // after which tile t + 1 is complete in LDS.
+  auto stage = [&](int t) __attribute__((always_inline)) { return ring + (t % STAGES) * (2 * TILE); };
   static_assert(STAGES >= 2 && STAGES <= 4, "K/V ring depth");
-  auto wait_next = [&](int j) __attribute__((always_inline)) {
+  auto wait_next = [&](int t) __attribute__((always_inline)) {
     if constexpr (STAGES >= 4) {
-      if (j + 3 < ntiles) {  // tiles j + 2 and j + 3 may stay in flight
+      if (t + 3 < ntiles) {  // tiles t + 2 and t + 3 may stay in flight
         wait_vmem_leave<4 * DMA_PER_WAVE>();
         return;
       }
     }
     if constexpr (STAGES >= 3) {
-      if (j + 2 < ntiles) {  // tile j + 2 may stay in flight
+      if (t + 2 < ntiles) {  // tile t + 2 may stay in flight
         wait_vmem_leave<2 * DMA_PER_WAVE>();
         return;
       }
@@ -226,26 +244,29 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
   };
 #pragma unroll
   for (int t = 0; t < STAGES - 1; ++t)
-    if (t < ntiles) issue(t, stage(t));
+    if (t < ntiles) issue(j0 + t, stage(t));
   wait_next(-1);
   __syncthreads();
   // Tiles before jm need no mask for any wave of this workgroup; they run in
   // a loop of their own so that the masked variant never joins the hot loop.
   // (causal: the tiles whose last key is visible to the block's first row)
-  const int jm = CAUSAL ? min(max(0, qblk * kFwdBR + delta + 1) / kFwdBC, Nk / kFwdBC) : Nk / kFwdBC;
-  int j = 0;
+  const int jm_all = CAUSAL ? min(max(0, qblk * kFwdBR + delta + 1) / kFwdBC, Nk / kFwdBC) : Nk / kFwdBC;
+  const int jm = min(max(jm_all, j0), j1);
+  int j = j0;
   for (; j < jm; ++j) {
-    if (j + STAGES - 1 < ntiles) issue(j + STAGES - 1, stage(j + STAGES - 1));
-    compute(j, stage(j), std::false_type{});
-    wait_next(j);
+    const int t = j - j0;
+    if (t + STAGES - 1 < ntiles) issue(j + STAGES - 1, stage(t + STAGES - 1));
+    compute(j, stage(t), std::false_type{});
+    wait_next(t);
     __syncthreads();
   }
-  for (; j < ntiles; ++j) {
-    if (j + STAGES - 1 < ntiles) issue(j + STAGES - 1, stage(j + STAGES - 1));
+  for (; j < j1; ++j) {
+    const int t = j - j0;
+    if (t + STAGES - 1 < ntiles) issue(j + STAGES - 1, stage(t + STAGES - 1));
     // A tile whose first key lies past this wave's last row is fully masked
     // for it and contributes nothing.
-    if (!CAUSAL || j * kFwdBC <= qw0 + 31 + delta) compute(j, stage(j), std::true_type{});
-    wait_next(j);
+    if (!CAUSAL || j * kFwdBC <= qw0 + 31 + delta) compute(j, stage(t), std::true_type{});
+    wait_next(t);
     __syncthreads();
   }
 
@@ -255,8 +276,8 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
   const bool seen = l_tot > 0.f;
   const float inv = seen ? 1.f / l_tot : 0.f;
   if (myq < Nq) {
-    if (g == 0) LSE[(long)head * Nq + myq] = seen ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
-    const long row = hq + (long)myq * H * D;
+    if (g == 0) LSE[split * l_split + (long)head * Nq + myq] = seen ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+    const long row = split * o_split + hq + (long)myq * H * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -285,17 +306,52 @@ hipError_t launch_fwd(const FwdArgs& a) {
   const auto* k = static_cast<const bf16*>(a.k);
   const auto* v = static_cast<const bf16*>(a.v);
   if (a.f32_out)
-    hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, true>), dim3(total), dim3(BR * 2), 0, a.stream, q, k, v, a.o,
-                       a.lse, a.Nq, a.Nk, a.delta, a.H, nqb, total, c2, q_sign);
+    hipLaunchKernelGGL((fwd_kernel<FwdCfg<D>, CAUSAL, true>), dim3(total), dim3(BR * 2), 0, a.stream, q, k, v,
+                       a.o, a.lse, a.Nq, a.Nk, a.delta, a.H, nqb, 1, a.Nk, 0L, 0L, total, c2, q_sign);
   else
-    hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, false>), dim3(total), dim3(BR * 2), 0, a.stream, q, k, v, a.o,
-                       a.lse, a.Nq, a.Nk, a.delta, a.H, nqb, total, c2, q_sign);
+    hipLaunchKernelGGL((fwd_kernel<FwdCfg<D>, CAUSAL, false>), dim3(total), dim3(BR * 2), 0, a.stream, q, k, v,
+                       a.o, a.lse, a.Nq, a.Nk, a.delta, a.H, nqb, 1, a.Nk, 0L, 0L, total, c2, q_sign);
   return hipGetLastError();
+}
+
+// Decode: the keys are split into ranges (decode_split); each range's result
+// goes to the float32 workspace and the merge combines them into o and lse.
+// With a single range the kernel writes o (bf16) and lse directly.
+template <int D, bool CAUSAL>
+hipError_t launch_decode(const DecodeArgs& a) {
+  using Cfg = DecCfg<D>;
+  const DecodeSplit sp = decode_split(a.B, a.Nq, a.Nk, a.H);
+  const int nqb = (a.Nq + Cfg::BR - 1) / Cfg::BR;
+  const int total = a.B * a.H * nqb * sp.nsplit;
+  const float c2 = fabsf(a.scale) * kLog2e;
+  const uint32_t q_sign = a.scale < 0.f ? 0x80008000u : 0u;
+  const auto* q = static_cast<const bf16*>(a.q);
+  const auto* k = static_cast<const bf16*>(a.k);
+  const auto* v = static_cast<const bf16*>(a.v);
+  if (sp.nsplit == 1) {
+    hipLaunchKernelGGL((fwd_kernel<Cfg, CAUSAL, false>), dim3(total), dim3(Cfg::BR * 2), 0, a.stream, q, k, v,
+                       a.o, a.lse, a.Nq, a.Nk, a.delta, a.H, nqb, 1, sp.split_len, 0L, 0L, total, c2, q_sign);
+    return hipGetLastError();
+  }
+  const long rows = (long)a.B * a.Nq * a.H;
+  float* o_parts = a.workspace;
+  float* l_parts = a.workspace + decode_part_elems((long)sp.nsplit * rows * D);
+  hipLaunchKernelGGL((fwd_kernel<Cfg, CAUSAL, true>), dim3(total), dim3(Cfg::BR * 2), 0, a.stream, q, k, v,
+                     o_parts, l_parts, a.Nq, a.Nk, a.delta, a.H, nqb, sp.nsplit, sp.split_len, rows * D, rows,
+                     total, c2, q_sign);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const MergeArgs m{o_parts, l_parts, sp.nsplit, a.o, a.lse, a.B, a.Nq, a.H, a.stream};
+  return launch_merge<D>(m);
 }
 
 template hipError_t launch_fwd<64, false>(const FwdArgs&);
 template hipError_t launch_fwd<64, true>(const FwdArgs&);
 template hipError_t launch_fwd<128, false>(const FwdArgs&);
 template hipError_t launch_fwd<128, true>(const FwdArgs&);
+template hipError_t launch_decode<64, false>(const DecodeArgs&);
+template hipError_t launch_decode<64, true>(const DecodeArgs&);
+template hipError_t launch_decode<128, false>(const DecodeArgs&);
+template hipError_t launch_decode<128, true>(const DecodeArgs&);
 
 }  // namespace fa

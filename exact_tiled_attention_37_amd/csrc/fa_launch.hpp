@@ -57,6 +57,56 @@ hipError_t launch_bwd(const BwdArgs& a);
 template <int D>
 hipError_t launch_merge(const MergeArgs& a);
 
+// Decode-shaped attention: Nq query rows (the last Nq positions) against Nk
+// keys, split into key ranges whose float32 results are merged.
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  float* workspace;  // decode_workspace_bytes() bytes, 256-byte aligned
+  int B, Nq, Nk, H;
+  int delta;         // causal: key j visible to query i iff j <= i + delta
+  float scale;
+  hipStream_t stream;
+};
+
+template <int D, bool CAUSAL>
+hipError_t launch_decode(const DecodeArgs& a);
+
+// Keys per tile of the decode kernel; key ranges are multiples of it.
+constexpr int kDecodeBC = 32;
+
+// Key split of a decode call: enough (batch, head, range) workgroups to keep
+// every CU streaming (about 2048), but ranges of at least 256 keys.
+struct DecodeSplit {
+  int nsplit, split_len;
+};
+inline DecodeSplit decode_split(long B, long Nq, long Nk, long H) {
+  constexpr long kTargetBlocks = 2048, kMinKeys = 256;
+  const long nqb = (Nq + 31) / 32;
+  const long tiles = (Nk + kDecodeBC - 1) / kDecodeBC;
+  const long units = B * H * nqb;
+  long s = (kTargetBlocks + units - 1) / units;
+  const long by_len = (Nk + kMinKeys - 1) / kMinKeys;
+  if (s > by_len) s = by_len;
+  if (s > tiles) s = tiles;
+  if (s < 1) s = 1;
+  const long len = (tiles + s - 1) / s * kDecodeBC;
+  return {(int)((Nk + len - 1) / len), (int)len};
+}
+// Workspace of a split decode call: the float32 partial outputs
+// [nsplit, B, Nq, H, d], then the partial logsumexps [nsplit, B, H, Nq],
+// each padded to a multiple of 256 bytes.
+inline long decode_part_elems(long elems) { return (elems + 63) / 64 * 64; }
+inline size_t decode_workspace_bytes(long B, long Nq, long Nk, long H, long D) {
+  const DecodeSplit sp = decode_split(B, Nq, Nk, H);
+  if (sp.nsplit == 1) return 0;
+  const long rows = B * Nq * H;
+  return (size_t)(decode_part_elems(sp.nsplit * rows * D) + decode_part_elems(sp.nsplit * rows)) * 4;
+}
+
 // Workspace layout of the backward pass: L * log2(e), then D; each part is a
 // float32 [B, H, N] array starting on a 256-byte boundary.
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }

@@ -149,6 +149,37 @@ FA_API fa_status fa_fwd_chunk(const void* q, const void* k, const void* v, float
 FA_API fa_status fa_merge(const float* o_parts, const float* lse_parts, int C, void* o, float* lse,
                    int B, int N, int H, int d, hipStream_t stream);
 
+/*
+ * Decode-shaped attention: a few new query rows against a long key/value
+ * history. The IPLEX post (section "Document the implementation
+ * difference") separates decoding from prefill as a workload with its own
+ * bottleneck: here it is streaming K and V from memory, so the keys are
+ * split into ranges processed in parallel and their results are combined
+ * exactly as fa_merge does (Ring Attention entry on the "High-Bandwidth
+ * Memory" keyword page; post section "Tiling preserves the attention
+ * calculation").
+ *
+ *   q          [B, Nq, H, d] bf16: the last Nq positions of the sequence
+ *   k, v       [B, Nk, H, d] bf16: the whole sequence's keys and values
+ *   o          [B, Nq, H, d] bf16 output (rounded to nearest even)
+ *   lse        [B, H, Nq] float32 output, natural log
+ *   causal     query row i sits at position Nk - Nq + i and sees key j iff
+ *              j <= Nk - Nq + i (bottom-right alignment); with Nq > Nk the
+ *              first Nq - Nk rows see no key and get o = 0, lse = -inf.
+ *              Non-causal: every key is visible.
+ *   workspace  device scratch of fa_decode_workspace_bytes(B, Nq, Nk, H, d)
+ *              bytes, 256-byte aligned, owned by the caller (may be NULL
+ *              when that size is 0); contents on entry do not matter. Two
+ *              calls in flight at once need two workspaces.
+ *   Nq, Nk >= 1 (any Nq; 1 ... 32 is the shape this entry point is built
+ *   for). Errors as for fa_fwd; FA_ERR_WORKSPACE for a missing or short
+ *   workspace.
+ */
+FA_API size_t fa_decode_workspace_bytes(int B, int Nq, int Nk, int H, int d);
+FA_API fa_status fa_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int B, int Nq, int Nk, int H, int d, int causal, float softmax_scale,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Human-readable text of a status code (a static string; never NULL). */
 FA_API const char* fa_status_string(fa_status status);
 

@@ -6,7 +6,8 @@ CPU oracle and the GPU library are fed the very same bits.
 
 Recipe (stated once, used everywhere):
   * generator  numpy.random.Generator(PCG64(seed))
-  * draw order Q, K, V, then dO (only when a backward is wanted)
+  * draw order Q, K, V, then dO (only when a backward is wanted); for
+               decode shapes Q has Nq rows and K, V have Nk rows
   * each draw  standard_normal((B, N, H, d), dtype=float32), C order,
                then fp32 -> bf16 round-to-nearest-even, kept as uint16 bits.
 
@@ -49,6 +50,34 @@ WORKLOADS = {
     "mid_causal": Workload("mid_causal", 8, 16, 2048, 128, True, False, 3),
     "long_causal": Workload("long_causal", 1, 16, 16384, 128, True, False, 4),
     "train_causal": Workload("train_causal", 4, 16, 4096, 128, True, True, 5),
+}
+
+
+@dataclass(frozen=True)
+class DecodeWorkload:
+    """A few new query rows (the last Nq positions) against Nk keys."""
+
+    name: str
+    B: int
+    H: int
+    Nq: int
+    Nk: int
+    d: int
+    causal: bool
+    seed: int
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+
+# Decode-shaped workloads (the post's section "Document the implementation
+# difference" sets decoding apart from prefill): one new token, a
+# speculative block of 16, and a d = 64 case, each against a long history.
+DECODE_WORKLOADS = {
+    "decode_1x8k": DecodeWorkload("decode_1x8k", 16, 16, 1, 8192, 128, True, 6),
+    "decode_16x16k": DecodeWorkload("decode_16x16k", 4, 16, 16, 16384, 128, True, 7),
+    "decode_4x4k_d64": DecodeWorkload("decode_4x4k_d64", 32, 16, 4, 4096, 64, True, 8),
 }
 
 
@@ -103,3 +132,18 @@ def torch_to_bits(t) -> np.ndarray:
     import torch
 
     return t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def draw_qkv(B: int, Nq: int, Nk: int, H: int, d: int, seed: int):
+    """Q [B, Nq, H, d] and K, V [B, Nk, H, d] as bf16 bits, drawn in that
+    order from one PCG64 stream (same recipe as `draw`)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = {}
+    for name, n in (("q", Nq), ("k", Nk), ("v", Nk)):
+        out[name] = f32_to_bf16_bits(rng.standard_normal((B, n, H, d), dtype=np.float32))
+    return out
+
+
+def draw_decode(w: DecodeWorkload):
+    return draw_qkv(w.B, w.Nq, w.Nk, w.H, w.d, w.seed)
+

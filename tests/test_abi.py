@@ -185,3 +185,49 @@ def test_binding_rejects_wrong_chunk_tensors(lib):
         fa.fa_fwd_chunk(q, q, q, causal=True)
     with pytest.raises(ValueError):
         fa.fa_merge(torch.zeros(2, 1, 8, 2, 64), torch.zeros(2, 1, 2, 8))
+
+
+def _decode_split(B, Nq, Nk, H):
+    """The library's key split for decode calls (mirrors its documented rule:
+    about 2048 workgroups, ranges of at least 256 keys, 32-key tiles)."""
+    bc = 32
+    nqb = (Nq + 31) // 32
+    tiles = (Nk + bc - 1) // bc
+    s = (2048 + B * H * nqb - 1) // (B * H * nqb)
+    s = max(1, min(s, (Nk + 255) // 256, tiles))
+    ln = (tiles + s - 1) // s * bc
+    return (Nk + ln - 1) // ln, ln
+
+
+@pytest.mark.parametrize("B,Nq,Nk,H,d", [(16, 1, 8192, 16, 128), (4, 16, 16384, 16, 128), (1, 1, 100, 1, 64),
+                                         (2, 40, 1000, 3, 64), (1, 5, 300, 2, 128)])
+def test_decode_workspace_bytes(lib, B, Nq, Nk, H, d):
+    ns, _ = _decode_split(B, Nq, Nk, H)
+    pad = lambda elems: (elems + 63) // 64 * 64
+    rows = B * Nq * H
+    want = 0 if ns == 1 else (pad(ns * rows * d) + pad(ns * rows)) * 4
+    assert fa.fa_decode_workspace_bytes(B, Nq, Nk, H, d) == want
+    assert fa.fa_decode_workspace_bytes(B, Nq, Nk, H, 96) == 0
+
+
+def decode(lib, q=P, k=P, v=P, o=P, lse=P, B=1, Nq=4, Nk=4096, H=2, d=64, causal=1, scale=0.125, ws=P,
+           ws_bytes=1 << 24):
+    return lib.fa_decode(q, k, v, o, lse, B, Nq, Nk, H, d, causal, scale, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "o", "lse"])
+def test_decode_null_pointer(lib, which):
+    assert decode(lib, **{which: None}) == FA_ERR_NULL
+
+
+def test_decode_errors(lib):
+    assert decode(lib, d=80) == FA_ERR_HEADDIM
+    assert decode(lib, Nq=0) == FA_ERR_SHAPE
+    assert decode(lib, Nk=0) == FA_ERR_SHAPE
+    assert decode(lib, scale=float("inf")) == FA_ERR_SCALE
+    need = fa.fa_decode_workspace_bytes(1, 4, 4096, 2, 64)
+    assert need > 0
+    assert decode(lib, ws=None) == FA_ERR_WORKSPACE
+    assert decode(lib, ws_bytes=need - 1) == FA_ERR_WORKSPACE
+    assert decode(lib, ws=P + 64, ws_bytes=need) == FA_ERR_ALIGN
+    assert decode(lib, q=P + 2) == FA_ERR_ALIGN
