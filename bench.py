@@ -75,6 +75,7 @@ def parse():
     ap.add_argument("--cpu-heads", type=int, default=8,
                     help="heads of the workload the CPU oracle baseline runs (0 = skip)")
     ap.add_argument("--no-sweep", action="store_true", help="skip the forward sweep over the other workloads")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode-shaped calls")
     ap.add_argument("--no-ring", action="store_true",
                     help="skip the key-chunk leg (one rank's share of the 16384-token sequence over 8 ranks)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -150,6 +151,37 @@ def ring_rank_leg(fa, si, torch, dev, stream):
                            "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes_per_launch": int(mbytes)},
         "total_ms": round((t_chunks + t_merge) * 1e3, 4),
     }
+
+
+def decode_leg(fa, si, torch, dev, stream):
+    """Decode-shaped calls (a few query rows against a long key history):
+    bound by streaming K and V from memory, so each is priced by its
+    algorithmic bytes (K, V, Q read; O and logsumexp written) against HBM
+    bandwidth; TFLOP/s (4*B*H*Nq*Nk*d) is reported beside it."""
+    out = {}
+    for name, w in si.DECODE_WORKLOADS.items():
+        b = si.draw_decode(w)
+        q, k, v = (si.bits_to_torch(b[t], dev) for t in ("q", "k", "v"))
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
+        need = fa.fa_decode_workspace_bytes(w.B, w.Nq, w.Nk, w.H, w.d)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        call = lambda: fa.fa_decode(q, k, v, w.causal, w.scale, out=o, lse=lse, workspace=ws)
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        t = time_calls(call, 50, stream)
+        kv = 2 * w.B * w.Nk * w.H * w.d * 2
+        byts = kv + 2 * (w.B * w.Nq * w.H * w.d * 2) + w.B * w.H * w.Nq * 4
+        gbs = byts / t / 1e9
+        out[name] = {"B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d, "causal": w.causal,
+                     "ms": round(t * 1e3, 4),
+                     "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                  "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes_per_launch": int(byts)},
+                     "tflops": round(4.0 * w.B * w.H * w.Nq * w.Nk * w.d / t / 1e12, 2),
+                     "workspace_bytes": int(need)}
+        del q, k, v, o, lse, ws
+    return out
 
 
 def main():
@@ -275,6 +307,8 @@ def main():
 
     if not args.no_ring:
         detail["ring_rank"] = ring_rank_leg(fa, si, torch, dev, stream)
+    if not args.no_decode:
+        detail["decode"] = decode_leg(fa, si, torch, dev, stream)
 
     cpu = None
     if args.cpu_heads > 0:

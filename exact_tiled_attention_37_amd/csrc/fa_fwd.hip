@@ -63,7 +63,11 @@ template <> struct FwdCfg<128> : KernelCfg<128, 128, 64, 2, 2> {};
 // bound by streaming K and V from memory, and their parallelism comes from
 // splitting the keys, not from query blocks: one wave per workgroup holds
 // all (up to 32) query rows of a (batch, head) and streams one key range.
-template <int D> struct DecCfg : KernelCfg<D, 32, kDecodeBC, 2, 2> {};
+// d = 64 keeps two tiles in flight per wave (3 stages; its tiles are half
+// the size), d = 128 one (measured best).
+template <int D> struct DecCfg;
+template <> struct DecCfg<64> : KernelCfg<64, 32, kDecodeBC, 3, 2> {};
+template <> struct DecCfg<128> : KernelCfg<128, 32, kDecodeBC, 2, 2> {};
 constexpr float kRescaleSlack = 8.f;  // log2 units a row max may exceed the running max
 
 // Nq query rows attend to Nk key rows. With the causal mask key j is visible
@@ -320,7 +324,7 @@ hipError_t launch_fwd(const FwdArgs& a) {
 template <int D, bool CAUSAL>
 hipError_t launch_decode(const DecodeArgs& a) {
   using Cfg = DecCfg<D>;
-  const DecodeSplit sp = decode_split(a.B, a.Nq, a.Nk, a.H);
+  const DecodeSplit sp = decode_split(a.B, a.Nq, a.Nk, a.H, D);
   const int nqb = (a.Nq + Cfg::BR - 1) / Cfg::BR;
   const int total = a.B * a.H * nqb * sp.nsplit;
   const float c2 = fabsf(a.scale) * kLog2e;

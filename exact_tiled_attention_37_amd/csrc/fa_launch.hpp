@@ -79,12 +79,13 @@ hipError_t launch_decode(const DecodeArgs& a);
 constexpr int kDecodeBC = 32;
 
 // Key split of a decode call: enough (batch, head, range) workgroups to keep
-// every CU streaming (about 2048), but ranges of at least 256 keys.
+// every CU streaming (about 2048 at d = 128, 4096 at d = 64, where a tile
+// holds half the bytes), but ranges of at least 256 keys.
 struct DecodeSplit {
   int nsplit, split_len;
 };
-inline DecodeSplit decode_split(long B, long Nq, long Nk, long H) {
-  constexpr long kTargetBlocks = 2048, kMinKeys = 256;
+inline DecodeSplit decode_split(long B, long Nq, long Nk, long H, long D) {
+  const long kTargetBlocks = D == 64 ? 4096 : 2048, kMinKeys = 256;
   const long nqb = (Nq + 31) / 32;
   const long tiles = (Nk + kDecodeBC - 1) / kDecodeBC;
   const long units = B * H * nqb;
@@ -101,7 +102,7 @@ inline DecodeSplit decode_split(long B, long Nq, long Nk, long H) {
 // each padded to a multiple of 256 bytes.
 inline long decode_part_elems(long elems) { return (elems + 63) / 64 * 64; }
 inline size_t decode_workspace_bytes(long B, long Nq, long Nk, long H, long D) {
-  const DecodeSplit sp = decode_split(B, Nq, Nk, H);
+  const DecodeSplit sp = decode_split(B, Nq, Nk, H, D);
   if (sp.nsplit == 1) return 0;
   const long rows = B * Nq * H;
   return (size_t)(decode_part_elems(sp.nsplit * rows * D) + decode_part_elems(sp.nsplit * rows)) * 4;

@@ -187,13 +187,15 @@ def test_binding_rejects_wrong_chunk_tensors(lib):
         fa.fa_merge(torch.zeros(2, 1, 8, 2, 64), torch.zeros(2, 1, 2, 8))
 
 
-def _decode_split(B, Nq, Nk, H):
+def _decode_split(B, Nq, Nk, H, d):
     """The library's key split for decode calls (mirrors its documented rule:
-    about 2048 workgroups, ranges of at least 256 keys, 32-key tiles)."""
+    about 2048 workgroups at d = 128 and 4096 at d = 64, ranges of at least
+    256 keys, 32-key tiles)."""
     bc = 32
     nqb = (Nq + 31) // 32
     tiles = (Nk + bc - 1) // bc
-    s = (2048 + B * H * nqb - 1) // (B * H * nqb)
+    target = 4096 if d == 64 else 2048
+    s = (target + B * H * nqb - 1) // (B * H * nqb)
     s = max(1, min(s, (Nk + 255) // 256, tiles))
     ln = (tiles + s - 1) // s * bc
     return (Nk + ln - 1) // ln, ln
@@ -202,7 +204,7 @@ def _decode_split(B, Nq, Nk, H):
 @pytest.mark.parametrize("B,Nq,Nk,H,d", [(16, 1, 8192, 16, 128), (4, 16, 16384, 16, 128), (1, 1, 100, 1, 64),
                                          (2, 40, 1000, 3, 64), (1, 5, 300, 2, 128)])
 def test_decode_workspace_bytes(lib, B, Nq, Nk, H, d):
-    ns, _ = _decode_split(B, Nq, Nk, H)
+    ns, _ = _decode_split(B, Nq, Nk, H, d)
     pad = lambda elems: (elems + 63) // 64 * 64
     rows = B * Nq * H
     want = 0 if ns == 1 else (pad(ns * rows * d) + pad(ns * rows)) * 4
