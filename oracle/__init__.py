@@ -6,9 +6,11 @@ import this package; the HIP library and its Python binding never do.
 
 from .attention import (
     attention_backward,
+    attention_backward_bias,
     attention_backward_head,
     attention_decode,
     attention_forward,
+    attention_forward_bias,
     attention_forward_chunk,
     attention_forward_rows,
     merge_chunks,
@@ -22,4 +24,6 @@ __all__ = [
     "attention_decode",
     "attention_backward",
     "attention_backward_head",
+    "attention_forward_bias",
+    "attention_backward_bias",
 ]

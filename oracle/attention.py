@@ -273,3 +273,97 @@ def attention_decode(q, k, v, causal: bool, scale: float):
     (O = 0, L = -inf)."""
     nq, nk = np.shape(q)[1], np.shape(k)[1]
     return attention_forward_chunk(q, k, v, causal, scale, q_start=nk - nq, k_start=0)
+
+
+# ---------------------------------------------------------------------------
+# Attention with an additive bias. One of the abstracts on the related-papers
+# page for "FlashAttention on a Napkin" describes attention with bias as
+# standard attention whose query-key scores receive an additive bias matrix
+# carrying prior knowledge. The page gives no formula; the plain reading is
+#
+#     S = scale * Q K^T + Bias            (Bias [B, H, N, N], added after scaling)
+#     causal: S[i, j] = -inf for j > i    (on top of the bias)
+#     O = softmax(S) V,  L = logsumexp(S) (natural log)
+#
+# and, with the loss sum(dO * O), since dS is the gradient of the loss with
+# respect to S and S depends on Bias with unit weight:
+#
+#     dBias = dS = P * (dP - D),  dQ = scale * dS K,  dK = scale * dS^T Q,
+#     dV = P^T dO  (as without bias).
+#
+# A bias entry of -inf removes that key for that query; a row whose every
+# score is -inf gets O = 0 and L = -inf and contributes no gradient.
+
+
+def _bias_scores(qh, kh, bh, row0, causal, scale):
+    s = scale * (qh @ kh.T) + bh
+    if causal:
+        qi = np.arange(row0, row0 + s.shape[0])[:, None]
+        kj = np.arange(kh.shape[0])[None, :]
+        s = np.where(kj > qi, -np.inf, s)
+    return s
+
+
+def attention_forward_bias(q, k, v, bias, causal: bool, scale: float):
+    """Forward with an additive bias [B, H, N, N] (float64, may hold -inf).
+    Returns (O [B, N, H, d], L [B, H, N])."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    bias = np.asarray(bias, dtype=np.float64)
+    _check(q, k, v)
+    B, N, H, d = q.shape
+    if bias.shape != (B, H, N, N):
+        raise ValueError("bias must be [B, H, N, N]")
+    o = np.zeros((B, N, H, d))
+    lse = np.zeros((B, H, N))
+    for b in range(B):
+        for h in range(H):
+            qh, kh, vh = q[b, :, h, :], k[b, :, h, :], v[b, :, h, :]
+            for r0, r1 in _row_chunks(N, N):
+                s = _bias_scores(qh[r0:r1], kh, bias[b, h, r0:r1], r0, causal, scale)
+                p, m, l = _softmax_rows(s)
+                o[b, r0:r1, h, :] = p @ vh
+                with np.errstate(divide="ignore"):
+                    lse[b, h, r0:r1] = np.where(l > 0, m + np.log(np.where(l > 0, l, 1.0)), -np.inf)
+    return o, lse
+
+
+def attention_backward_bias(q, k, v, bias, do, causal: bool, scale: float):
+    """Backward of sum(dO * O) for the biased forward. Returns
+    (dQ, dK, dV, dBias [B, H, N, N], O, L, D)."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    bias = np.asarray(bias, dtype=np.float64)
+    _check(q, k, v)
+    B, N, H, d = q.shape
+    if bias.shape != (B, H, N, N) or do.shape != q.shape:
+        raise ValueError("bias must be [B, H, N, N] and dO shaped like Q")
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(q)
+    dv = np.zeros_like(q)
+    dbias = np.zeros((B, H, N, N))
+    o = np.zeros_like(q)
+    lse = np.zeros((B, H, N))
+    dsum = np.zeros((B, H, N))
+    for b in range(B):
+        for h in range(H):
+            qh, kh, vh, doh = q[b, :, h, :], k[b, :, h, :], v[b, :, h, :], do[b, :, h, :]
+            for r0, r1 in _row_chunks(N, N):
+                s = _bias_scores(qh[r0:r1], kh, bias[b, h, r0:r1], r0, causal, scale)
+                p, m, l = _softmax_rows(s)
+                oc = p @ vh
+                o[b, r0:r1, h, :] = oc
+                with np.errstate(divide="ignore"):
+                    lse[b, h, r0:r1] = np.where(l > 0, m + np.log(np.where(l > 0, l, 1.0)), -np.inf)
+                dp = doh[r0:r1] @ vh.T
+                drow = np.sum(doh[r0:r1] * oc, axis=1)
+                dsum[b, h, r0:r1] = drow
+                ds = p * (dp - drow[:, None])
+                dbias[b, h, r0:r1] = ds
+                dq[b, r0:r1, h, :] = scale * (ds @ kh)
+                dk[b, :, h, :] += scale * (ds.T @ qh[r0:r1])
+                dv[b, :, h, :] += p.T @ doh[r0:r1]
+    return dq, dk, dv, dbias, o, lse, dsum

@@ -516,6 +516,124 @@ def pin_decode_alignment(mod):
     _close(l_long[:, :, 3:], l_tail, what="rows from the first key on (lse)")
 
 
+# --------------------------------------------------------------------------
+# additive-bias pins
+
+
+def _brute_bias_forward(q, k, v, bias, causal, scale):
+    """Scalar loops with math.exp / math.fsum for the biased forward."""
+    B, N, H, d = q.shape
+    o = np.zeros((B, N, H, d))
+    lse = np.full((B, H, N), -np.inf)
+    for b in range(B):
+        for h in range(H):
+            for i in range(N):
+                keys = [j for j in (range(i + 1) if causal else range(N)) if bias[b, h, i, j] != -np.inf]
+                if not keys:
+                    continue
+                s = [scale * math.fsum(q[b, i, h, t] * k[b, j, h, t] for t in range(d)) + bias[b, h, i, j]
+                     for j in keys]
+                m = max(s)
+                w = [math.exp(x - m) for x in s]
+                tot = math.fsum(w)
+                for t in range(d):
+                    o[b, i, h, t] = math.fsum(w[n] * v[b, j, h, t] for n, j in enumerate(keys)) / tot
+                lse[b, h, i] = m + math.log(tot)
+    return o, lse
+
+
+def pin_bias_brute_force(mod):
+    """Biased forward against scalar loops, with some -inf bias entries
+    (including a row that loses every key)."""
+    for (B, N, H, d), seed in (((1, 6, 2, 3), 401), ((2, 9, 1, 4), 402)):
+        q, k, v = (_rand((B, N, H, d), seed + 1000 * t) for t in range(3))
+        bias = _rand((B, H, N, N), seed + 3000) * 2.0
+        bias[0, 0, 1, :3] = -np.inf
+        bias[0, 0, 2, :] = -np.inf
+        for causal in (False, True):
+            o, lse = mod.attention_forward_bias(q, k, v, bias, causal, 0.6)
+            ob, lseb = _brute_bias_forward(q, k, v, bias, causal, 0.6)
+            _close(o, ob, 1e-13, what="bias brute output")
+            _close_inf(lse, lseb, 1e-13, what="bias brute lse")
+
+
+def pin_bias_special_cases(mod):
+    """Bias = 0 is plain attention (and dBias = dS has zero row sums); a -inf
+    strictly-upper-triangular bias is the causal mask; a bias constant along
+    each row leaves O unchanged and shifts L by that constant."""
+    B, N, H, d = 2, 11, 2, 4
+    q, k, v, do = (_rand((B, N, H, d), 410 + t) for t in range(4))
+    zero = np.zeros((B, H, N, N))
+    for causal in (False, True):
+        o0, l0 = mod.attention_forward(q, k, v, causal, 0.5)
+        o, l = mod.attention_forward_bias(q, k, v, zero, causal, 0.5)
+        _close(o, o0, what="zero bias output")
+        _close(l, l0, what="zero bias lse")
+        g0 = mod.attention_backward(q, k, v, do, causal, 0.5)
+        g = mod.attention_backward_bias(q, k, v, zero, do, causal, 0.5)
+        for a, b_, name in zip(g[:3], g0[:3], ("dQ", "dK", "dV")):
+            _close(a, b_, what=f"zero bias {name}")
+        _close(g[3].sum(axis=3), np.zeros((B, H, N)), what="dBias row sums")
+    tri = np.where(np.arange(N)[None, :] > np.arange(N)[:, None], -np.inf, 0.0)
+    mask = np.broadcast_to(tri, (B, H, N, N)).copy()
+    oc, lc = mod.attention_forward(q, k, v, True, 0.5)
+    om, lm = mod.attention_forward_bias(q, k, v, mask, False, 0.5)
+    _close(om, oc, what="-inf triangle output")
+    _close(lm, lc, what="-inf triangle lse")
+    gc = mod.attention_backward(q, k, v, do, True, 0.5)
+    gm = mod.attention_backward_bias(q, k, v, mask, do, False, 0.5)
+    for a, b_, name in zip(gm[:3], gc[:3], ("dQ", "dK", "dV")):
+        _close(a, b_, what=f"-inf triangle {name}")
+    assert np.all(gm[3][..., np.triu_indices(N, 1)[0], np.triu_indices(N, 1)[1]] == 0.0), "masked dBias"
+    row = _rand((B, H, N, 1), 420) * 3.0
+    ob, lb = mod.attention_forward_bias(q, k, v, np.broadcast_to(row, (B, H, N, N)).copy(), False, 0.5)
+    o0, l0 = mod.attention_forward(q, k, v, False, 0.5)
+    _close(ob, o0, what="row-constant bias output")
+    _close(lb, l0 + row[..., 0], what="row-constant bias lse")
+
+
+def pin_bias_torch_sdpa(mod):
+    """Forward and all four gradients against torch's fp64 CPU
+    scaled_dot_product_attention with an additive float mask (autograd)."""
+    import torch
+
+    B, N, H, d = 2, 13, 3, 5
+    q, k, v, do = (_rand((B, N, H, d), 430 + t) for t in range(4))
+    bias = _rand((B, H, N, N), 434)
+    t = [torch.tensor(x.transpose(0, 2, 1, 3), dtype=torch.float64, requires_grad=True) for x in (q, k, v)]
+    tb = torch.tensor(bias, dtype=torch.float64, requires_grad=True)
+    out = torch.nn.functional.scaled_dot_product_attention(t[0], t[1], t[2], attn_mask=tb, scale=0.45)
+    out.backward(torch.tensor(do.transpose(0, 2, 1, 3), dtype=torch.float64))
+    dq, dk, dv, db, o, _, _ = mod.attention_backward_bias(q, k, v, bias, do, False, 0.45)
+    _close(o, out.detach().numpy().transpose(0, 2, 1, 3), 1e-12, what="sdpa bias output")
+    for got, ref, name in ((dq, t[0], "dQ"), (dk, t[1], "dK"), (dv, t[2], "dV")):
+        _close(got, ref.grad.numpy().transpose(0, 2, 1, 3), 1e-12, what=f"sdpa bias {name}")
+    _close(db, tb.grad.numpy(), 1e-12, what="sdpa dBias")
+
+
+def pin_bias_finite_differences(mod):
+    """dBias (and dQ) against central differences of sum(dO * O)."""
+    B, N, H, d = 1, 4, 1, 3
+    q, k, v, do = (_rand((B, N, H, d), 440 + t) for t in range(4))
+    bias = _rand((B, H, N, N), 444)
+    for causal in (False, True):
+        dq, _, _, db, _, _, _ = mod.attention_backward_bias(q, k, v, bias, do, causal, 0.8)
+        f = lambda bb, qq: float(np.sum(do * mod.attention_forward_bias(qq, k, v, bb, causal, 0.8)[0]))
+        h = 1e-6
+        for (i, j) in ((0, 0), (2, 1), (3, 3), (1, 3)):
+            bp, bm = bias.copy(), bias.copy()
+            bp[0, 0, i, j] += h
+            bm[0, 0, i, j] -= h
+            num = (f(bp, q) - f(bm, q)) / (2 * h)
+            assert abs(num - db[0, 0, i, j]) <= 1e-7 * max(1.0, abs(num)), f"dBias[{i},{j}] {num} vs {db[0, 0, i, j]}"
+        for (i, t) in ((1, 0), (3, 2)):
+            qp, qm = q.copy(), q.copy()
+            qp[0, i, 0, t] += h
+            qm[0, i, 0, t] -= h
+            num = (f(bias, qp) - f(bias, qm)) / (2 * h)
+            assert abs(num - dq[0, i, 0, t]) <= 1e-7 * max(1.0, abs(num)), f"dQ[{i},{t}]"
+
+
 FORWARD_PINS = [
     pin_rows_sum_to_one,
     pin_q_zero,
@@ -535,6 +653,12 @@ CHUNK_PINS = [
     pin_merge_closed_forms,
     pin_decode_alignment,
 ]
+BIAS_PINS = [
+    pin_bias_brute_force,
+    pin_bias_special_cases,
+    pin_bias_torch_sdpa,
+    pin_bias_finite_differences,
+]
 BACKWARD_PINS = [
     pin_constant_v,
     pin_backward_invariants,
@@ -543,4 +667,4 @@ BACKWARD_PINS = [
     pin_worked_examples,
     pin_backward_head,
 ]
-ALL_PINS = FORWARD_PINS + CHUNK_PINS + BACKWARD_PINS
+ALL_PINS = FORWARD_PINS + CHUNK_PINS + BIAS_PINS + BACKWARD_PINS

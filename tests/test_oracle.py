@@ -47,12 +47,12 @@ def test_oracle_pin_chunked(pin):
 
 # (name, text in the oracle source, planted replacement)
 MUTATIONS = [
-    ("scale dropped", "s = scale * (qh @ kh.T)", "s = (qh @ kh.T)"),
-    ("scale squared", "s = scale * (qh @ kh.T)", "s = scale * scale * (qh @ kh.T)"),
+    ("scale dropped", "s = scale * (qh @ kh.T)\n", "s = (qh @ kh.T)\n"),
+    ("scale squared", "s = scale * (qh @ kh.T)\n", "s = scale * scale * (qh @ kh.T)\n"),
     ("diagonal masked", "np.where(kj > qi,", "np.where(kj >= qi,"),
     ("wrong triangle", "np.where(kj > qi,", "np.where(kj < qi,"),
     ("chunk offset lost", "qi = np.arange(row0, row0 + s.shape[0])", "qi = np.arange(0, s.shape[0])"),
-    ("scores transposed", "(qh @ kh.T)", "(kh @ qh.T)"),
+    ("scores transposed", "s = scale * (qh @ kh.T)\n", "s = scale * (kh @ qh.T)\n"),
     ("max over columns", "m = s.max(axis=1, keepdims=True)", "m = s.max(axis=0, keepdims=True)"),
     ("sum over columns", "l = e.sum(axis=1, keepdims=True)", "l = e.sum(axis=0, keepdims=True)"),
     ("P transposed in PV", "o[b, r0:r1, h, :] = p @ vh\n                with np.errstate(divide=\"ignore\"):\n                    lse[b, h, r0:r1] = m + np.log(l)",
@@ -92,16 +92,34 @@ MUTATIONS = [
      "return attention_forward_chunk(q, k, v, causal, scale, q_start=0, k_start=0)"),
     ("decode offset off by one", "return attention_forward_chunk(q, k, v, causal, scale, q_start=nk - nq, k_start=0)",
      "return attention_forward_chunk(q, k, v, causal, scale, q_start=nk - nq - 1, k_start=0)"),
+    ("bias before the scale", "s = scale * (qh @ kh.T) + bh", "s = scale * (qh @ kh.T + bh)"),
+    ("bias transposed", "s = scale * (qh @ kh.T) + bh", "s = scale * (qh @ kh.T) + bh.T[: qh.shape[0], : kh.shape[0]]"),
+    ("bias sign", "s = scale * (qh @ kh.T) + bh", "s = scale * (qh @ kh.T) - bh"),
+    ("dBias from P", "dbias[b, h, r0:r1] = ds", "dbias[b, h, r0:r1] = p"),
+    ("dBias scaled", "dbias[b, h, r0:r1] = ds", "dbias[b, h, r0:r1] = scale * ds"),
+    ("bias causal mask dropped", "        s = np.where(kj > qi, -np.inf, s)\n    return s\n\n\ndef attention_forward_bias",
+     "        s = s\n    return s\n\n\ndef attention_forward_bias"),
+    ("bias row chunk offset", "s = _bias_scores(qh[r0:r1], kh, bias[b, h, r0:r1], r0, causal, scale)\n                p, m, l = _softmax_rows(s)\n                o[b, r0:r1, h, :] = p @ vh",
+     "s = _bias_scores(qh[r0:r1], kh, bias[b, h, 0:r1 - r0], r0, causal, scale)\n                p, m, l = _softmax_rows(s)\n                o[b, r0:r1, h, :] = p @ vh"),
+    ("bias dS sign", "ds = p * (dp - drow[:, None])\n                dbias[b, h, r0:r1] = ds",
+     "ds = p * (dp + drow[:, None])\n                dbias[b, h, r0:r1] = ds"),
+    ("bias dV not transposed", "dv[b, :, h, :] += p.T @ doh[r0:r1]\n    return dq, dk, dv, dbias",
+     "dv[b, :, h, :] += p @ doh[r0:r1]\n    return dq, dk, dv, dbias"),
+    ("bias dK unscaled", "dk[b, :, h, :] += scale * (ds.T @ qh[r0:r1])\n                dv[b, :, h, :] += p.T @ doh[r0:r1]\n    return dq, dk, dv, dbias",
+     "dk[b, :, h, :] += (ds.T @ qh[r0:r1])\n                dv[b, :, h, :] += p.T @ doh[r0:r1]\n    return dq, dk, dv, dbias"),
     ("head slice swapped", "sl = (slice(b, b + 1), slice(None), slice(h, h + 1), slice(None))",
      "sl = (slice(h, h + 1), slice(None), slice(b, b + 1), slice(None))"),
 ]
 
 
 def _load_mutant(old, new):
+    """The oracle with the first occurrence of `old` replaced (functions that
+    repeat a line plant it in the earliest one; later copies have mutations
+    of their own with longer, unique anchors)."""
     src = open(ORACLE_SRC).read()
-    assert src.count(old) == 1, f"mutation anchor not found exactly once: {old!r}"
+    assert src.count(old) >= 1, f"mutation anchor not found: {old!r}"
     mod = types.ModuleType("oracle_mutant")
-    exec(compile(src.replace(old, new), ORACLE_SRC + " (mutant)", "exec"), mod.__dict__)
+    exec(compile(src.replace(old, new, 1), ORACLE_SRC + " (mutant)", "exec"), mod.__dict__)
     return mod
 
 
