@@ -30,6 +30,8 @@ __all__ = [
     "fa_merge",
     "fa_decode",
     "fa_decode_workspace_bytes",
+    "fa_fwd_bias",
+    "fa_bwd_bias",
     "fa_status_string",
     "fa_version",
     "EXPORTED_SYMBOLS",
@@ -38,7 +40,7 @@ __all__ = [
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libfa_mi355x.so"
 EXPORTED_SYMBOLS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd_chunk", "fa_merge", "fa_decode",
-                    "fa_decode_workspace_bytes", "fa_status_string", "fa_version")
+                    "fa_decode_workspace_bytes", "fa_fwd_bias", "fa_bwd_bias", "fa_status_string", "fa_version")
 
 _lib = None
 
@@ -81,6 +83,10 @@ def load_library():
     lib.fa_decode.restype = i
     lib.fa_decode_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.fa_decode_workspace_bytes.restype = sz
+    lib.fa_fwd_bias.argtypes = [vp, vp, vp, vp, ll, ll, i, vp, vp, i, i, i, i, i, f, vp]
+    lib.fa_fwd_bias.restype = i
+    lib.fa_bwd_bias.argtypes = [vp, vp, vp, vp, ll, ll, i, vp, vp, vp, vp, vp, vp, vp, i, vp, sz, i, i, i, i, i, f, vp]
+    lib.fa_bwd_bias.restype = i
     lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i]
     lib.fa_bwd_workspace_bytes.restype = sz
     lib.fa_status_string.argtypes = [i]
@@ -281,3 +287,94 @@ def fa_decode(q, k, v, causal: bool, softmax_scale: Optional[float] = None, out=
     if st != 0:
         raise FaError(st, "fa_decode")
     return out, lse
+
+
+def _bias_layout(bias, B, N, H):
+    """(pointer, stride_b, stride_h, stride_row) of a bf16 bias tensor viewed
+    as [B or 1, H or 1, N, >= N] (a size-1 batch or head dimension is
+    broadcast); the last dimension must be contiguous."""
+    import torch
+
+    if bias.dtype != torch.bfloat16 or not bias.is_cuda or bias.dim() != 4:
+        raise ValueError("bias must be a bfloat16 device tensor [B or 1, H or 1, N, N]")
+    if bias.shape[2] != N or bias.shape[3] != N or bias.shape[0] not in (1, B) or bias.shape[1] not in (1, H):
+        raise ValueError(f"bias has shape {tuple(bias.shape)}, expected [{B} or 1, {H} or 1, {N}, {N}]")
+    if bias.stride(3) != 1:
+        raise ValueError("bias rows must be contiguous")
+    sb = 0 if bias.shape[0] == 1 else bias.stride(0)
+    sh = 0 if bias.shape[1] == 1 else bias.stride(1)
+    return bias.data_ptr(), sb, sh, bias.stride(2)
+
+
+def padded_bias(B: int, H: int, N: int, device=None):
+    """An empty bf16 bias [B, H, N, N] whose rows are padded to a multiple of
+    8 elements (a view of [B, H, N, ceil8(N)] storage), as the biased entry
+    points require."""
+    import torch
+
+    n8 = (N + 7) // 8 * 8
+    return torch.empty((B, H, N, n8), dtype=torch.bfloat16, device=device)[..., :N]
+
+
+def fa_fwd_bias(q, k, v, bias, causal: bool, softmax_scale: Optional[float] = None, out=None, lse=None):
+    """Forward with an additive bf16 bias on the scaled scores. Returns (o, lse)."""
+    import torch
+
+    _check_bnhd("q", q)
+    B, N, H, d = q.shape
+    _check_bnhd("k", k, q.shape)
+    _check_bnhd("v", v, q.shape)
+    bp, sb, sh, sr = _bias_layout(bias, B, N, H)
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        out = torch.empty_like(q)
+    _check_bnhd("out", out, q.shape)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check_lse(lse, B, N, H)
+    st = load_library().fa_fwd_bias(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), bp, sb, sh, sr, out.data_ptr(), lse.data_ptr(),
+        B, N, H, d, int(bool(causal)), scale, _stream_handle(q.device),
+    )
+    if st != 0:
+        raise FaError(st, "fa_fwd_bias")
+    return out, lse
+
+
+def fa_bwd_bias(q, k, v, bias, o, lse, do, causal: bool, softmax_scale: Optional[float] = None,
+                dq=None, dk=None, dv=None, dbias=None, want_dbias: bool = True, workspace=None):
+    """Backward of fa_fwd_bias. Returns (dq, dk, dv, dbias); dbias is a bf16
+    [B, H, N, N] view with rows padded to a multiple of 8 (None when
+    want_dbias is False and no dbias is given)."""
+    import torch
+
+    _check_bnhd("q", q)
+    B, N, H, d = q.shape
+    for name, t in (("k", k), ("v", v), ("o", o), ("do", do)):
+        _check_bnhd(name, t, q.shape)
+    _check_lse(lse, B, N, H)
+    bp, sb, sh, sr = _bias_layout(bias, B, N, H)
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _check_bnhd(name, t, q.shape)
+    if dbias is None and want_dbias:
+        dbias = padded_bias(B, H, N, q.device)
+    if dbias is not None:
+        if (dbias.dtype != torch.bfloat16 or tuple(dbias.shape) != (B, H, N, N) or dbias.stride(3) != 1
+                or dbias.stride(1) != N * dbias.stride(2) or dbias.stride(0) != H * N * dbias.stride(2)):
+            raise ValueError("dbias must be a bf16 [B, H, N, N] view with unit key stride and packed rows")
+    need = fa_bwd_workspace_bytes(B, N, H, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    st = load_library().fa_bwd_bias(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), bp, sb, sh, sr, o.data_ptr(), lse.data_ptr(), do.data_ptr(),
+        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), dbias.data_ptr() if dbias is not None else None,
+        dbias.stride(2) if dbias is not None else 0, workspace.data_ptr(), workspace.numel(),
+        B, N, H, d, int(bool(causal)), scale, _stream_handle(q.device),
+    )
+    if st != 0:
+        raise FaError(st, "fa_bwd_bias")
+    return dq, dk, dv, dbias

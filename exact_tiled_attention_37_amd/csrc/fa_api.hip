@@ -107,6 +107,75 @@ fa_status fa_fwd_chunk(const void* q, const void* k, const void* v, float* o, fl
   return dispatch(d, causal, [&](auto D, auto C) { return fa::launch_fwd<decltype(D)::value, decltype(C)::value>(a); });
 }
 
+namespace {
+// Bias layout checks shared by the biased entry points: row stride a multiple
+// of 8 elements and at least N, batch/head strides multiples of 8 (0 =
+// broadcast), 16-byte aligned base, and every (batch, head) slice addressable
+// with 32-bit byte offsets.
+fa_status check_bias(const void* bias, long long sb, long long sh, int srow, int N) {
+  if (srow < N || srow % 8 != 0 || sb < 0 || sh < 0 || sb % 8 != 0 || sh % 8 != 0) return FA_ERR_SHAPE;
+  if ((long long)N * srow * 2 >= (1LL << 32)) return FA_ERR_SHAPE;
+  if (!aligned(bias, 16)) return FA_ERR_ALIGN;
+  return FA_OK;
+}
+}  // namespace
+
+fa_status fa_fwd_bias(const void* q, const void* k, const void* v, const void* bias, long long bias_stride_b,
+                      long long bias_stride_h, int bias_stride_row, void* o, float* lse, int B, int N, int H,
+                      int d, int causal, float softmax_scale, hipStream_t stream) {
+  if (!q || !k || !v || !bias || !o || !lse) return FA_ERR_NULL;
+  fa_status st = check_shape(B, N, H, d);
+  if (st != FA_OK) return st;
+  if (!std::isfinite(softmax_scale)) return FA_ERR_SCALE;
+  if ((st = check_bias(bias, bias_stride_b, bias_stride_h, bias_stride_row, N)) != FA_OK) return st;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
+    return FA_ERR_ALIGN;
+  st = check_device();
+  if (st != FA_OK) return st;
+  (void)hipGetLastError();
+  fa::FwdArgs a{q, k, v, o, lse, B, N, N, H, 0, false, softmax_scale, stream};
+  a.bias = bias;
+  a.bias_sb = (long)bias_stride_b;
+  a.bias_sh = (long)bias_stride_h;
+  a.bias_srow = bias_stride_row;
+  return dispatch(d, causal, [&](auto D, auto C) { return fa::launch_fwd<decltype(D)::value, decltype(C)::value>(a); });
+}
+
+fa_status fa_bwd_bias(const void* q, const void* k, const void* v, const void* bias, long long bias_stride_b,
+                      long long bias_stride_h, int bias_stride_row, const void* o, const float* lse,
+                      const void* dout, void* dq, void* dk, void* dv, void* dbias, int dbias_stride_row,
+                      void* workspace, size_t workspace_bytes, int B, int N, int H, int d, int causal,
+                      float softmax_scale, hipStream_t stream) {
+  if (!q || !k || !v || !bias || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
+  fa_status st = check_shape(B, N, H, d);
+  if (st != FA_OK) return st;
+  if (!std::isfinite(softmax_scale)) return FA_ERR_SCALE;
+  if ((st = check_bias(bias, bias_stride_b, bias_stride_h, bias_stride_row, N)) != FA_OK) return st;
+  if (dbias) {
+    if (dbias_stride_row < N || dbias_stride_row % 8 != 0) return FA_ERR_SHAPE;
+    if (!aligned(dbias, 16)) return FA_ERR_ALIGN;
+  }
+  if (!workspace || workspace_bytes < fa_bwd_workspace_bytes(B, N, H, d)) return FA_ERR_WORKSPACE;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(dout, 16) ||
+      !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(lse, 4) || !aligned(workspace, 256))
+    return FA_ERR_ALIGN;
+  st = check_device();
+  if (st != FA_OK) return st;
+  (void)hipGetLastError();
+  char* ws = static_cast<char*>(workspace);
+  fa::BwdArgs a{q, k, v, o, lse, dout, dq, dk, dv,
+                reinterpret_cast<float*>(ws),
+                reinterpret_cast<float*>(ws + fa::bwd_row_bytes(B, N, H)),
+                B, N, H, softmax_scale, stream};
+  a.bias = bias;
+  a.bias_sb = (long)bias_stride_b;
+  a.bias_sh = (long)bias_stride_h;
+  a.bias_srow = bias_stride_row;
+  a.dbias = dbias;
+  a.dbias_srow = dbias_stride_row;
+  return dispatch(d, causal, [&](auto D, auto C) { return fa::launch_bwd<decltype(D)::value, decltype(C)::value>(a); });
+}
+
 size_t fa_decode_workspace_bytes(int B, int Nq, int Nk, int H, int d) {
   if (check_shape(B, Nq, H, d) != FA_OK || check_shape(B, Nk, H, d) != FA_OK) return 0;
   return fa::decode_workspace_bytes(B, Nq, Nk, H, d);

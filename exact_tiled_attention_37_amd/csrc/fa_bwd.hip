@@ -89,18 +89,24 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16* __restrict__ O
     const long n = bn - b * N;
     const long i = (b * H + h) * N + n;
     dsum[i] = acc;
-    lse2[i] = LSE[i] * kLog2e;
+    // A row that saw no key (possible only with a -inf bias) has L = -inf;
+    // +inf here makes every recomputed probability exp2(x - inf) exactly 0.
+    const float L = LSE[i];
+    lse2[i] = L == -INFINITY ? INFINITY : L * kLog2e;
   }
 }
 
 // ---------------------------------------------------------------------------
 // 2. dK, dV.
-template <int D, bool CAUSAL>
+// BIAS: the bf16 additive bias enters the recomputed probabilities; element
+// (b, h, i, j) at Bias[b * bias_sb + h * bias_sh + i * bias_srow + j].
+template <int D, bool CAUSAL, bool BIAS = false>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dkdv_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ dsum,
     bf16* __restrict__ dK, bf16* __restrict__ dV, int N, int H, int nkb, int total_blocks,
-    float c2, uint32_t k_sign, float dk_scale) {
+    float c2, uint32_t k_sign, float dk_scale, const bf16* __restrict__ Bias = nullptr, long bias_sb = 0,
+    long bias_sh = 0, int bias_srow = 0) {
   using TQ = Tile<kQStep, D>;    // one Q or dO block (rows = queries)
   using TV = Tile<kKvBlock, D>;  // the workgroup's V rows (rows = keys)
   constexpr int KS = D / 16;
@@ -132,6 +138,10 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   const int kb0 = kblk * kKvBlock;
   const int kw0 = kb0 + 32 * wave;
   const int mykey = kw0 + l32;
+  // Bias column of this lane's key (rows of bias_srow readable elements):
+  // rows at or past N read as zeros.
+  const auto rb = make_rsrc(BIAS ? Bias + b * bias_sb + h * bias_sh : Q,
+                            BIAS ? (uint32_t)((long)N * bias_srow * 2) : 0u);
 
   // This wave's K rows as B operands of S = Q K^T (registers), and the
   // block's V rows (LDS, read as B operands of dP = dO V^T).
@@ -180,6 +190,15 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
     constexpr bool MASK = decltype(mask_tag)::value;
     const int q0 = step * kQStep;
     const char* dot = qt + QT;
+    // Bias of this lane's key for its 16 accumulator rows (queries).
+    uint32_t bb[BIAS ? 16 : 1];
+    if constexpr (BIAS) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int q = q0 + 8 * (r >> 2) + 4 * g + (r & 3);
+        bb[r] = buf_load2(rb, ((uint32_t)min(q, N) * (uint32_t)bias_srow + (uint32_t)mykey) * 2u);
+      }
+    }
     f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -195,7 +214,11 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * rq4 + e;
-        float p = fast_exp2(__builtin_fmaf(s[r], c2, -l4[e]));
+        float p;
+        if constexpr (BIAS)
+          p = fast_exp2(__builtin_fmaf(s[r], c2, __builtin_fmaf(bf16_bits_to_float(bb[r]), kLog2e, -l4[e])));
+        else
+          p = fast_exp2(__builtin_fmaf(s[r], c2, -l4[e]));
         if constexpr (MASK) p = (mykey > q0 + qi0 + e) ? 0.f : p;
         p8[r >> 3][r & 7] = p;
         ds8[r >> 3][r & 7] = p * (dp[r] - d4[e]);
@@ -269,12 +292,17 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
 
 // ---------------------------------------------------------------------------
 // 3. dQ.
-template <int D, bool CAUSAL>
+// BIAS: as in the dK/dV kernel; in addition, when dBias is given, this kernel
+// writes dBias = dS (bf16) at dBias[((b * H + h) * N + i) * dbias_srow + j]
+// for every query row i < N and key j < N: the tiles it visits write their
+// dS (0 where masked), the causal keys it never visits are written as 0.
+template <int D, bool CAUSAL, bool BIAS = false>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ dsum,
     bf16* __restrict__ dQ, int N, int H, int nqb, int total_blocks, float c2, uint32_t q_sign,
-    float dq_scale) {
+    float dq_scale, const bf16* __restrict__ Bias = nullptr, long bias_sb = 0, long bias_sh = 0,
+    int bias_srow = 0, bf16* __restrict__ dBias = nullptr, int dbias_srow = 0) {
   using T = Tile<kKTile, D>;  // one K or V tile (rows = keys)
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
@@ -299,6 +327,10 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
 
   const int qw0 = qblk * kQBlock + wave * 32;
   const int myq = qw0 + l32;
+  const auto rb = make_rsrc(BIAS ? Bias + b * bias_sb + h * bias_sh : Q,
+                            BIAS ? (uint32_t)((long)N * bias_srow * 2) : 0u);
+  const uint32_t boff = BIAS ? (uint32_t)min(myq, N) * (uint32_t)bias_srow * 2u : 0u;
+  bf16* const dbrow = (BIAS && dBias) ? dBias + ((long)head * N + myq) * dbias_srow : nullptr;
 
   // This wave's Q and dO rows as B operands of S^T = K Q^T and dP^T = V dO^T.
   bf16x8 qf[KS], dof[KS];
@@ -340,6 +372,11 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
     const char* vt = kt + TILE;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
+      u32x2 bw[BIAS ? 4 : 1];  // this lane's bias: 4 groups of 4 consecutive keys
+      if constexpr (BIAS) {
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) bw[rg] = buf_load8(rb, boff + (uint32_t)(key0 + kb * 32 + 8 * rg + 4 * g) * 2u);
+      }
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
@@ -353,14 +390,36 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
         for (int s8 = 0; s8 < 8; ++s8) {
           const int r = 8 * hh + s8;
-          float p = fast_exp2(__builtin_fmaf(s[r], c2, -l2));
+          float p;
+          if constexpr (BIAS)
+            p = fast_exp2(__builtin_fmaf(s[r], c2, __builtin_fmaf(bf16_elem(bw[r >> 2], r & 3), kLog2e, -l2)));
+          else
+            p = fast_exp2(__builtin_fmaf(s[r], c2, -l2));
           if constexpr (MASK) {
             const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-            p = (key > myq) ? 0.f : p;
+            // with a bias, keys past N are masked too (their bias is row padding)
+            p = ((CAUSAL && key > myq) || (BIAS && key >= N)) ? 0.f : p;
           }
           x[s8] = p * (dp[r] - dd);
         }
         dsf[hh] = to_bf16x8(x);
+      }
+      if constexpr (BIAS) {
+        if (dbrow && myq < N) {
+#pragma unroll
+          for (int rg = 0; rg < 4; ++rg) {
+            const int key = key0 + kb * 32 + 8 * rg + 4 * g;
+            const bf16x8 v8 = dsf[rg >> 1];
+            const int o = 4 * (rg & 1);
+            if (key + 3 < N) {
+              const bf16x4 v4 = {v8[o], v8[o + 1], v8[o + 2], v8[o + 3]};
+              *reinterpret_cast<bf16x4*>(dbrow + key) = v4;
+            } else {
+              for (int e = 0; e < 4; ++e)
+                if (key + e < N) dbrow[key + e] = v8[o + e];
+            }
+          }
+        }
       }
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
@@ -377,7 +436,8 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   // need no mask. Keys past N need none: their K and V rows read as zero.
   const int kv_len = CAUSAL ? min(N, (qblk + 1) * kQBlock) : N;
   const int ntiles = (kv_len + kKTile - 1) / kKTile;
-  const int jm = CAUSAL ? qblk * (kQBlock / kKTile) : ntiles;
+  // (with a bias a ragged last tile runs the masked variant: see above)
+  const int jm = CAUSAL ? qblk * (kQBlock / kKTile) : (BIAS ? N / kKTile : ntiles);
   issue(0, kv0);
   wait_vmem();
   __syncthreads();
@@ -394,14 +454,28 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   }
   for (; j < ntiles; j += 2) {
     if (j + 1 < ntiles) issue(j + 1, kv1);
-    compute(j, kv0, std::integral_constant<bool, CAUSAL>{});
+    compute(j, kv0, std::integral_constant<bool, CAUSAL || BIAS>{});
     wait_vmem();
     __syncthreads();
     if (j + 1 >= ntiles) break;
     if (j + 2 < ntiles) issue(j + 2, kv0);
-    compute(j + 1, kv1, std::integral_constant<bool, CAUSAL>{});
+    compute(j + 1, kv1, std::integral_constant<bool, CAUSAL || BIAS>{});
     wait_vmem();
     __syncthreads();
+  }
+
+  // Causal: dBias of keys past the visited tiles is 0 (16-byte stores, the
+  // two lanes of a row taking alternate 8-key chunks).
+  if constexpr (BIAS && CAUSAL) {
+    if (dbrow && myq < N) {
+      const bf16x8 z = {};
+      for (int c = ntiles * (kKTile / 8) + g; 8 * c < N; c += 2) {
+        if (8 * c + 8 <= N)
+          *reinterpret_cast<bf16x8*>(dbrow + 8 * c) = z;
+        else
+          for (int e = 0; 8 * c + e < N; ++e) dbrow[8 * c + e] = z[0];
+      }
+    }
   }
 
   if (myq < N) {
@@ -435,21 +509,37 @@ hipError_t launch_bwd(const BwdArgs& a) {
   {
     const int nkb = (a.N + kKvBlock - 1) / kKvBlock;
     const int total = a.B * a.H * nkb;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(total), dim3(kBwdThreads), 0, a.stream,
-                       static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k),
-                       static_cast<const bf16*>(a.v), static_cast<const bf16*>(a.dout), a.lse2,
-                       a.dsum, static_cast<bf16*>(a.dk), static_cast<bf16*>(a.dv), a.N, a.H, nkb,
-                       total, c2, sign, a.scale);
+    if (a.bias)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, true>), dim3(total), dim3(kBwdThreads), 0, a.stream,
+                         static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k),
+                         static_cast<const bf16*>(a.v), static_cast<const bf16*>(a.dout), a.lse2,
+                         a.dsum, static_cast<bf16*>(a.dk), static_cast<bf16*>(a.dv), a.N, a.H, nkb,
+                         total, c2, sign, a.scale, static_cast<const bf16*>(a.bias), a.bias_sb, a.bias_sh,
+                         a.bias_srow);
+    else
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(total), dim3(kBwdThreads), 0, a.stream,
+                         static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k),
+                         static_cast<const bf16*>(a.v), static_cast<const bf16*>(a.dout), a.lse2,
+                         a.dsum, static_cast<bf16*>(a.dk), static_cast<bf16*>(a.dv), a.N, a.H, nkb,
+                         total, c2, sign, a.scale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   {
     const int nqb = (a.N + kQBlock - 1) / kQBlock;
     const int total = a.B * a.H * nqb;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(total), dim3(kBwdThreads), 0, a.stream,
-                       static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k),
-                       static_cast<const bf16*>(a.v), static_cast<const bf16*>(a.dout), a.lse2,
-                       a.dsum, static_cast<bf16*>(a.dq), a.N, a.H, nqb, total, c2, sign, a.scale);
+    if (a.bias)
+      hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, true>), dim3(total), dim3(kBwdThreads), 0, a.stream,
+                         static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k),
+                         static_cast<const bf16*>(a.v), static_cast<const bf16*>(a.dout), a.lse2,
+                         a.dsum, static_cast<bf16*>(a.dq), a.N, a.H, nqb, total, c2, sign, a.scale,
+                         static_cast<const bf16*>(a.bias), a.bias_sb, a.bias_sh, a.bias_srow,
+                         static_cast<bf16*>(a.dbias), a.dbias_srow);
+    else
+      hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(total), dim3(kBwdThreads), 0, a.stream,
+                         static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k),
+                         static_cast<const bf16*>(a.v), static_cast<const bf16*>(a.dout), a.lse2,
+                         a.dsum, static_cast<bf16*>(a.dq), a.N, a.H, nqb, total, c2, sign, a.scale);
     return hipGetLastError();
   }
 }

@@ -162,6 +162,19 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
 }
+__device__ __forceinline__ u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ uint32_t buf_load2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+}
+
+// bfloat16 element e (0..3) of four packed in two dwords, as float32 (exact).
+__device__ __forceinline__ float bf16_elem(const u32x2& w, int e) {
+  const uint32_t x = w[e >> 1];
+  return __builtin_bit_cast(float, (e & 1) ? (x & 0xFFFF0000u) : (x << 16));
+}
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) { return __builtin_bit_cast(float, bits16 << 16); }
 
 // The four descriptor words of the same resource, held in scalar registers,
 // for the loads below that are written as inline assembly.

@@ -77,12 +77,17 @@ constexpr float kRescaleSlack = 8.f;  // log2 units a row max may exceed the run
 // The keys may be split into nsplit ranges of split_len keys (a multiple of
 // the tile width), one workgroup each; split s writes its result at
 // O + s * o_split and LSE + s * l_split (elements).
-template <typename Cfg, bool CAUSAL, bool F32OUT>
+// BIAS: bfloat16 additive bias on the scaled scores, element (b, h, i, j) at
+// Bias[b * bias_sb + h * bias_sh + i * bias_srow + j] (bias_srow a multiple
+// of 8, the row base 16-byte aligned); keys past Nk are always masked so the
+// padding of a bias row is never used.
+template <typename Cfg, bool CAUSAL, bool F32OUT, bool BIAS = false>
 __global__ __launch_bounds__(Cfg::BR * 2)
 __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD))) void fwd_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     void* __restrict__ O, float* __restrict__ LSE, int Nq, int Nk, int delta, int H, int nqb,
-    int nsplit, int split_len, long o_split, long l_split, int total_blocks, float c2, uint32_t q_sign) {
+    int nsplit, int split_len, long o_split, long l_split, int total_blocks, float c2, uint32_t q_sign,
+    const bf16* __restrict__ Bias = nullptr, long bias_sb = 0, long bias_sh = 0, int bias_srow = 0) {
   constexpr int D = Cfg::D;                        // head dimension
   constexpr int kFwdBR = Cfg::BR;                  // query rows per workgroup
   constexpr int kFwdBC = Cfg::BC;                  // keys per K/V tile
@@ -118,6 +123,13 @@ __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD))) v
 
   const int qw0 = qblk * kFwdBR + wave * 32;       // first query row of this wave
   const int myq = qw0 + l32;
+
+  // Bias rows of this (batch, head), each bias_srow elements of readable
+  // memory (the 8-byte loads of a row's last keys reach into its padding);
+  // rows at or past Nq read as zeros.
+  const auto rb = make_rsrc(BIAS ? Bias + b * bias_sb + h * bias_sh : Q,
+                            BIAS ? (uint32_t)((long)Nq * bias_srow * 2) : 0u);
+  const uint32_t boff = BIAS ? (uint32_t)min(myq, Nq) * (uint32_t)bias_srow * 2u : 0u;
 
   // Q as the B operand of S^T = K Q^T: row myq, d = 16*ks + 8*g .. +7.
   bf16x8 qf[KS];
@@ -163,6 +175,15 @@ __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD))) v
     constexpr bool MASK = decltype(mask_tag)::value;
     const int key0 = j * kFwdBC;
     const char* vt = kt + TILE;
+    // This lane's bias terms: for each 32-key block, 4 groups of 4
+    // consecutive keys (the keys of its accumulator rows), 8 bytes each.
+    u32x2 bw[BIAS ? KB : 1][4];
+    if constexpr (BIAS) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) bw[kb][rg] = buf_load8(rb, boff + (uint32_t)(key0 + kb * 32 + 8 * rg + 4 * g) * 2u);
+    }
     // The KB accumulation chains are interleaved (independent MFMAs back to back).
     f32x16 s[KB];
 #pragma unroll
@@ -171,6 +192,13 @@ __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD))) v
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) s[kb] = mfma32(T::row8(kt, kb * 32 + l32, 2 * ks + g), qf[ks], s[kb]);
+    // With a bias the scores become log2-domain values here, c2 * s + bias * log2(e).
+    if constexpr (BIAS) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][r] = __builtin_fmaf(s[kb][r], c2, bf16_elem(bw[kb][r >> 2], r & 3) * kLog2e);
+    }
     if constexpr (MASK) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
@@ -184,7 +212,7 @@ __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD))) v
 #pragma unroll
     for (int kb = 1; kb < KB; ++kb) mx = max16(s[kb], mx);
     mx = xhalf_max(mx);
-    const float tile_m = (mx == -INFINITY) ? -INFINITY : mx * c2;
+    const float tile_m = (mx == -INFINITY) ? -INFINITY : (BIAS ? mx : mx * c2);
     const bool grow = tile_m > m_run + kRescaleSlack;
     if (__builtin_amdgcn_ballot_w64(grow)) {  // wave-uniform, rarely taken
       asm volatile("" ::: "memory");          // keep it a branch (no speculation)
@@ -208,8 +236,13 @@ __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD))) v
 #pragma unroll
       for (int s8 = 0; s8 < 8; ++s8) {
         const float sv = s[ks >> 1][8 * (ks & 1) + s8];
-        float e = fast_exp2(__builtin_fmaf(sv, c2, -m_use));
-        if constexpr (MASK) e = (sv == -INFINITY) ? 0.f : e;  // exact zero even when c2 = 0
+        float e;
+        if constexpr (BIAS) {
+          e = fast_exp2(sv - m_use);  // -inf (masked or a -inf bias) gives exactly 0
+        } else {
+          e = fast_exp2(__builtin_fmaf(sv, c2, -m_use));
+          if constexpr (MASK) e = (sv == -INFINITY) ? 0.f : e;  // exact zero even when c2 = 0
+        }
         p[s8] = e;
       }
       l_run += sum8(p);
@@ -309,7 +342,11 @@ hipError_t launch_fwd(const FwdArgs& a) {
   const auto* q = static_cast<const bf16*>(a.q);
   const auto* k = static_cast<const bf16*>(a.k);
   const auto* v = static_cast<const bf16*>(a.v);
-  if (a.f32_out)
+  if (a.bias)
+    hipLaunchKernelGGL((fwd_kernel<FwdCfg<D>, CAUSAL, false, true>), dim3(total), dim3(BR * 2), 0, a.stream, q, k,
+                       v, a.o, a.lse, a.Nq, a.Nk, a.delta, a.H, nqb, 1, a.Nk, 0L, 0L, total, c2, q_sign,
+                       static_cast<const bf16*>(a.bias), a.bias_sb, a.bias_sh, a.bias_srow);
+  else if (a.f32_out)
     hipLaunchKernelGGL((fwd_kernel<FwdCfg<D>, CAUSAL, true>), dim3(total), dim3(BR * 2), 0, a.stream, q, k, v,
                        a.o, a.lse, a.Nq, a.Nk, a.delta, a.H, nqb, 1, a.Nk, 0L, 0L, total, c2, q_sign);
   else

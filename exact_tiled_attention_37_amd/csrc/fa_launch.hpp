@@ -19,6 +19,11 @@ struct FwdArgs {
   bool f32_out;
   float scale;
   hipStream_t stream;
+  // Optional additive bias (bf16); element (b, h, i, j) at
+  // bias[b * bias_sb + h * bias_sh + i * bias_srow + j]. Only with bf16 output.
+  const void* bias = nullptr;
+  long bias_sb = 0, bias_sh = 0;
+  int bias_srow = 0;
 };
 
 struct MergeArgs {
@@ -46,6 +51,14 @@ struct BwdArgs {
   int B, N, H;
   float scale;
   hipStream_t stream;
+  // Optional additive bias (as in FwdArgs) and its gradient dBias (bf16,
+  // element (b, h, i, j) at dbias[((b * H + h) * N + i) * dbias_srow + j];
+  // NULL: not computed).
+  const void* bias = nullptr;
+  long bias_sb = 0, bias_sh = 0;
+  int bias_srow = 0;
+  void* dbias = nullptr;
+  int dbias_srow = 0;
 };
 
 template <int D, bool CAUSAL>

@@ -150,6 +150,58 @@ FA_API fa_status fa_merge(const float* o_parts, const float* lse_parts, int C, v
                    int B, int N, int H, int d, hipStream_t stream);
 
 /*
+ * Attention with an additive bias on the query-key scores (the bias abstract
+ * on the related-papers page for "FlashAttention on a Napkin": prior
+ * knowledge enters as a bias matrix added to the scores):
+ *   S = scale * Q K^T + Bias  [+ causal mask],  O = softmax(S) V.
+ *
+ *   bias       bf16, element (b, h, i, j) at
+ *              bias[b * bias_stride_b + h * bias_stride_h + i * bias_stride_row + j]
+ *              (element strides; bias_stride_b or bias_stride_h may be 0 to
+ *              share one matrix across batches or heads). bias_stride_row
+ *              >= N and every stride a multiple of 8 (16-byte rows; pad the
+ *              rows when N is not a multiple of 8), and every row, the last
+ *              one included, spans bias_stride_row elements of readable
+ *              device memory (a pitched [.., N, bias_stride_row] allocation);
+ *              bias 16-byte aligned; N * bias_stride_row * 2 < 2^32.
+ *              Entries must be finite or -inf (-inf removes that key for
+ *              that query); row padding may be read but never affects the
+ *              result.
+ *   o, lse     as for fa_fwd; a row whose every score is -inf gets o = 0 and
+ *              lse = -inf.
+ *   Other arguments and errors as for fa_fwd (FA_ERR_SHAPE also for a bias
+ *   layout outside the rules above, FA_ERR_ALIGN for a misaligned bias).
+ */
+FA_API fa_status fa_fwd_bias(const void* q, const void* k, const void* v, const void* bias,
+                      long long bias_stride_b, long long bias_stride_h, int bias_stride_row,
+                      void* o, float* lse, int B, int N, int H, int d, int causal,
+                      float softmax_scale, hipStream_t stream);
+
+/*
+ * Backward of fa_fwd_bias (same loss as fa_bwd). Gradients as for fa_bwd,
+ * with the probabilities recomputed including the bias, and
+ *   dBias = dS = P * (dP - D)   (the bias enters S with unit weight).
+ *
+ *   bias, strides   exactly as passed to fa_fwd_bias
+ *   o, lse          fa_fwd_bias's outputs for the same inputs and flags
+ *   dbias           bf16 output [B, H, N, N] with row stride
+ *                   dbias_stride_row (>= N, multiple of 8; 16-byte aligned):
+ *                   element (b, h, i, j) at ((b*H + h)*N + i)*dbias_stride_row + j.
+ *                   Every element with i, j < N is written (0 where the
+ *                   causal mask or a -inf bias hides the key); row padding
+ *                   is left untouched. dBias is per (batch, head): for a bias
+ *                   shared across batches or heads the caller sums over
+ *                   them. NULL: dBias is not computed.
+ *   workspace       as for fa_bwd (fa_bwd_workspace_bytes bytes).
+ */
+FA_API fa_status fa_bwd_bias(const void* q, const void* k, const void* v, const void* bias,
+                      long long bias_stride_b, long long bias_stride_h, int bias_stride_row,
+                      const void* o, const float* lse, const void* dout, void* dq, void* dk,
+                      void* dv, void* dbias, int dbias_stride_row, void* workspace,
+                      size_t workspace_bytes, int B, int N, int H, int d, int causal,
+                      float softmax_scale, hipStream_t stream);
+
+/*
  * Decode-shaped attention: a few new query rows against a long key/value
  * history. The IPLEX post (section "Document the implementation
  * difference") separates decoding from prefill as a workload with its own

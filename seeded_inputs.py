@@ -7,7 +7,8 @@ CPU oracle and the GPU library are fed the very same bits.
 Recipe (stated once, used everywhere):
   * generator  numpy.random.Generator(PCG64(seed))
   * draw order Q, K, V, then dO (only when a backward is wanted); for
-               decode shapes Q has Nq rows and K, V have Nk rows
+               decode shapes Q has Nq rows and K, V have Nk rows; a bias
+               [B, H, N, N] is drawn last
   * each draw  standard_normal((B, N, H, d), dtype=float32), C order,
                then fp32 -> bf16 round-to-nearest-even, kept as uint16 bits.
 
@@ -81,6 +82,13 @@ DECODE_WORKLOADS = {
 }
 
 
+# Attention with an additive bias (a variant named on the related-papers page
+# for "FlashAttention on a Napkin"): a dense bias matrix per (batch, head).
+BIAS_WORKLOADS = {
+    "bias_2k": Workload("bias_2k", 2, 16, 2048, 128, False, True, 9),
+}
+
+
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round fp32 to bfloat16 (round to nearest, ties to even); return uint16 bits.
 
@@ -146,4 +154,15 @@ def draw_qkv(B: int, Nq: int, Nk: int, H: int, d: int, seed: int):
 
 def draw_decode(w: DecodeWorkload):
     return draw_qkv(w.B, w.Nq, w.Nk, w.H, w.d, w.seed)
+
+
+def draw_with_bias(B: int, N: int, H: int, d: int, seed: int):
+    """Q, K, V, dO (as `draw` with backward=True), then a bias [B, H, N, N],
+    all from one PCG64 stream, as bf16 bits."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = {}
+    for name in ("q", "k", "v", "do"):
+        out[name] = f32_to_bf16_bits(rng.standard_normal((B, N, H, d), dtype=np.float32))
+    out["bias"] = f32_to_bf16_bits(rng.standard_normal((B, H, N, N), dtype=np.float32))
+    return out
 

@@ -233,3 +233,40 @@ def test_decode_errors(lib):
     assert decode(lib, ws_bytes=need - 1) == FA_ERR_WORKSPACE
     assert decode(lib, ws=P + 64, ws_bytes=need) == FA_ERR_ALIGN
     assert decode(lib, q=P + 2) == FA_ERR_ALIGN
+
+
+def fwdb(lib, q=P, k=P, v=P, bias=P, sb=0, sh=0, sr=16, o=P, lse=P, B=1, N=9, H=2, d=64, causal=0, scale=0.125):
+    return lib.fa_fwd_bias(q, k, v, bias, sb, sh, sr, o, lse, B, N, H, d, causal, scale, None)
+
+
+def bwdb(lib, dbias=P, dsr=16, ws=P, ws_bytes=1 << 20, sr=16, sb=0, sh=0, B=1, N=9, H=2, d=64, **ptrs):
+    p = dict(q=P, k=P, v=P, bias=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P)
+    p.update(ptrs)
+    return lib.fa_bwd_bias(p["q"], p["k"], p["v"], p["bias"], sb, sh, sr, p["o"], p["lse"], p["do"], p["dq"],
+                           p["dk"], p["dv"], dbias, dsr, ws, ws_bytes, B, N, H, d, 0, 0.125, None)
+
+
+def test_bias_validation(lib):
+    assert fwdb(lib, bias=None) == FA_ERR_NULL
+    assert fwdb(lib, sr=8) == FA_ERR_SHAPE          # row stride below N
+    assert fwdb(lib, sr=12) == FA_ERR_SHAPE         # not a multiple of 8
+    assert fwdb(lib, sb=-8) == FA_ERR_SHAPE
+    assert fwdb(lib, sh=4) == FA_ERR_SHAPE
+    assert fwdb(lib, bias=P + 8) == FA_ERR_ALIGN
+    assert fwdb(lib, N=70000, sr=70000) == FA_ERR_SHAPE  # slice beyond 32-bit byte offsets
+    assert fwdb(lib, d=96) == FA_ERR_HEADDIM
+    assert bwdb(lib, bias=None) == FA_ERR_NULL
+    assert bwdb(lib, dsr=12) == FA_ERR_SHAPE
+    assert bwdb(lib, dbias=P + 8) == FA_ERR_ALIGN
+    assert bwdb(lib, ws=None) == FA_ERR_WORKSPACE
+    assert bwdb(lib, dq=None) == FA_ERR_NULL
+
+
+def test_binding_bias_layout(lib):
+    import torch
+
+    q = torch.zeros(1, 8, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.fa_fwd_bias(q, q, q, torch.zeros(1, 2, 8, 8, dtype=torch.bfloat16), causal=False)
+    pb = fa.padded_bias(2, 3, 13)
+    assert tuple(pb.shape) == (2, 3, 13, 13) and pb.stride(2) == 16 and pb.stride(3) == 1
