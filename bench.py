@@ -76,6 +76,7 @@ def parse():
                     help="heads of the workload the CPU oracle baseline runs (0 = skip)")
     ap.add_argument("--no-sweep", action="store_true", help="skip the forward sweep over the other workloads")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-shaped calls")
+    ap.add_argument("--no-bias", action="store_true", help="skip the additive-bias calls")
     ap.add_argument("--no-ring", action="store_true",
                     help="skip the key-chunk leg (one rank's share of the 16384-token sequence over 8 ranks)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -181,6 +182,48 @@ def decode_leg(fa, si, torch, dev, stream):
                      "tflops": round(4.0 * w.B * w.H * w.Nq * w.Nk * w.d / t / 1e12, 2),
                      "workspace_bytes": int(need)}
         del q, k, v, o, lse, ws
+    return out
+
+
+def bias_leg(fa, si, torch, dev, stream):
+    """Attention with an additive bias (a dense bf16 [B, H, N, N] matrix) on
+    the bias workload: forward and backward (with dBias), each priced both
+    by FLOPs against the MFMA peak and by algorithmic bytes against HBM (the
+    bias makes the traffic quadratic in N)."""
+    out = {}
+    for name, w in si.BIAS_WORKLOADS.items():
+        b = si.draw_with_bias(w.B, w.N, w.H, w.d, w.seed)
+        q, k, v, do = (si.bits_to_torch(b[t], dev) for t in ("q", "k", "v", "do"))
+        bias = fa.padded_bias(w.B, w.H, w.N, dev)
+        bias.copy_(si.bits_to_torch(b["bias"], dev))
+        del b
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+        dbias = fa.padded_bias(w.B, w.H, w.N, dev)
+        ws = torch.empty(fa.fa_bwd_workspace_bytes(w.B, w.N, w.H, w.d), dtype=torch.uint8, device=dev)
+        fwd = lambda: fa.fa_fwd_bias(q, k, v, bias, w.causal, w.scale, out=o, lse=lse)
+        bwd = lambda: fa.fa_bwd_bias(q, k, v, bias, o, lse, do, w.causal, w.scale, dq=dq, dk=dk, dv=dv,
+                                     dbias=dbias, workspace=ws)
+        for _ in range(3):
+            fwd()
+            bwd()
+        torch.cuda.synchronize()
+        tf_, tb_ = time_calls(fwd, 20, stream), time_calls(bwd, 10, stream)
+        ff = fwd_flops(w)
+        tok = w.B * w.N * w.H * w.d * 2
+        nn = w.B * w.H * w.N * w.N * 2
+        rows = w.B * w.H * w.N * 4
+        fbytes = 4 * tok + rows + nn
+        bbytes = 5 * tok + rows + nn + 3 * tok + nn + 2 * rows
+        def roof(flops, byts, t):
+            return {"ms": round(t * 1e3, 4), "tflops": round(flops / t / 1e12, 2),
+                    "mfma_frac": round(flops / t / 1e12 / PEAK_BF16_TFLOPS, 4),
+                    "gbs": round(byts / t / 1e9, 1), "hbm_frac": round(byts / t / 1e9 / PEAK_HBM_GBS, 4),
+                    "bytes_per_launch": int(byts), "flops_per_launch": flops}
+        out[name] = {"B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
+                     "fwd": roof(ff, fbytes, tf_), "bwd": roof(2.5 * ff, bbytes, tb_)}
+        del q, k, v, do, bias, o, lse, dq, dk, dv, dbias, ws
     return out
 
 
@@ -309,6 +352,8 @@ def main():
         detail["ring_rank"] = ring_rank_leg(fa, si, torch, dev, stream)
     if not args.no_decode:
         detail["decode"] = decode_leg(fa, si, torch, dev, stream)
+    if not args.no_bias:
+        detail["bias"] = bias_leg(fa, si, torch, dev, stream)
 
     cpu = None
     if args.cpu_heads > 0:

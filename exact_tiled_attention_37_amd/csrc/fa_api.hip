@@ -114,7 +114,7 @@ namespace {
 // with 32-bit byte offsets.
 fa_status check_bias(const void* bias, long long sb, long long sh, int srow, int N) {
   if (srow < N || srow % 8 != 0 || sb < 0 || sh < 0 || sb % 8 != 0 || sh % 8 != 0) return FA_ERR_SHAPE;
-  if ((long long)N * srow * 2 >= (1LL << 32)) return FA_ERR_SHAPE;
+  if (((long long)N + 64) * srow * 2 >= (1LL << 32)) return FA_ERR_SHAPE;
   if (!aligned(bias, 16)) return FA_ERR_ALIGN;
   return FA_OK;
 }

@@ -113,10 +113,8 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   constexpr int DB = D / 32;
   constexpr int QT = TQ::BYTES;
   constexpr int DMA_PER_WAVE = TQ::LOADS / 4;
-  __shared__ __attribute__((aligned(1024))) char buf0[2 * QT];  // Q tile, then dO tile
-  __shared__ __attribute__((aligned(1024))) char buf1[2 * QT];
-  __shared__ __attribute__((aligned(256))) float row0[2 * 64];  // L*log2e, then D
-  __shared__ __attribute__((aligned(256))) float row1[2 * 64];
+  __shared__ __attribute__((aligned(1024))) char qbuf[2][2 * QT];  // per stage: Q tile, then dO tile
+  __shared__ __attribute__((aligned(256))) float rowbuf[2][2 * 64];  // per stage: L*log2e, then D
   __shared__ __attribute__((aligned(1024))) char vblk[TV::BYTES];
 
   const int tid = threadIdx.x;
@@ -191,13 +189,14 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
     const int q0 = step * kQStep;
     const char* dot = qt + QT;
     // Bias of this lane's key for its 16 accumulator rows (queries).
+    // Rows past N fall beyond the resource and read as zeros (the library
+    // keeps (N + 64) * bias_srow * 2 below 2^32).
     uint32_t bb[BIAS ? 16 : 1];
     if constexpr (BIAS) {
+      const uint32_t vq = ((uint32_t)(q0 + 4 * g) * (uint32_t)bias_srow + (uint32_t)mykey) * 2u;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int q = q0 + 8 * (r >> 2) + 4 * g + (r & 3);
-        bb[r] = buf_load2(rb, ((uint32_t)min(q, N) * (uint32_t)bias_srow + (uint32_t)mykey) * 2u);
-      }
+      for (int r = 0; r < 16; ++r)
+        bb[r] = buf_load2(rb, vq, (uint32_t)(8 * (r >> 2) + (r & 3)) * (uint32_t)bias_srow * 2u);
     }
     f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
@@ -237,37 +236,27 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   };
 
   // Causal: query blocks start at the diagonal; the first kKvBlock / kQStep
-  // of them straddle it and are masked, the rest need no mask. Both loops go
-  // through the steps in pairs so each LDS buffer is named statically.
+  // of them straddle it and are masked, the rest need no mask. Step s lives
+  // in stage (s - s0) % 2; each loop has a single exit, so the accumulators
+  // keep their registers across the loop boundaries.
   const int nqs = (N + kQStep - 1) / kQStep;
   const int s0 = CAUSAL ? kb0 / kQStep : 0;
   const int sm = CAUSAL ? min(nqs, s0 + kKvBlock / kQStep) : s0;  // masked steps: [s0, sm)
-  issue(s0, buf0, row0);
+  issue(s0, qbuf[0], rowbuf[0]);
   wait_vmem();
   __syncthreads();
   int step = s0;
-  for (; step < sm; step += 2) {
-    if (step + 1 < nqs) issue(step + 1, buf1, row1);
-    compute(step, buf0, row0, std::true_type{});
-    wait_vmem();
-    __syncthreads();
-    if (step + 1 >= nqs) {  // that was the last step: nothing left for the next loop
-      step = nqs;
-      break;
-    }
-    if (step + 2 < nqs) issue(step + 2, buf0, row0);
-    compute(step + 1, buf1, row1, std::integral_constant<bool, CAUSAL>{});
+  for (; step < sm; ++step) {
+    const int t = (step - s0) & 1;
+    if (step + 1 < nqs) issue(step + 1, qbuf[t ^ 1], rowbuf[t ^ 1]);
+    compute(step, qbuf[t], rowbuf[t], std::true_type{});
     wait_vmem();
     __syncthreads();
   }
-  for (; step < nqs; step += 2) {
-    if (step + 1 < nqs) issue(step + 1, buf1, row1);
-    compute(step, buf0, row0, std::false_type{});
-    wait_vmem();
-    __syncthreads();
-    if (step + 1 >= nqs) break;
-    if (step + 2 < nqs) issue(step + 2, buf0, row0);
-    compute(step + 1, buf1, row1, std::false_type{});
+  for (; step < nqs; ++step) {
+    const int t = (step - s0) & 1;
+    if (step + 1 < nqs) issue(step + 1, qbuf[t ^ 1], rowbuf[t ^ 1]);
+    compute(step, qbuf[t], rowbuf[t], std::false_type{});
     wait_vmem();
     __syncthreads();
   }
@@ -308,8 +297,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   constexpr int DB = D / 32;
   constexpr int TILE = T::BYTES;
   constexpr int DMA_PER_WAVE = T::LOADS / 4;
-  __shared__ __attribute__((aligned(1024))) char kv0[2 * TILE];  // K tile, then V tile
-  __shared__ __attribute__((aligned(1024))) char kv1[2 * TILE];
+  __shared__ __attribute__((aligned(1024))) char kvbuf[2][2 * TILE];  // per stage: K tile, then V tile
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -329,7 +317,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   const int myq = qw0 + l32;
   const auto rb = make_rsrc(BIAS ? Bias + b * bias_sb + h * bias_sh : Q,
                             BIAS ? (uint32_t)((long)N * bias_srow * 2) : 0u);
-  const uint32_t boff = BIAS ? (uint32_t)min(myq, N) * (uint32_t)bias_srow * 2u : 0u;
+  const uint32_t boff = BIAS ? ((uint32_t)min(myq, N) * (uint32_t)bias_srow + 4u * g) * 2u : 0u;
   bf16* const dbrow = (BIAS && dBias) ? dBias + ((long)head * N + myq) * dbias_srow : nullptr;
 
   // This wave's Q and dO rows as B operands of S^T = K Q^T and dP^T = V dO^T.
@@ -375,7 +363,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
       u32x2 bw[BIAS ? 4 : 1];  // this lane's bias: 4 groups of 4 consecutive keys
       if constexpr (BIAS) {
 #pragma unroll
-        for (int rg = 0; rg < 4; ++rg) bw[rg] = buf_load8(rb, boff + (uint32_t)(key0 + kb * 32 + 8 * rg + 4 * g) * 2u);
+        for (int rg = 0; rg < 4; ++rg) bw[rg] = buf_load8(rb, boff, (uint32_t)(key0 + kb * 32 + 8 * rg) * 2u);
       }
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
@@ -438,28 +426,20 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   const int ntiles = (kv_len + kKTile - 1) / kKTile;
   // (with a bias a ragged last tile runs the masked variant: see above)
   const int jm = CAUSAL ? qblk * (kQBlock / kKTile) : (BIAS ? N / kKTile : ntiles);
-  issue(0, kv0);
+  // Tile j lives in stage j % 2; single-exit loops as in the dK/dV kernel.
+  issue(0, kvbuf[0]);
   wait_vmem();
   __syncthreads();
   int j = 0;
-  for (; j + 1 < jm; j += 2) {
-    issue(j + 1, kv1);
-    compute(j, kv0, std::false_type{});
-    wait_vmem();
-    __syncthreads();
-    if (j + 2 < ntiles) issue(j + 2, kv0);
-    compute(j + 1, kv1, std::false_type{});
+  for (; j < jm; ++j) {
+    if (j + 1 < ntiles) issue(j + 1, kvbuf[(j + 1) & 1]);
+    compute(j, kvbuf[j & 1], std::false_type{});
     wait_vmem();
     __syncthreads();
   }
-  for (; j < ntiles; j += 2) {
-    if (j + 1 < ntiles) issue(j + 1, kv1);
-    compute(j, kv0, std::integral_constant<bool, CAUSAL || BIAS>{});
-    wait_vmem();
-    __syncthreads();
-    if (j + 1 >= ntiles) break;
-    if (j + 2 < ntiles) issue(j + 2, kv0);
-    compute(j + 1, kv1, std::integral_constant<bool, CAUSAL || BIAS>{});
+  for (; j < ntiles; ++j) {
+    if (j + 1 < ntiles) issue(j + 1, kvbuf[(j + 1) & 1]);
+    compute(j, kvbuf[j & 1], std::integral_constant<bool, CAUSAL || BIAS>{});
     wait_vmem();
     __syncthreads();
   }

@@ -129,7 +129,7 @@ __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD))) v
   // rows at or past Nq read as zeros.
   const auto rb = make_rsrc(BIAS ? Bias + b * bias_sb + h * bias_sh : Q,
                             BIAS ? (uint32_t)((long)Nq * bias_srow * 2) : 0u);
-  const uint32_t boff = BIAS ? (uint32_t)min(myq, Nq) * (uint32_t)bias_srow * 2u : 0u;
+  const uint32_t boff = BIAS ? ((uint32_t)min(myq, Nq) * (uint32_t)bias_srow + 4u * g) * 2u : 0u;
 
   // Q as the B operand of S^T = K Q^T: row myq, d = 16*ks + 8*g .. +7.
   bf16x8 qf[KS];
@@ -182,7 +182,7 @@ __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD))) v
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int rg = 0; rg < 4; ++rg) bw[kb][rg] = buf_load8(rb, boff + (uint32_t)(key0 + kb * 32 + 8 * rg + 4 * g) * 2u);
+        for (int rg = 0; rg < 4; ++rg) bw[kb][rg] = buf_load8(rb, boff, (uint32_t)(key0 + kb * 32 + 8 * rg) * 2u);
     }
     // The KB accumulation chains are interleaved (independent MFMAs back to back).
     f32x16 s[KB];

@@ -163,7 +163,7 @@ FA_API fa_status fa_merge(const float* o_parts, const float* lse_parts, int C, v
  *              rows when N is not a multiple of 8), and every row, the last
  *              one included, spans bias_stride_row elements of readable
  *              device memory (a pitched [.., N, bias_stride_row] allocation);
- *              bias 16-byte aligned; N * bias_stride_row * 2 < 2^32.
+ *              bias 16-byte aligned; (N + 64) * bias_stride_row * 2 < 2^32.
  *              Entries must be finite or -inf (-inf removes that key for
  *              that query); row padding may be read but never affects the
  *              result.
