@@ -11,8 +11,11 @@ from .attention import (
     attention_decode,
     attention_forward,
     attention_forward_bias,
+    attention_forward_fp8,
     attention_forward_chunk,
     attention_forward_rows,
+    dequantize_fp8,
+    e4m3_decode,
     merge_chunks,
 )
 
@@ -26,4 +29,7 @@ __all__ = [
     "attention_backward_head",
     "attention_forward_bias",
     "attention_backward_bias",
+    "e4m3_decode",
+    "dequantize_fp8",
+    "attention_forward_fp8",
 ]

@@ -367,3 +367,39 @@ def attention_backward_bias(q, k, v, bias, do, causal: bool, scale: float):
                 dk[b, :, h, :] += scale * (ds.T @ qh[r0:r1])
                 dv[b, :, h, :] += p.T @ doh[r0:r1]
     return dq, dk, dv, dbias, o, lse, dsum
+
+
+# ---------------------------------------------------------------------------
+# FP8 (e4m3) inputs. The related-papers page for "FlashAttention on a Napkin"
+# lists an abstract on low-precision attention that runs attention on the
+# narrow-format matrix units of a newer GPU to accelerate it; the MI355X
+# analogue is the FP8 matrix unit. The page fixes no format or scaling; the
+# plain reading taken here: Q, K and V arrive as OCP FP8 E4M3 codes together
+# with one float32 descale factor per (batch, head) and tensor, a code c
+# standing for descale * e4m3(c); attention is then computed exactly on those
+# values (the oracle below). How much the low-precision arithmetic inside a
+# kernel may move the result is a separate, derived bound (see the tests).
+
+
+def e4m3_decode(codes):
+    """Values of OCP FP8 E4M3 codes: 1 sign bit, 4 exponent bits (bias 7), 3
+    mantissa bits; exponent field 0 is subnormal (mantissa * 2^-9); codes
+    0x7F and 0xFF are NaN; there are no infinities."""
+    c = np.asarray(codes, dtype=np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    return np.where((c & 0x7F) == 0x7F, np.nan, sign * mag)
+
+
+def dequantize_fp8(codes, descale):
+    """codes [B, N, H, d] (uint8) and descale [B, H] -> float64 values."""
+    return e4m3_decode(codes) * np.asarray(descale, dtype=np.float64)[:, None, :, None]
+
+
+def attention_forward_fp8(q8, k8, v8, q_descale, k_descale, v_descale, causal: bool, scale: float):
+    """Attention on FP8 inputs: the plain forward on the dequantized values.
+    Returns (O [B, N, H, d], L [B, H, N]) in float64."""
+    return attention_forward(dequantize_fp8(q8, q_descale), dequantize_fp8(k8, k_descale),
+                             dequantize_fp8(v8, v_descale), causal, scale)

@@ -89,6 +89,20 @@ BIAS_WORKLOADS = {
 }
 
 
+# FP8 (e4m3) forward workloads: the bf16 training shape and the long
+# sequence, with Q, K, V given as e4m3 codes and a descale factor per
+# (batch, head) (a low-precision attention variant named on the
+# related-papers page for "FlashAttention on a Napkin").
+FP8_WORKLOADS = {
+    "fp8_train_causal": Workload("fp8_train_causal", 4, 16, 4096, 128, True, False, 10),
+    "fp8_long_causal": Workload("fp8_long_causal", 1, 16, 16384, 128, True, False, 11),
+}
+
+# Largest |value| an input is scaled to before rounding to e4m3 (of the 448
+# the format holds), leaving headroom.
+FP8_INPUT_AMAX = 224.0
+
+
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round fp32 to bfloat16 (round to nearest, ties to even); return uint16 bits.
 
@@ -164,5 +178,44 @@ def draw_with_bias(B: int, N: int, H: int, d: int, seed: int):
     for name in ("q", "k", "v", "do"):
         out[name] = f32_to_bf16_bits(rng.standard_normal((B, N, H, d), dtype=np.float32))
     out["bias"] = f32_to_bf16_bits(rng.standard_normal((B, H, N, N), dtype=np.float32))
+    return out
+
+
+
+
+def f64_to_e4m3_bits(x: np.ndarray) -> np.ndarray:
+    """Round to the OCP FP8 E4M3 format (1 sign, 4 exponent bits with bias 7,
+    3 mantissa bits, subnormals, largest finite 448, no infinities) with
+    round-to-nearest-even, saturating at +-448; returns uint8 codes."""
+    x = np.asarray(x, dtype=np.float64)
+    sign = np.where(np.signbit(x), 0x80, 0).astype(np.uint8)
+    a = np.minimum(np.abs(x), 448.0)
+    code = np.zeros(a.shape, dtype=np.int64)
+    sub = a < 2.0 ** -6
+    code[sub] = np.rint(a[sub] / 2.0 ** -9).astype(np.int64)          # 0 .. 8 (8 is the smallest normal)
+    m, e = np.frexp(a[~sub])                                           # a = m * 2^e, m in [0.5, 1)
+    e = e - 1                                                          # a = (2m) * 2^e, 2m in [1, 2)
+    mq = np.rint((2.0 * m - 1.0) * 8.0).astype(np.int64)
+    carry = mq == 8
+    e = e + carry
+    mq = np.where(carry, 0, mq)
+    code[~sub] = ((e + 7) << 3) | mq
+    return (np.minimum(code, 0x7E).astype(np.uint8) | sign).astype(np.uint8)
+
+
+def draw_fp8(B: int, N: int, H: int, d: int, seed: int):
+    """Q, K, V drawn as in `draw` (float32 N(0,1), one PCG64 stream), then for
+    each tensor and each (batch, head) a descale factor D = max|x| / 224
+    (float32) and e4m3 codes of x / D. Returns uint8 codes q, k, v
+    [B, N, H, d] and float32 descales q_descale, k_descale, v_descale [B, H];
+    the value a code stands for is D * e4m3(code)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = {}
+    for name in ("q", "k", "v"):
+        x = rng.standard_normal((B, N, H, d), dtype=np.float32)
+        amax = np.abs(x).max(axis=(1, 3)).astype(np.float32)            # [B, H]
+        desc = (amax / np.float32(FP8_INPUT_AMAX)).astype(np.float32)
+        out[name] = f64_to_e4m3_bits(x.astype(np.float64) / desc.astype(np.float64)[:, None, :, None])
+        out[name + "_descale"] = desc
     return out
 

@@ -634,6 +634,51 @@ def pin_bias_finite_differences(mod):
             assert abs(num - dq[0, i, 0, t]) <= 1e-7 * max(1.0, abs(num)), f"dQ[{i},{t}]"
 
 
+# --------------------------------------------------------------------------
+# FP8 (e4m3) input pins
+
+
+def pin_e4m3_decode(mod):
+    """The e4m3 decode against values fixed by the format (1.0, 448, the
+    smallest subnormal and normal, signs, NaN codes) and, for all 256 codes,
+    against torch's independent float8_e4m3fn implementation."""
+    import torch
+
+    dec = mod.e4m3_decode(np.arange(256))
+    fixed = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x38: 1.0, 0x39: 1.125,
+             0x40: 2.0, 0x7E: 448.0, 0xB8: -1.0, 0xFE: -448.0, 0x80: -0.0}
+    for code, val in fixed.items():
+        assert dec[code] == val, f"code {code:#x}: {dec[code]} != {val}"
+    assert np.isnan(dec[0x7F]) and np.isnan(dec[0xFF])
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    both_nan = np.isnan(ref) & np.isnan(dec)
+    assert np.all(both_nan | (ref == dec)), "decode differs from torch float8_e4m3fn"
+    # monotone over the positive finite codes
+    pos = dec[:0x7F]
+    assert np.all(np.diff(pos) > 0)
+
+
+def pin_fp8_forward(mod):
+    """FP8 attention is the forward on the dequantized values: checked
+    against scalar loops on the decoded inputs, and the descale of V scales
+    the output while the descales of Q and K act only through their product."""
+    B, N, H, d = 1, 7, 2, 4
+    rng = np.random.Generator(np.random.PCG64(350))
+    codes = [rng.integers(0, 0x7F, (B, N, H, d)).astype(np.uint8) | (rng.integers(0, 2, (B, N, H, d)) * 0x80).astype(np.uint8)
+             for _ in range(3)]
+    desc = [np.abs(rng.standard_normal((B, H))) * 0.01 + 0.002 for _ in range(3)]
+    for causal in (False, True):
+        o, lse = mod.attention_forward_fp8(*codes, *desc, causal, 0.5)
+        vals = [mod.e4m3_decode(c) * dd[:, None, :, None] for c, dd in zip(codes, desc)]
+        ob, lseb = _brute_forward(*vals, causal, 0.5)
+        _close(o, ob, 1e-13, what="fp8 brute output")
+        _close(lse, lseb, 1e-13, what="fp8 brute lse")
+        o2, l2 = mod.attention_forward_fp8(codes[0], codes[1], codes[2], desc[0] * 2.0, desc[1] / 2.0,
+                                           desc[2] * 3.0, causal, 0.5)
+        _close(o2, 3.0 * o, what="descale V scales O")
+        _close(l2, lse, what="only the product of the Q and K descales matters")
+
+
 FORWARD_PINS = [
     pin_rows_sum_to_one,
     pin_q_zero,
@@ -659,6 +704,10 @@ BIAS_PINS = [
     pin_bias_torch_sdpa,
     pin_bias_finite_differences,
 ]
+FP8_PINS = [
+    pin_e4m3_decode,
+    pin_fp8_forward,
+]
 BACKWARD_PINS = [
     pin_constant_v,
     pin_backward_invariants,
@@ -667,4 +716,4 @@ BACKWARD_PINS = [
     pin_worked_examples,
     pin_backward_head,
 ]
-ALL_PINS = FORWARD_PINS + CHUNK_PINS + BIAS_PINS + BACKWARD_PINS
+ALL_PINS = FORWARD_PINS + CHUNK_PINS + BIAS_PINS + FP8_PINS + BACKWARD_PINS

@@ -107,6 +107,13 @@ MUTATIONS = [
      "dv[b, :, h, :] += p @ doh[r0:r1]\n    return dq, dk, dv, dbias"),
     ("bias dK unscaled", "dk[b, :, h, :] += scale * (ds.T @ qh[r0:r1])\n                dv[b, :, h, :] += p.T @ doh[r0:r1]\n    return dq, dk, dv, dbias",
      "dk[b, :, h, :] += (ds.T @ qh[r0:r1])\n                dv[b, :, h, :] += p.T @ doh[r0:r1]\n    return dq, dk, dv, dbias"),
+    ("e4m3 exponent bias", "(1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0)",
+     "(1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 8.0)"),
+    ("e4m3 subnormal scale", "np.where(e == 0, m * 2.0 ** -9,", "np.where(e == 0, m * 2.0 ** -10,"),
+    ("e4m3 sign ignored", "sign = np.where(c & 0x80, -1.0, 1.0)", "sign = np.where(c & 0x80, 1.0, 1.0)"),
+    ("fp8 Q takes the K descale", "return attention_forward(dequantize_fp8(q8, q_descale),",
+     "return attention_forward(dequantize_fp8(q8, k_descale),"),
+    ("fp8 V descale dropped", "dequantize_fp8(v8, v_descale), causal, scale)", "dequantize_fp8(v8, v_descale * 0 + 1), causal, scale)"),
     ("head slice swapped", "sl = (slice(b, b + 1), slice(None), slice(h, h + 1), slice(None))",
      "sl = (slice(h, h + 1), slice(None), slice(b, b + 1), slice(None))"),
 ]
