@@ -29,6 +29,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6  # 256 CUs x 4096 dense bf16 flop/clk/CU x 2.4 GHz
+PEAK_FP8_TFLOPS = 5033.2   # dense fp8 MFMA: twice the bf16 rate
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "train_causal_traffic.json")
 
@@ -77,6 +78,7 @@ def parse():
     ap.add_argument("--no-sweep", action="store_true", help="skip the forward sweep over the other workloads")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-shaped calls")
     ap.add_argument("--no-bias", action="store_true", help="skip the additive-bias calls")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 forward calls")
     ap.add_argument("--no-ring", action="store_true",
                     help="skip the key-chunk leg (one rank's share of the 16384-token sequence over 8 ranks)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -227,6 +229,37 @@ def bias_leg(fa, si, torch, dev, stream):
     return out
 
 
+def fp8_leg(fa, si, torch, dev, stream):
+    """FP8 (e4m3) forward on the FP8 workloads: TFLOP/s against the dense FP8
+    MFMA peak, with the bf16 forward of the same shape (random bf16 inputs)
+    timed beside it."""
+    out = {}
+    for name, w in si.FP8_WORKLOADS.items():
+        b8 = si.draw_fp8(w.B, w.N, w.H, w.d, w.seed)
+        t = {k: torch.from_numpy(v).to(dev) for k, v in b8.items()}
+        del b8
+        o = torch.empty((w.B, w.N, w.H, w.d), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+        call = lambda: fa.fa_fwd_fp8(t["q"], t["k"], t["v"], t["q_descale"], t["k_descale"], t["v_descale"],
+                                     w.causal, w.scale, out=o, lse=lse)
+        bq = torch.randn((w.B, w.N, w.H, w.d), device=dev).to(torch.bfloat16)
+        bk, bv = torch.randn_like(bq, dtype=torch.float32).to(torch.bfloat16), torch.randn_like(bq, dtype=torch.float32).to(torch.bfloat16)
+        ref = lambda: fa.fa_fwd(bq, bk, bv, w.causal, w.scale, out=o, lse=lse)
+        for _ in range(3):
+            call()
+            ref()
+        torch.cuda.synchronize()
+        reps = 10 if w.N * w.N * w.B * w.H >= (1 << 30) else 30
+        t8, t16 = time_calls(call, reps, stream), time_calls(ref, reps, stream)
+        ff = fwd_flops(w)
+        out[name] = {"B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal, "ms": round(t8 * 1e3, 4),
+                     "roofline": {"bound": "mfma", "achieved": round(ff / t8 / 1e12, 2), "peak": PEAK_FP8_TFLOPS,
+                                  "unit": "TFLOP/s", "frac": round(ff / t8 / 1e12 / PEAK_FP8_TFLOPS, 4)},
+                     "bf16_fwd_ms": round(t16 * 1e3, 4), "speedup_vs_bf16": round(t16 / t8, 3)}
+        del t, o, lse, bq, bk, bv
+    return out
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -354,6 +387,8 @@ def main():
         detail["decode"] = decode_leg(fa, si, torch, dev, stream)
     if not args.no_bias:
         detail["bias"] = bias_leg(fa, si, torch, dev, stream)
+    if not args.no_fp8:
+        detail["fp8"] = fp8_leg(fa, si, torch, dev, stream)
 
     cpu = None
     if args.cpu_heads > 0:

@@ -32,6 +32,7 @@ __all__ = [
     "fa_decode_workspace_bytes",
     "fa_fwd_bias",
     "fa_bwd_bias",
+    "fa_fwd_fp8",
     "fa_status_string",
     "fa_version",
     "EXPORTED_SYMBOLS",
@@ -40,7 +41,8 @@ __all__ = [
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libfa_mi355x.so"
 EXPORTED_SYMBOLS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd_chunk", "fa_merge", "fa_decode",
-                    "fa_decode_workspace_bytes", "fa_fwd_bias", "fa_bwd_bias", "fa_status_string", "fa_version")
+                    "fa_decode_workspace_bytes", "fa_fwd_bias", "fa_bwd_bias", "fa_fwd_fp8", "fa_status_string",
+                    "fa_version")
 
 _lib = None
 
@@ -87,6 +89,8 @@ def load_library():
     lib.fa_fwd_bias.restype = i
     lib.fa_bwd_bias.argtypes = [vp, vp, vp, vp, ll, ll, i, vp, vp, vp, vp, vp, vp, vp, i, vp, sz, i, i, i, i, i, f, vp]
     lib.fa_bwd_bias.restype = i
+    lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
+    lib.fa_fwd_fp8.restype = i
     lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i]
     lib.fa_bwd_workspace_bytes.restype = sz
     lib.fa_status_string.argtypes = [i]
@@ -378,3 +382,36 @@ def fa_bwd_bias(q, k, v, bias, o, lse, do, causal: bool, softmax_scale: Optional
     if st != 0:
         raise FaError(st, "fa_bwd_bias")
     return dq, dk, dv, dbias
+
+
+def fa_fwd_fp8(q8, k8, v8, q_descale, k_descale, v_descale, causal: bool, softmax_scale: Optional[float] = None,
+               out=None, lse=None):
+    """FP8 forward: q8, k8, v8 are uint8 e4m3 codes [B, N, H, 128] and the
+    descales float32 [B, H]. Returns (o bf16 [B, N, H, 128], lse float32
+    [B, H, N])."""
+    import torch
+
+    for name, t in (("q8", q8), ("k8", k8), ("v8", v8)):
+        if t.dtype != torch.uint8 or t.dim() != 4 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous uint8 device tensor [B, N, H, d]")
+        if tuple(t.shape) != tuple(q8.shape):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(q8.shape)}")
+    B, N, H, d = q8.shape
+    for name, t in (("q_descale", q_descale), ("k_descale", k_descale), ("v_descale", v_descale)):
+        if t.dtype != torch.float32 or tuple(t.shape) != (B, H) or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous float32 device tensor of shape {(B, H)}")
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        out = torch.empty((B, N, H, d), dtype=torch.bfloat16, device=q8.device)
+    _check_bnhd("out", out, (B, N, H, d))
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
+    _check_lse(lse, B, N, H)
+    st = load_library().fa_fwd_fp8(
+        q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), q_descale.data_ptr(), k_descale.data_ptr(),
+        v_descale.data_ptr(), out.data_ptr(), lse.data_ptr(), B, N, H, d, int(bool(causal)), scale,
+        _stream_handle(q8.device),
+    )
+    if st != 0:
+        raise FaError(st, "fa_fwd_fp8")
+    return out, lse

@@ -176,6 +176,25 @@ fa_status fa_bwd_bias(const void* q, const void* k, const void* v, const void* b
   return dispatch(d, causal, [&](auto D, auto C) { return fa::launch_bwd<decltype(D)::value, decltype(C)::value>(a); });
 }
 
+fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, const float* q_descale, const float* k_descale,
+                     const float* v_descale, void* o, float* lse, int B, int N, int H, int d, int causal,
+                     float softmax_scale, hipStream_t stream) {
+  if (!q || !k || !v || !q_descale || !k_descale || !v_descale || !o || !lse) return FA_ERR_NULL;
+  if (d != 128) return FA_ERR_HEADDIM;
+  fa_status st = check_shape(B, N, H, d);
+  if (st != FA_OK) return st;
+  if (!std::isfinite(softmax_scale)) return FA_ERR_SCALE;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4) ||
+      !aligned(q_descale, 4) || !aligned(k_descale, 4) || !aligned(v_descale, 4))
+    return FA_ERR_ALIGN;
+  st = check_device();
+  if (st != FA_OK) return st;
+  (void)hipGetLastError();
+  const fa::Fp8Args a{q, k, v, q_descale, k_descale, v_descale, o, lse, B, N, H, softmax_scale, stream};
+  const hipError_t e = causal ? fa::launch_fwd_fp8<true>(a) : fa::launch_fwd_fp8<false>(a);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 size_t fa_decode_workspace_bytes(int B, int Nq, int Nk, int H, int d) {
   if (check_shape(B, Nq, H, d) != FA_OK || check_shape(B, Nk, H, d) != FA_OK) return 0;
   return fa::decode_workspace_bytes(B, Nq, Nk, H, d);

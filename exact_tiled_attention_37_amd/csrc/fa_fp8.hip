@@ -1,0 +1,250 @@
+// FP8 (e4m3) forward of exact tiled attention for gfx950.
+//
+// Low-precision attention (an abstract on the related-papers page for
+// "FlashAttention on a Napkin" runs attention on narrow-format matrix units)
+// moved to the MI355X FP8 matrix unit: Q, K and V arrive as OCP E4M3 codes
+// with one float32 descale per (batch, head) and tensor, and both products run
+// on v_mfma_scale_f32_32x32x64_f8f6f4 (64-deep, twice the bf16 rate). The
+// tiling, online softmax, deferred normalisation and causal skipping are
+// those of the bf16 forward (IPLEX post on FlashAttention-2 work
+// partitioning, sections "Tiling preserves the attention calculation" and
+// "Three changes improve GPU utilisation").
+//
+// What changes with 8-bit operands:
+//   * S^T = K Q^T: a lane's A/B operand is 32 consecutive bytes of a K or Q
+//     row (both operands use the same byte order, so the reduction pairs
+//     them correctly); the descales of Q and K fold into the exp2 scale.
+//   * P is rounded to e4m3 for the PV product. It is taken as
+//     2^4 * exp2(s - m) with the running max allowed to lag by at most 2^4,
+//     so every value is <= 2^8 (the format holds 448) and values down to
+//     2^-10 still land on normal e4m3 numbers. The row sum uses the fp32
+//     values; the scale cancels in O = (P V) / l and is removed from the
+//     logsumexp.
+//   * P^T comes straight from the S^T accumulators: with the V rows of a
+//     tile stored in LDS in a key order that exchanges bits 2 and 3 of the
+//     key index, byte p of a lane's P operand (accumulator p % 16 of 32-key
+//     block p / 16) meets byte p of its V^T operand, which four 8-bit
+//     transpose loads (ds_read_b64_tr_b8) deliver.
+//   * LDS tiles hold 64 rows of 128 bytes (d = 128); the 16-byte chunk c of
+//     row r sits at position c ^ (r & 7), which keeps both the row reads of
+//     K and the transpose reads of V free of bank conflicts.
+// O is written as bf16 (times the V descale), the logsumexp as fp32.
+
+#include <type_traits>
+
+#include "fa_common.hpp"
+#include "fa_launch.hpp"
+
+namespace fa {
+
+namespace {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kF8D = 128;                  // head dimension = bytes per row
+constexpr int kF8BR = 128;                 // query rows per workgroup (4 waves x 32)
+constexpr int kF8BC = 64;                  // keys per K/V tile
+constexpr int kF8Threads = 256;
+constexpr int kF8Tile = kF8BC * kF8D;      // bytes of one K or V tile
+constexpr float kF8Slack = 4.f;            // log2 units the running max may lag
+constexpr float kF8Shift = 4.f;            // P is scaled by 2^4 before rounding
+
+__device__ __forceinline__ constexpr int f8_slot(int r, int c) { return r * kF8D + ((c ^ (r & 7)) << 4); }
+// LDS row r of a V tile holds key row vperm(r) (bits 2 and 3 exchanged; an involution).
+__device__ __forceinline__ constexpr int vperm(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+
+__device__ __forceinline__ f32x16 mfma_f8(const i32x8& a, const i32x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);  // scales 2^0
+}
+
+__device__ __forceinline__ i32x2 lds_read_tr8(const char* base, int off) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((FA_LDS i32x2*)((FA_LDS char*)base + off));
+}
+
+__device__ __forceinline__ i32x8 cat(const u32x4& lo, const u32x4& hi) {
+  return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+}
+
+template <bool CAUSAL>
+__global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_fp8_kernel(
+    const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, const uint8_t* __restrict__ V,
+    const float* __restrict__ q_descale, const float* __restrict__ k_descale, const float* __restrict__ v_descale,
+    bf16* __restrict__ O, float* __restrict__ LSE, int N, int H, int nqb, int total_blocks, float scale) {
+  __shared__ __attribute__((aligned(1024))) char ring[2][2 * kF8Tile];  // per stage: K tile, V tile
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5, l32 = lane & 31, G = lane >> 4, j16 = lane & 15;
+
+  const int logical = xcd_remap(blockIdx.x, total_blocks);
+  const int head = logical / nqb;                      // b * H + h
+  const int qblk = nqb - 1 - (logical - head * nqb);   // longest causal rows first
+  const int b = head / H, h = head - b * H;
+  const float qk = scale * q_descale[head] * k_descale[head];
+  const float c2 = fabsf(qk) * kLog2e;
+  const uint32_t q_sign = qk < 0.f ? 0x80808080u : 0u;  // a negative factor negates Q
+  const float v_scale = v_descale[head];
+  const long hoff = ((long)b * N * H + h) * kF8D;      // byte offset of token 0
+  const uint32_t tokb = (uint32_t)H * kF8D;
+  const uint32_t nrec = (uint32_t)(N - 1) * tokb + kF8D;
+  const auto rq = make_rsrc(Q + hoff, nrec);
+  const u32x4 rk = make_raw_rsrc(K + hoff, nrec);
+  const u32x4 rv = make_raw_rsrc(V + hoff, nrec);
+
+  const int qw0 = qblk * kF8BR + wave * 32;
+  const int myq = qw0 + l32;
+
+  // Q as the B operand: bytes 64 ks + 32 g .. +31 of row myq.
+  i32x8 qf[2];
+  {
+    const uint32_t qoff = row_off(myq, N, tokb, 32u * g);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const u32x4 lo = buf_load16(rq, qoff + 64 * ks) ^ q_sign;
+      const u32x4 hi = buf_load16(rq, qoff + 64 * ks + 16) ^ q_sign;
+      qf[ks] = cat(lo, hi);
+    }
+  }
+
+  // LDS-DMA of one tile: wave load u (0..7) fills LDS rows 8u .. 8u + 7;
+  // lane i writes slot i, i.e. row 8u + i / 8 at chunk position i % 8.
+  auto issue = [&](int tile, char* dst) __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int u = wave + 4 * t;
+      const int r = 8 * u + (lane >> 3);
+      const uint32_t c16 = 16u * (uint32_t)((lane & 7) ^ (r & 7));
+      dma16(rk, dst + u * 1024, row_off(tile * kF8BC + r, N, tokb, c16));
+      dma16(rv, dst + kF8Tile + u * 1024, row_off(tile * kF8BC + vperm(r), N, tokb, c16));
+    }
+  };
+
+  const int kv_len = CAUSAL ? min(N, (qblk + 1) * kF8BR) : N;
+  const int ntiles = (kv_len + kF8BC - 1) / kF8BC;
+
+  f32x16 oacc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) oacc[i] = f32x16{};
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+
+  auto compute = [&](int j, const char* kt, auto mask_tag) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    const int key0 = j * kF8BC;
+    const char* vt = kt + kF8Tile;
+    f32x16 s[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int row = kb * 32 + l32;
+        const i32x8 a = cat(lds_read16(kt, f8_slot(row, 4 * ks + 2 * g)), lds_read16(kt, f8_slot(row, 4 * ks + 2 * g + 1)));
+        s[kb] = mfma_f8(a, qf[ks], s[kb]);
+      }
+    if constexpr (MASK) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+          if ((CAUSAL && key > myq) || key >= N) s[kb][r] = -INFINITY;
+        }
+    }
+    float mx = max16(s[1], max16(s[0], -INFINITY));
+    mx = xhalf_max(mx);
+    const float tile_m = (mx == -INFINITY) ? -INFINITY : mx * c2;
+    const bool grow = tile_m > m_run + kF8Slack;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      asm volatile("" ::: "memory");
+      const float m_new = grow ? tile_m : m_run;
+      const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+    const float bias = kF8Shift - m_use;
+    // P^T operand: byte p = 2^4 * exp2(s - m) of accumulator p % 16 of block p / 16.
+    i32x8 pf;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      float e[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float sv = s[w >> 2][4 * (w & 3) + i];
+        float x = fast_exp2(__builtin_fmaf(sv, c2, bias));
+        if constexpr (MASK) x = (sv == -INFINITY) ? 0.f : x;
+        e[i] = x;
+      }
+      l_run += (e[0] + e[1]) + (e[2] + e[3]);
+      int d = __builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], 0, false);
+      pf[w] = __builtin_amdgcn_cvt_pk_fp8_f32(e[2], e[3], d, true);
+    }
+    // O^T += V^T P^T: for each 32-column block of d, four transpose loads.
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      i32x8 a;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const i32x2 t = lds_read_tr8(vt, f8_slot(16 * q4 + 8 * g + (j16 >> 1), 2 * db + (G & 1)) + 8 * (j16 & 1));
+        a[2 * q4] = t[0];
+        a[2 * q4 + 1] = t[1];
+      }
+      oacc[db] = mfma_f8(a, pf, oacc[db]);
+    }
+  };
+
+  const int jm = CAUSAL ? min(qblk * (kF8BR / kF8BC), N / kF8BC) : N / kF8BC;
+  issue(0, ring[0]);
+  wait_vmem();
+  __syncthreads();
+  int j = 0;
+  for (; j < jm; ++j) {
+    if (j + 1 < ntiles) issue(j + 1, ring[(j + 1) & 1]);
+    compute(j, ring[j & 1], std::false_type{});
+    wait_vmem();
+    __syncthreads();
+  }
+  for (; j < ntiles; ++j) {
+    if (j + 1 < ntiles) issue(j + 1, ring[(j + 1) & 1]);
+    if (!CAUSAL || j * kF8BC <= qw0 + 31) compute(j, ring[j & 1], std::true_type{});
+    wait_vmem();
+    __syncthreads();
+  }
+
+  const float l_tot = xhalf_sum(l_run);
+  const bool seen = l_tot > 0.f;
+  const float inv = seen ? v_scale / l_tot : 0.f;
+  if (myq < N) {
+    if (g == 0) LSE[(long)head * N + myq] = seen ? (m_run - kF8Shift + log2f(l_tot)) * kLn2 : -INFINITY;
+    bf16* orow = O + ((long)b * N * H + h) * kF8D + (long)myq * H * kF8D;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int rq4 = 0; rq4 < 4; ++rq4) {
+        const f32x4 x = {oacc[db][4 * rq4] * inv, oacc[db][4 * rq4 + 1] * inv, oacc[db][4 * rq4 + 2] * inv,
+                         oacc[db][4 * rq4 + 3] * inv};
+        *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * rq4 + 4 * g) = to_bf16x4(x);
+      }
+  }
+}
+
+}  // namespace
+
+template <bool CAUSAL>
+hipError_t launch_fwd_fp8(const Fp8Args& a) {
+  const int nqb = (a.N + kF8BR - 1) / kF8BR;
+  const int total = a.B * a.H * nqb;
+  hipLaunchKernelGGL((fwd_fp8_kernel<CAUSAL>), dim3(total), dim3(kF8Threads), 0, a.stream,
+                     static_cast<const uint8_t*>(a.q), static_cast<const uint8_t*>(a.k),
+                     static_cast<const uint8_t*>(a.v), a.q_descale, a.k_descale, a.v_descale,
+                     static_cast<bf16*>(a.o), a.lse, a.N, a.H, nqb, total, a.scale);
+  return hipGetLastError();
+}
+
+template hipError_t launch_fwd_fp8<false>(const Fp8Args&);
+template hipError_t launch_fwd_fp8<true>(const Fp8Args&);
+
+}  // namespace fa

@@ -70,6 +70,25 @@ hipError_t launch_bwd(const BwdArgs& a);
 template <int D>
 hipError_t launch_merge(const MergeArgs& a);
 
+// FP8 (e4m3) forward, d = 128: q, k, v are e4m3 codes [B, N, H, 128]; the
+// descales are float32 [B, H].
+struct Fp8Args {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* q_descale;
+  const float* k_descale;
+  const float* v_descale;
+  void* o;      // bf16 [B, N, H, 128]
+  float* lse;   // [B, H, N]
+  int B, N, H;
+  float scale;
+  hipStream_t stream;
+};
+
+template <bool CAUSAL>
+hipError_t launch_fwd_fp8(const Fp8Args& a);
+
 // Decode-shaped attention: Nq query rows (the last Nq positions) against Nk
 // keys, split into key ranges whose float32 results are merged.
 struct DecodeArgs {

@@ -202,6 +202,33 @@ FA_API fa_status fa_bwd_bias(const void* q, const void* k, const void* v, const 
                       float softmax_scale, hipStream_t stream);
 
 /*
+ * FP8 (e4m3) forward, d = 128 (low-precision attention on narrow-format
+ * matrix units: an abstract on the related-papers page for "FlashAttention
+ * on a Napkin"; here the MI355X FP8 matrix unit). Same result definition as
+ * fa_fwd, computed on the values the codes stand for:
+ *
+ *   q, k, v      uint8 OCP FP8 E4M3 codes, [B, N, H, 128], 16-byte aligned
+ *                (codes 0x7F / 0xFF are NaN and must not occur)
+ *   q_descale,   float32 [B, H] each: the value of code c of (batch b, head h)
+ *   k_descale,   is descale[b * H + h] * e4m3(c)
+ *   v_descale
+ *   o            [B, N, H, 128] bf16 output; lse [B, H, N] float32 (natural
+ *                log of the scaled scores of the dequantized inputs)
+ *
+ * Inside the kernel both products run on the FP8 matrix unit and the
+ * probabilities are rounded to e4m3 for the P V product (the row sums and the
+ * logsumexp use their fp32 values). That rounding bounds the error of each
+ * output element by about 2^-4 times the probability-weighted mean of |V| in
+ * its column (plus 2^-14 per key for probabilities below 2^-10), a bound the
+ * tests check element by element. Errors as for fa_fwd; FA_ERR_HEADDIM for
+ * d != 128.
+ */
+FA_API fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, const float* q_descale,
+                     const float* k_descale, const float* v_descale, void* o, float* lse,
+                     int B, int N, int H, int d, int causal, float softmax_scale,
+                     hipStream_t stream);
+
+/*
  * Decode-shaped attention: a few new query rows against a long key/value
  * history. The IPLEX post (section "Document the implementation
  * difference") separates decoding from prefill as a workload with its own

@@ -270,3 +270,20 @@ def test_binding_bias_layout(lib):
         fa.fa_fwd_bias(q, q, q, torch.zeros(1, 2, 8, 8, dtype=torch.bfloat16), causal=False)
     pb = fa.padded_bias(2, 3, 13)
     assert tuple(pb.shape) == (2, 3, 13, 13) and pb.stride(2) == 16 and pb.stride(3) == 1
+
+
+def fp8(lib, q=P, k=P, v=P, qd=P, kd=P, vd=P, o=P, lse=P, B=1, N=9, H=2, d=128, causal=1, scale=0.1):
+    return lib.fa_fwd_fp8(q, k, v, qd, kd, vd, o, lse, B, N, H, d, causal, scale, None)
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "qd", "kd", "vd", "o", "lse"])
+def test_fp8_null_pointer(lib, which):
+    assert fp8(lib, **{which: None}) == FA_ERR_NULL
+
+
+def test_fp8_errors(lib):
+    assert fp8(lib, d=64) == FA_ERR_HEADDIM
+    assert fp8(lib, N=0) == FA_ERR_SHAPE
+    assert fp8(lib, scale=float("nan")) == FA_ERR_SCALE
+    assert fp8(lib, q=P + 8) == FA_ERR_ALIGN
+    assert fp8(lib, kd=P + 2) == FA_ERR_ALIGN

@@ -1,0 +1,59 @@
+"""CPU self-check of the FP8 forward's per-element error bound: an exact
+result and a result with e4m3-rounded probabilities lie inside it, while
+plausible kernel mistakes (planted here, in fp64 on the CPU) fall outside."""
+
+import numpy as np
+
+import oracle
+import seeded_inputs as si
+from tests.fp8_bound import head_bound
+
+
+def _e4m3_round(x):
+    return oracle.e4m3_decode(si.f64_to_e4m3_bits(x))
+
+
+def _inputs(N, seed, causal):
+    b8 = si.draw_fp8(1, N, 1, 128, seed)
+    q, k, v = (oracle.dequantize_fp8(b8[n], b8[n + "_descale"])[0, :, 0] for n in ("q", "k", "v"))
+    return q, k, v, b8["v_descale"][0, 0]
+
+
+def _emulate(q, k, v, causal, scale, c_log2=4.0, vrows=None, vscale=1.0, score_scale=None):
+    """The kernel's arithmetic in fp64: P = 2^c * exp2(t - m) rounded to e4m3,
+    O = (P v) / sum(unrounded P)."""
+    N = k.shape[0]
+    s = (scale if score_scale is None else score_scale) * (q @ k.T)
+    if causal:
+        s = np.where(np.arange(N)[None, :] > np.arange(N)[:, None], -np.inf, s)
+    m = s.max(axis=1, keepdims=True)
+    p = np.exp2((s - m) / np.log(2.0) + c_log2)
+    pr = _e4m3_round(p)
+    vv = v if vrows is None else v[vrows]
+    return (pr @ vv) * vscale / p.sum(axis=1, keepdims=True)
+
+
+def _ratio(o, q, k, v, causal, scale):
+    ro, rl, bd = head_bound(q, k, v, causal, scale)
+    return float((np.abs(o - ro) / bd).max())
+
+
+def test_exact_and_rounded_results_are_inside():
+    for causal in (False, True):
+        q, k, v, _ = _inputs(300, 20, causal)
+        ro, _, _ = head_bound(q, k, v, causal, 0.088)
+        assert _ratio(ro, q, k, v, causal, 0.088) < 1e-3
+        for c in (4.0, 6.0, 8.0):        # every scale the lagging running max allows
+            assert _ratio(_emulate(q, k, v, causal, 0.088, c), q, k, v, causal, 0.088) <= 1.0
+
+
+def test_planted_kernel_mistakes_are_outside():
+    q, k, v, vd = _inputs(300, 21, True)
+    N = k.shape[0]
+    perm = np.arange(N)
+    swapped = (perm & ~12) | ((perm & 4) << 1) | ((perm & 8) >> 1)     # V rows left in LDS key order
+    assert _ratio(_emulate(q, k, v, True, 0.088, vrows=swapped), q, k, v, True, 0.088) > 1.0
+    assert _ratio(_emulate(q, k, v, True, 0.088, vscale=1.0 / vd), q, k, v, True, 0.088) > 1.0  # V descale dropped
+    assert _ratio(_emulate(q, k, v, True, 0.088, score_scale=1.0), q, k, v, True, 0.088) > 1.0  # unscaled scores
+    shift = np.roll(np.arange(N), 1)                                   # off-by-one key
+    assert _ratio(_emulate(q, k, v, True, 0.088, vrows=shift), q, k, v, True, 0.088) > 1.0

@@ -1,0 +1,131 @@
+"""GPU parity of the FP8 (e4m3) forward (fa_fwd_fp8) against the fp64 oracle,
+through the C ABI.
+
+The reference is exact attention on the dequantized inputs. The kernel's own
+low-precision step is the rounding of the probabilities to e4m3 for the P V
+product (the products of e4m3 inputs are exact in fp32). A probability p' =
+exp(s - max) is held as P = c p' with c between 2^4 and 2^8 (the running
+max lags by at most 2^4) and rounded to nearest: the error is at most
+2^-4 P in the normal range and 2^-10 below 2^-6. Divided by the fp32 row sum
+sum(P), the error of output element (i, d) is therefore at most
+
+    sum_j max(2^-4 p'_ij, 2^-14) |v_jd| / sum_j p'_ij
+
+plus the bf16 rounding of the output (2^-9 |O|, taken as 2^-8 |O|); the
+fp32 accumulation and exp2 errors are orders of magnitude smaller. Every
+output element must lie within that bound. The logsumexp uses the fp32
+values and keeps the core 1e-3 bound.
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import exact_tiled_attention_37_amd as fa
+import oracle
+import seeded_inputs as si
+from tests.fp8_bound import head_bound
+
+pytestmark = pytest.mark.gpu
+
+LSE_TOL = 1e-3
+
+
+def announce(msg):
+    sys.__stderr__.write(f"[gpu-case] {msg}\n")
+    sys.__stderr__.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible: GPU tests need an MI355X")
+    fa.load_library()
+
+
+def run(b8, causal, scale):
+    import torch
+
+    t = {k: torch.from_numpy(np.ascontiguousarray(v)).cuda() for k, v in b8.items()}
+    o, lse = fa.fa_fwd_fp8(t["q"], t["k"], t["v"], t["q_descale"], t["k_descale"], t["v_descale"], causal, scale)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
+def check_head(o_gpu, l_gpu, q, k, v, causal, scale, rows=None, what=""):
+    ro, rl, bd = head_bound(q, k, v, causal, scale, rows)
+    err = np.abs(o_gpu - ro)
+    ratio = err / bd
+    worst = np.unravel_index(int(ratio.argmax()), ratio.shape)
+    assert np.all(np.isfinite(o_gpu)), f"{what}: non-finite output"
+    announce(f"{what}: max error / bound = {ratio.max():.3f}")
+    assert ratio.max() <= 1.0, (f"{what}: error {err[worst]:.3e} exceeds its bound {bd[worst]:.3e} at {worst} "
+                                f"(max ratio {ratio.max():.3f})")
+    lerr = np.abs(l_gpu - rl).max()
+    assert lerr <= LSE_TOL, f"{what}: logsumexp max-abs {lerr:.3e}"
+    return ratio.max()
+
+
+def deq(b8, name):
+    return oracle.dequantize_fp8(b8[name], b8[name + "_descale"])
+
+
+SMALL = [(1, 1, 1), (1, 17, 2), (2, 64, 2), (1, 129, 3), (1, 200, 2), (2, 333, 1), (1, 1000, 1)]
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "B%dN%dH%d" % s)
+def test_fp8_small(shape, causal):
+    B, N, H = shape
+    d = 128
+    seed = 10100 + N + int(causal)
+    scale = 1.0 / math.sqrt(d)
+    announce(f"fp8 fwd shape={(B, N, H, d)} causal={causal} seed={seed}")
+    b8 = si.draw_fp8(B, N, H, d, seed)
+    o, lse = run(b8, causal, scale)
+    q, k, v = deq(b8, "q"), deq(b8, "k"), deq(b8, "v")
+    ro, rl = oracle.attention_forward_fp8(b8["q"], b8["k"], b8["v"], b8["q_descale"], b8["k_descale"],
+                                          b8["v_descale"], causal, scale)
+    for bb in range(B):
+        for h in range(H):
+            check_head(o[bb, :, h], lse[bb, h], q[bb, :, h], k[bb, :, h], v[bb, :, h], causal, scale,
+                       what=f"b{bb} h{h}")
+            # the bound's reference rows are the oracle's
+            assert np.allclose(head_bound(q[bb, :, h], k[bb, :, h], v[bb, :, h], causal, scale)[0],
+                               ro[bb, :, h], rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("qd_sign", [1.0, -1.0], ids=["pos", "neg"])
+def test_fp8_descales(qd_sign):
+    """Descales far from 1 and a negative Q descale (negates the scores)."""
+    B, N, H, d = 1, 300, 2, 128
+    announce(f"fp8 descales sign={qd_sign}")
+    b8 = si.draw_fp8(B, N, H, d, 10200)
+    b8["q_descale"] = (b8["q_descale"] * np.float32(qd_sign) * np.float32(8.0)).astype(np.float32)
+    b8["k_descale"] = (b8["k_descale"] / np.float32(4.0)).astype(np.float32)
+    b8["v_descale"] = (b8["v_descale"] * np.float32(1000.0)).astype(np.float32)
+    o, lse = run(b8, True, 0.09)
+    q, k, v = deq(b8, "q"), deq(b8, "k"), deq(b8, "v")
+    for h in range(H):
+        check_head(o[0, :, h], lse[0, h], q[0, :, h], k[0, :, h], v[0, :, h], True, 0.09, what=f"h{h}")
+
+
+@pytest.mark.parametrize("name", list(si.FP8_WORKLOADS))
+def test_fp8_workload(name):
+    """The FP8 workloads at full size, as the benchmark runs them: sampled
+    heads (training shape) or sampled rows (long sequence) against the bound."""
+    w = si.FP8_WORKLOADS[name]
+    announce(f"fp8 workload {name}: B={w.B} H={w.H} N={w.N} d={w.d}")
+    b8 = si.draw_fp8(w.B, w.N, w.H, w.d, w.seed)
+    o, lse = run(b8, w.causal, w.scale)
+    q, k, v = deq(b8, "q"), deq(b8, "k"), deq(b8, "v")
+    rng = np.random.Generator(np.random.PCG64(10300))
+    rows = None if w.N <= 4096 else np.unique(np.concatenate([[0, 1, w.N - 1], rng.choice(w.N, 40, replace=False)]))
+    for bb, h in ((0, 0), (w.B - 1, w.H - 1), (w.B // 2, 7)):
+        og = o[bb, :, h] if rows is None else o[bb, rows, h]
+        lg = lse[bb, h] if rows is None else lse[bb, h, rows]
+        check_head(og, lg, q[bb, :, h], k[bb, :, h], v[bb, :, h], w.causal, w.scale, rows, what=f"b{bb} h{h}")
