@@ -121,9 +121,9 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   const int lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31, G = lane >> 4;
 
-  const int logical = xcd_remap(blockIdx.x, total_blocks);
-  const int head = logical / nkb;
-  const int kblk = logical - head * nkb;  // block 0 has the most causal work: it goes first
+  const HeadRank hr = block_order<CAUSAL>(blockIdx.x, total_blocks / nkb, nkb);
+  const int head = hr.head;
+  const int kblk = hr.rank;  // block 0 has the most causal work: it goes first
   const int b = head / H, h = head - b * H;
   const long hoff = ((long)b * N * H + h) * D;
   const uint32_t tokb = (uint32_t)H * D * 2;
@@ -303,9 +303,9 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   const int lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31, G = lane >> 4;
 
-  const int logical = xcd_remap(blockIdx.x, total_blocks);
-  const int head = logical / nqb;
-  const int qblk = nqb - 1 - (logical - head * nqb);  // longest causal rows first
+  const HeadRank hr = block_order<CAUSAL>(blockIdx.x, total_blocks / nqb, nqb);
+  const int head = hr.head;
+  const int qblk = nqb - 1 - hr.rank;  // longest causal rows first
   const int b = head / H, h = head - b * H;
   const long hoff = ((long)b * N * H + h) * D;
   const uint32_t tokb = (uint32_t)H * D * 2;

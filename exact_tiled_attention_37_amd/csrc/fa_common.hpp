@@ -223,15 +223,41 @@ __device__ __forceinline__ void wait_vmem_leave() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
-// Blocks are dispatched round-robin over the XCDs (block i goes to XCD i % 8).
-// Remap so that each XCD receives one contiguous range of logical blocks:
-// consecutive logical blocks (the query blocks of one head) then share an L2.
-// The map is a bijection of [0, total) for any total, so correctness never
-// depends on the dispatch order.
+// Blocks are dispatched round-robin over the XCDs (block i goes to XCD i % 8)
+// and, inside an XCD, start in index order.
+//
+// xcd_remap: each XCD receives one contiguous range of logical blocks, so
+// consecutive logical blocks (the blocks of one head) share an L2. The map
+// is a bijection of [0, total) for any total, so correctness never depends
+// on the dispatch order.
 __device__ __forceinline__ int xcd_remap(int bid, int total) {
   const int per = total / kNumXcd, rem = total % kNumXcd;
   const int x = bid % kNumXcd, idx = bid / kNumXcd;
   return (x < rem) ? x * (per + 1) + idx : rem * (per + 1) + (x - rem) * per + idx;
+}
+
+// Block order of a launch over `heads` (batch, head) pairs with per_head
+// blocks each; rank 0 is the block with the most work. Causal blocks of one
+// head differ in work: block i takes head i % heads and rank i / heads, so
+// every XCD starts its heaviest blocks first across all of its heads
+// (longest-first list scheduling; the order by head left the last head's
+// heavy blocks for the end) and, when heads is a multiple of 8, all blocks
+// of a head still run on one XCD. Non-causal blocks do equal work: the
+// blocks of a head stay together (xcd_remap), so they run at the same time
+// and read their K and V through one L2.
+struct HeadRank {
+  int head, rank;
+};
+template <bool CAUSAL>
+__device__ __forceinline__ HeadRank block_order(int bid, int heads, int per_head) {
+  if constexpr (CAUSAL) {
+    const int r = bid / heads;
+    return {bid - r * heads, r};
+  } else {
+    const int l = xcd_remap(bid, heads * per_head);
+    const int h = l / per_head;
+    return {h, l - h * per_head};
+  }
 }
 
 }  // namespace fa

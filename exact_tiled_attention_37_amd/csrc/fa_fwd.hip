@@ -106,12 +106,10 @@ __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD))) v
   const int lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31, G = lane >> 4;
 
-  const int logical = xcd_remap(blockIdx.x, total_blocks);
-  const int per_head = nqb * nsplit;
-  const int head = logical / per_head;             // b * H + h
-  const int rest = logical - head * per_head;
-  const int qblk = nqb - 1 - rest / nsplit;        // longest causal rows first
-  const int split = rest - (rest / nsplit) * nsplit;
+  const HeadRank hr = block_order<CAUSAL>(blockIdx.x, total_blocks / (nqb * nsplit), nqb * nsplit);
+  const int head = hr.head;                        // b * H + h
+  const int qblk = nqb - 1 - hr.rank / nsplit;     // longest causal rows first
+  const int split = hr.rank - (hr.rank / nsplit) * nsplit;
   const int b = head / H, h = head - b * H;
   const long hq = ((long)b * Nq * H + h) * D;      // element offset of query / output token 0
   const long hk = ((long)b * Nk * H + h) * D;      // element offset of key / value token 0
