@@ -115,11 +115,17 @@ struct Tile {
   }
 };
 
+// Maxima that propagate NaN (IEEE maximum; v_maximum3_f32 on gfx950). fmaxf
+// would make the compiler quiet possible signalling NaNs in every operand
+// first (one extra v_max_f32 per MFMA result).
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float vmax3(float a, float b, float c) { return vmax(vmax(a, b), c); }
+
 // Combine a value with the same value of lane l ^ 32 (v_permlane32_swap).
 __device__ __forceinline__ float xhalf_max(float x) {
   uint32_t u = __float_as_uint(x);
   auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float xhalf_sum(float x) {
   uint32_t u = __float_as_uint(x);
@@ -132,13 +138,16 @@ __device__ __forceinline__ bf16x4 to_bf16x4(f32x4 x) { return __builtin_convertv
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Reductions over the values of an MFMA accumulator as a few independent
-// chains (short dependency depth); each chain of three-input maxima becomes
-// v_max3 instructions.
+// Reductions over the values of an MFMA accumulator as two independent
+// chains (short dependency depth): 8 three-input maxima for 16 values and init.
 __device__ __forceinline__ float max16(const f32x16& v, float init) {
-  float a = fmaxf(fmaxf(fmaxf(fmaxf(fmaxf(fmaxf(fmaxf(v[0], v[1]), v[2]), v[3]), v[4]), v[5]), v[6]), v[7]);
-  float b = fmaxf(fmaxf(fmaxf(fmaxf(fmaxf(fmaxf(fmaxf(v[8], v[9]), v[10]), v[11]), v[12]), v[13]), v[14]), v[15]);
-  return fmaxf(fmaxf(a, b), init);
+  float a = vmax3(v[0], v[1], v[2]);
+  float b = vmax3(v[8], v[9], v[10]);
+  a = vmax3(a, v[3], v[4]);
+  b = vmax3(b, v[11], v[12]);
+  a = vmax3(a, v[5], v[6]);
+  b = vmax3(b, v[13], v[14]);
+  return vmax3(vmax3(a, v[7], v[15]), b, init);
 }
 __device__ __forceinline__ float sum8(const f32x8& v) {
   return ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));

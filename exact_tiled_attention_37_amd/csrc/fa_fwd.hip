@@ -139,9 +139,10 @@ __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD))) v
 
   // LDS-DMA: wave load u = wave + NW t of a tile; lane i fills the chunk
   // (row, column) the layout assigns to it. A tile row is a key.
-  auto issue = [&](int tile, char* dst) __attribute__((always_inline)) {
+  auto issue = [&](int tile, char* dst, int t0 = 0, int t1 = 1 << 20) __attribute__((always_inline)) {
 #pragma unroll
     for (int t = 0; t < DMA_PER_WAVE; ++t) {
+      if (t < t0 || t >= t1) continue;
       const int u = wave + NW * t;
       if (T::LOADS < NW && u >= T::LOADS) break;  // fewer loads than waves: the rest issue none
       const uint32_t off = row_off(tile * kFwdBC + T::dma_row(u, lane), Nk, tokb, 16u * T::dma_chunk(u, lane));
@@ -169,7 +170,7 @@ __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD))) v
   // One K/V tile. MASK selects the variant for tiles that straddle the
   // causal diagonal or the end of the sequence; all other tiles run the
   // variant without any per-element masking.
-  auto compute = [&](int j, const char* kt, auto mask_tag) __attribute__((always_inline)) {
+  auto compute = [&](int j, const char* kt, auto mask_tag, auto&& mid) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
     const int key0 = j * kFwdBC;
     const char* vt = kt + TILE;
@@ -190,6 +191,7 @@ __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD))) v
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) s[kb] = mfma32(T::row8(kt, kb * 32 + l32, 2 * ks + g), qf[ks], s[kb]);
+    mid();  // the rest of the next tile's loads (after this tile's S product)
     // With a bias the scores become log2-domain values here, c2 * s + bias * log2(e).
     if constexpr (BIAS) {
 #pragma unroll
@@ -288,10 +290,18 @@ __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD))) v
   const int jm_all = CAUSAL ? min(max(0, qblk * kFwdBR + delta + 1) / kFwdBC, Nk / kFwdBC) : Nk / kFwdBC;
   const int jm = min(max(jm_all, j0), j1);
   int j = j0;
+  // In the unmasked causal loop half of a wave's loads of the next tile are
+  // issued before this tile's S product and half after it, so the LDS
+  // writes of the workgroup's loads do not arrive in one burst (long causal
+  // loops have the latency to spare; short non-causal ones do not).
+  constexpr int SPLIT = CAUSAL ? DMA_PER_WAVE / 2 : DMA_PER_WAVE;
   for (; j < jm; ++j) {
     const int t = j - j0;
-    if (t + STAGES - 1 < ntiles) issue(j + STAGES - 1, stage(t + STAGES - 1));
-    compute(j, stage(t), std::false_type{});
+    const bool more = t + STAGES - 1 < ntiles;
+    if (more) issue(j + STAGES - 1, stage(t + STAGES - 1), 0, SPLIT);
+    compute(j, stage(t), std::false_type{}, [&]() __attribute__((always_inline)) {
+      if (SPLIT < DMA_PER_WAVE && more) issue(j + STAGES - 1, stage(t + STAGES - 1), SPLIT, DMA_PER_WAVE);
+    });
     wait_next(t);
     __syncthreads();
   }
@@ -300,7 +310,7 @@ __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD))) v
     if (t + STAGES - 1 < ntiles) issue(j + STAGES - 1, stage(t + STAGES - 1));
     // A tile whose first key lies past this wave's last row is fully masked
     // for it and contributes nothing.
-    if (!CAUSAL || j * kFwdBC <= qw0 + 31 + delta) compute(j, stage(t), std::true_type{});
+    if (!CAUSAL || j * kFwdBC <= qw0 + 31 + delta) compute(j, stage(t), std::true_type{}, []() {});
     wait_next(t);
     __syncthreads();
   }
