@@ -246,27 +246,30 @@ __device__ __forceinline__ int xcd_remap(int bid, int total) {
 }
 
 // Block order of a launch over `heads` (batch, head) pairs with per_head
-// blocks each; rank 0 is the block with the most work. Causal blocks of one
-// head differ in work: block i takes head i % heads and rank i / heads, so
-// every XCD starts its heaviest blocks first across all of its heads
-// (longest-first list scheduling; the order by head left the last head's
-// heavy blocks for the end) and, when heads is a multiple of 8, all blocks
-// of a head still run on one XCD. Non-causal blocks do equal work: the
-// blocks of a head stay together (xcd_remap), so they run at the same time
-// and read their K and V through one L2.
+// blocks each; rank 0 is the block with the most work. The logical order
+// (xcd_remap: one contiguous range per XCD) takes the heads in groups of G;
+// inside a group the blocks go rank-major (heaviest rank of every head of
+// the group first). Causal blocks of one head differ in work: with G chosen
+// so that a group holds at least as many blocks as an XCD runs at once
+// (`slots`), every XCD runs longest-first within the group (the head-by-head
+// order left a head's heavy blocks behind the previous head's light ones),
+// while only about G heads share the XCD's L2 at a time. Non-causal blocks
+// do equal work: G = 1, the blocks of a head run together and read their K
+// and V through one L2.
 struct HeadRank {
   int head, rank;
 };
+constexpr int kCusPerXcd = 32;  // MI355X: 256 CUs in 8 XCDs
 template <bool CAUSAL>
-__device__ __forceinline__ HeadRank block_order(int bid, int heads, int per_head) {
-  if constexpr (CAUSAL) {
-    const int r = bid / heads;
-    return {bid - r * heads, r};
-  } else {
-    const int l = xcd_remap(bid, heads * per_head);
-    const int h = l / per_head;
-    return {h, l - h * per_head};
-  }
+__device__ __forceinline__ HeadRank block_order(int bid, int heads, int per_head, int slots) {
+  const int l = xcd_remap(bid, heads * per_head);
+  const int G = CAUSAL ? min(heads, max(1, (slots + per_head - 1) / per_head)) : 1;
+  const int gsize = G * per_head;
+  const int g = l / gsize;
+  const int within = l - g * gsize;
+  const int gh = min(G, heads - g * G);  // heads in this group (the last may be smaller)
+  const int r = within / gh;
+  return {g * G + (within - r * gh), r};
 }
 
 }  // namespace fa

@@ -106,7 +106,8 @@ __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD))) v
   const int lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31, G = lane >> 4;
 
-  const HeadRank hr = block_order<CAUSAL>(blockIdx.x, total_blocks / (nqb * nsplit), nqb * nsplit);
+  const HeadRank hr = block_order<CAUSAL>(blockIdx.x, total_blocks / (nqb * nsplit), nqb * nsplit,
+                                          kCusPerXcd * Cfg::WAVES_PER_SIMD);
   const int head = hr.head;                        // b * H + h
   const int qblk = nqb - 1 - hr.rank / nsplit;     // longest causal rows first
   const int split = hr.rank - (hr.rank / nsplit) * nsplit;
