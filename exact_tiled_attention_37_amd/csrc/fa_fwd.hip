@@ -171,19 +171,23 @@ __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD))) v
   // One K/V tile. MASK selects the variant for tiles that straddle the
   // causal diagonal or the end of the sequence; all other tiles run the
   // variant without any per-element masking.
-  auto compute = [&](int j, const char* kt, auto mask_tag, auto&& mid) __attribute__((always_inline)) {
+  // This lane's bias terms of one tile: for each 32-key block, 4 groups of 4
+  // consecutive keys (the keys of its accumulator rows), 8 bytes each. They
+  // are loaded two tiles ahead (bias_load) and consumed by compute().
+  struct BiasTile {
+    u32x2 v[BIAS ? KB : 1][4];
+  };
+  auto bias_load = [&](int j, BiasTile& bt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) bt.v[kb][rg] = buf_load8(rb, boff, (uint32_t)(j * kFwdBC + kb * 32 + 8 * rg) * 2u);
+  };
+  auto compute = [&](int j, const char* kt, auto mask_tag, auto&& mid, const BiasTile& bt) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
     const int key0 = j * kFwdBC;
     const char* vt = kt + TILE;
-    // This lane's bias terms: for each 32-key block, 4 groups of 4
-    // consecutive keys (the keys of its accumulator rows), 8 bytes each.
-    u32x2 bw[BIAS ? KB : 1][4];
-    if constexpr (BIAS) {
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int rg = 0; rg < 4; ++rg) bw[kb][rg] = buf_load8(rb, boff, (uint32_t)(key0 + kb * 32 + 8 * rg) * 2u);
-    }
+    const auto& bw = bt.v;
     // The KB accumulation chains are interleaved (independent MFMAs back to back).
     f32x16 s[KB];
 #pragma unroll
@@ -295,25 +299,65 @@ __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD))) v
   // issued before this tile's S product and half after it, so the LDS
   // writes of the workgroup's loads do not arrive in one burst (long causal
   // loops have the latency to spare; short non-causal ones do not).
-  constexpr int SPLIT = CAUSAL ? DMA_PER_WAVE / 2 : DMA_PER_WAVE;
+  // With a bias: tile j's bias was loaded two iterations earlier. Iteration j
+  // issues the K/V loads of tile j + 1 and then the bias loads of tile
+  // j + 2, and at its end waits for all but those bias loads (they complete
+  // in issue order). The compiler's own wait before the bias is used counts
+  // only the bias loads issued after it, which is stricter, never weaker.
+  constexpr int SPLIT = (CAUSAL && !BIAS) ? DMA_PER_WAVE / 2 : DMA_PER_WAVE;
+  constexpr int BIAS_LOADS = KB * 4;
+  static_assert(!BIAS || STAGES == 2, "bias prefetch assumes a two-stage K/V ring");
+  BiasTile b_cur{}, b_next{};
+  if constexpr (BIAS) {
+    if (j0 < j1) bias_load(j0, b_cur);
+    if (j0 + 1 < j1) bias_load(j0 + 1, b_next);
+    wait_vmem();
+  }
+  auto bias_step = [&](int j) __attribute__((always_inline)) {
+    BiasTile b_new{};
+    const bool ahead = BIAS && j + 2 < j1;
+    if constexpr (BIAS) {
+      if (ahead) bias_load(j + 2, b_new);
+    }
+    return b_new;
+  };
+  auto end_wait = [&](int t, int j) __attribute__((always_inline)) {
+    if constexpr (BIAS) {
+      if (j + 2 < j1) {
+        wait_vmem_leave<BIAS_LOADS>();
+        return;
+      }
+    }
+    wait_next(t);
+  };
   for (; j < jm; ++j) {
     const int t = j - j0;
     const bool more = t + STAGES - 1 < ntiles;
     if (more) issue(j + STAGES - 1, stage(t + STAGES - 1), 0, SPLIT);
+    BiasTile b_new = bias_step(j);
     compute(j, stage(t), std::false_type{}, [&]() __attribute__((always_inline)) {
       if (SPLIT < DMA_PER_WAVE && more) issue(j + STAGES - 1, stage(t + STAGES - 1), SPLIT, DMA_PER_WAVE);
-    });
-    wait_next(t);
+    }, b_cur);
+    end_wait(t, j);
     __syncthreads();
+    if constexpr (BIAS) {
+      b_cur = b_next;
+      b_next = b_new;
+    }
   }
   for (; j < j1; ++j) {
     const int t = j - j0;
     if (t + STAGES - 1 < ntiles) issue(j + STAGES - 1, stage(t + STAGES - 1));
+    BiasTile b_new = bias_step(j);
     // A tile whose first key lies past this wave's last row is fully masked
     // for it and contributes nothing.
-    if (!CAUSAL || j * kFwdBC <= qw0 + 31 + delta) compute(j, stage(t), std::true_type{}, []() {});
-    wait_next(t);
+    if (!CAUSAL || j * kFwdBC <= qw0 + 31 + delta) compute(j, stage(t), std::true_type{}, []() {}, b_cur);
+    end_wait(t, j);
     __syncthreads();
+    if constexpr (BIAS) {
+      b_cur = b_next;
+      b_next = b_new;
+    }
   }
 
   // A row that saw no key (possible only with a causal offset that puts every
