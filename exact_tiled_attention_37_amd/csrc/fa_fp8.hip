@@ -131,6 +131,7 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(3, 3
   float m_run = -INFINITY;
   float l_run = 0.f;
 
+  i32x8 pf = {};  // P^T operand of the current tile (kept across tiles)
   auto compute = [&](int j, const char* kt, auto mask_tag) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
     const int key0 = j * kF8BC;
@@ -169,7 +170,6 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(3, 3
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
     const float bias = kF8Shift - m_use;
     // P^T operand: byte p = 2^4 * exp2(s - m) of accumulator p % 16 of block p / 16.
-    i32x8 pf;
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
       float e[4];
@@ -181,7 +181,9 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(3, 3
         e[i] = x;
       }
       l_run += (e[0] + e[1]) + (e[2] + e[3]);
-      int d = __builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], 0, false);
+      // The two conversions write the low and the high half of the word; the
+      // other half starts as the previous tile's value (no zeroing move).
+      int d = __builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], pf[w], false);
       pf[w] = __builtin_amdgcn_cvt_pk_fp8_f32(e[2], e[3], d, true);
     }
     // O^T += V^T P^T: for each 32-column block of d, four transpose loads.
