@@ -101,6 +101,8 @@ __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD))) v
   constexpr int KS = D / 16;                       // MFMA k-steps over d
   constexpr int DB = D / 32;                       // 32-wide output column blocks
   __shared__ __attribute__((aligned(1024))) char ring[STAGES * 2 * TILE];  // per stage: K tile, V tile
+  // Bias of the next tile for each wave's 32 rows (see bias_fetch below).
+  __shared__ __attribute__((aligned(BIAS ? 1024 : 16))) char bias_lds[BIAS ? NW * 32 * kFwdBC * 2 : 16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -128,7 +130,6 @@ __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD))) v
   // rows at or past Nq read as zeros.
   const auto rb = make_rsrc(BIAS ? Bias + b * bias_sb + h * bias_sh : Q,
                             BIAS ? (uint32_t)((long)Nq * bias_srow * 2) : 0u);
-  const uint32_t boff = BIAS ? ((uint32_t)min(myq, Nq) * (uint32_t)bias_srow + 4u * g) * 2u : 0u;
 
   // Q as the B operand of S^T = K Q^T: row myq, d = 16*ks + 8*g .. +7.
   bf16x8 qf[KS];
@@ -171,23 +172,54 @@ __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD))) v
   // One K/V tile. MASK selects the variant for tiles that straddle the
   // causal diagonal or the end of the sequence; all other tiles run the
   // variant without any per-element masking.
-  // This lane's bias terms of one tile: for each 32-key block, 4 groups of 4
-  // consecutive keys (the keys of its accumulator rows), 8 bytes each. They
-  // are loaded two tiles ahead (bias_load) and consumed by compute().
-  struct BiasTile {
-    u32x2 v[BIAS ? KB : 1][4];
-  };
-  auto bias_load = [&](int j, BiasTile& bt) __attribute__((always_inline)) {
+  // Bias of a tile for the wave's 32 rows (32 x kFwdBC bf16): fetched with
+  // 16-byte loads that cover whole rows (each load instruction reads
+  // 64 / CH full rows) into registers, written to the wave's own LDS slice
+  // (row r, 16-byte chunk c at slot c ^ (r % CH)), and read back in the
+  // accumulator layout: per 32-key block, 4 groups of 4 consecutive keys
+  // (the keys of the lane's accumulator rows), 8 bytes each. A lane of the
+  // accumulator layout holds one query row, so reading the bias in that
+  // layout straight from memory touches 32 rows per load instruction.
+  constexpr int CH = kFwdBC / 8;        // 16-byte chunks per bias row of a tile
+  constexpr int RB = kFwdBC * 2;        // bytes per bias row of a tile
+  constexpr int BL = 32 * CH / 64;      // 16-byte loads per lane and tile
+  char* const bw_lds = bias_lds + wave * 32 * RB;
+  uint32_t bgo[BIAS ? BL : 1];          // per-lane global byte offsets at key 0
+  if constexpr (BIAS) {
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
+    for (int t = 0; t < BL; ++t) {
+      const int row = t * (64 / CH) + lane / CH, chunk = lane % CH;
+      bgo[t] = ((uint32_t)min(qw0 + row, Nq) * (uint32_t)bias_srow + 8u * chunk) * 2u;
+    }
+  }
+  u32x4 bst[BIAS ? BL : 1];
+  auto bias_fetch = [&](int j) __attribute__((always_inline)) {
 #pragma unroll
-      for (int rg = 0; rg < 4; ++rg) bt.v[kb][rg] = buf_load8(rb, boff, (uint32_t)(j * kFwdBC + kb * 32 + 8 * rg) * 2u);
+    for (int t = 0; t < BL; ++t)
+      bst[t] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, (int)bgo[t], j * RB, 0));
   };
-  auto compute = [&](int j, const char* kt, auto mask_tag, auto&& mid, const BiasTile& bt) __attribute__((always_inline)) {
+  auto bias_store = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < BL; ++t) {
+      const int row = t * (64 / CH) + lane / CH, chunk = lane % CH;
+      lds_write16(bw_lds, row * RB + ((chunk ^ (row % CH)) << 4), bst[t]);
+    }
+  };
+  auto compute = [&](int j, const char* kt, auto mask_tag, auto&& mid) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
     const int key0 = j * kFwdBC;
     const char* vt = kt + TILE;
-    const auto& bw = bt.v;
+    u32x2 bw[BIAS ? KB : 1][4];
+    if constexpr (BIAS) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          const int c = kb * 4 + rg;
+          bw[kb][rg] = *reinterpret_cast<const FA_LDS u32x2*>(
+              (const FA_LDS char*)bw_lds + l32 * RB + ((c ^ (l32 % CH)) << 4) + 8 * g);
+        }
+    }
     // The KB accumulation chains are interleaved (independent MFMAs back to back).
     f32x16 s[KB];
 #pragma unroll
@@ -287,7 +319,9 @@ __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD))) v
 #pragma unroll
   for (int t = 0; t < STAGES - 1; ++t)
     if (t < ntiles) issue(j0 + t, stage(t));
+  if (BIAS && j0 < j1) bias_fetch(j0);
   wait_next(-1);
+  if (BIAS && j0 < j1) bias_store();
   __syncthreads();
   // Tiles before jm need no mask for any wave of this workgroup; they run in
   // a loop of their own so that the masked variant never joins the hot loop.
@@ -299,65 +333,32 @@ __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD))) v
   // issued before this tile's S product and half after it, so the LDS
   // writes of the workgroup's loads do not arrive in one burst (long causal
   // loops have the latency to spare; short non-causal ones do not).
-  // With a bias: tile j's bias was loaded two iterations earlier. Iteration j
-  // issues the K/V loads of tile j + 1 and then the bias loads of tile
-  // j + 2, and at its end waits for all but those bias loads (they complete
-  // in issue order). The compiler's own wait before the bias is used counts
-  // only the bias loads issued after it, which is stricter, never weaker.
-  constexpr int SPLIT = (CAUSAL && !BIAS) ? DMA_PER_WAVE / 2 : DMA_PER_WAVE;
-  constexpr int BIAS_LOADS = KB * 4;
-  static_assert(!BIAS || STAGES == 2, "bias prefetch assumes a two-stage K/V ring");
-  BiasTile b_cur{}, b_next{};
-  if constexpr (BIAS) {
-    if (j0 < j1) bias_load(j0, b_cur);
-    if (j0 + 1 < j1) bias_load(j0 + 1, b_next);
-    wait_vmem();
-  }
-  auto bias_step = [&](int j) __attribute__((always_inline)) {
-    BiasTile b_new{};
-    const bool ahead = BIAS && j + 2 < j1;
-    if constexpr (BIAS) {
-      if (ahead) bias_load(j + 2, b_new);
-    }
-    return b_new;
-  };
-  auto end_wait = [&](int t, int j) __attribute__((always_inline)) {
-    if constexpr (BIAS) {
-      if (j + 2 < j1) {
-        wait_vmem_leave<BIAS_LOADS>();
-        return;
-      }
-    }
-    wait_next(t);
-  };
+  // With a bias, iteration j also fetches the bias of tile j + 1 into
+  // registers and writes it to the wave's LDS slice after this tile's
+  // compute has read tile j's (a wave's LDS operations run in order).
+  constexpr int SPLIT = CAUSAL ? DMA_PER_WAVE / 2 : DMA_PER_WAVE;
   for (; j < jm; ++j) {
     const int t = j - j0;
     const bool more = t + STAGES - 1 < ntiles;
     if (more) issue(j + STAGES - 1, stage(t + STAGES - 1), 0, SPLIT);
-    BiasTile b_new = bias_step(j);
+    if (BIAS && j + 1 < j1) bias_fetch(j + 1);
     compute(j, stage(t), std::false_type{}, [&]() __attribute__((always_inline)) {
       if (SPLIT < DMA_PER_WAVE && more) issue(j + STAGES - 1, stage(t + STAGES - 1), SPLIT, DMA_PER_WAVE);
-    }, b_cur);
-    end_wait(t, j);
+    });
+    wait_next(t);
+    if (BIAS && j + 1 < j1) bias_store();
     __syncthreads();
-    if constexpr (BIAS) {
-      b_cur = b_next;
-      b_next = b_new;
-    }
   }
   for (; j < j1; ++j) {
     const int t = j - j0;
     if (t + STAGES - 1 < ntiles) issue(j + STAGES - 1, stage(t + STAGES - 1));
-    BiasTile b_new = bias_step(j);
+    if (BIAS && j + 1 < j1) bias_fetch(j + 1);
     // A tile whose first key lies past this wave's last row is fully masked
     // for it and contributes nothing.
-    if (!CAUSAL || j * kFwdBC <= qw0 + 31 + delta) compute(j, stage(t), std::true_type{}, []() {}, b_cur);
-    end_wait(t, j);
+    if (!CAUSAL || j * kFwdBC <= qw0 + 31 + delta) compute(j, stage(t), std::true_type{}, []() {});
+    wait_next(t);
+    if (BIAS && j + 1 < j1) bias_store();
     __syncthreads();
-    if constexpr (BIAS) {
-      b_cur = b_next;
-      b_next = b_new;
-    }
   }
 
   // A row that saw no key (possible only with a causal offset that puts every
