@@ -221,6 +221,26 @@ __device__ __forceinline__ void dma4(const u32x4& r, const void* lds, uint32_t o
   asm volatile("buffer_load_dword %0, %1, 0 offen lds" ::"v"(off), "s"(r), "{m0}"(lds_base(lds)) : "memory");
 }
 
+// The same resource advanced by `off` bytes (wave-uniform): the base moves
+// up and the record count shrinks by `off`, so a per-lane offset relative to
+// the new base is range-checked against the same end. The values stay in
+// scalar registers, which keeps per-tile address arithmetic off the VALU.
+__device__ __forceinline__ u32x4 rsrc_advance(const u32x4& r, uint32_t off) {
+  const uint64_t base = (((uint64_t)r[1] << 32) | r[0]) + off;
+  u32x4 o;
+  o[0] = __builtin_amdgcn_readfirstlane((uint32_t)base);
+  o[1] = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
+  o[2] = __builtin_amdgcn_readfirstlane(r[2] - off);
+  o[3] = r[3];
+  return o;
+}
+// dma16 with the LDS destination given as an LDS byte address (uniform).
+__device__ __forceinline__ void dma16_at(const u32x4& r, uint32_t lds_addr, uint32_t off) {
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(r),
+               "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr))
+               : "memory");
+}
+
 // s_waitcnt vmcnt(0): all of this wave's vector memory loads (including the
 // ones that write LDS directly) have completed.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }

@@ -105,7 +105,7 @@ __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD))) v
   __shared__ __attribute__((aligned(BIAS ? 1024 : 16))) char bias_lds[BIAS ? NW * 32 * kFwdBC * 2 : 16];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar registers
   const int g = lane >> 5, l32 = lane & 31, G = lane >> 4;
 
   const HeadRank hr = block_order<CAUSAL>(blockIdx.x, total_blocks / (nqb * nsplit), nqb * nsplit,
@@ -140,17 +140,27 @@ __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD))) v
   }
 
   // LDS-DMA: wave load u = wave + NW t of a tile; lane i fills the chunk
-  // (row, column) the layout assigns to it. A tile row is a key.
+  // (row, column) the layout assigns to it. A tile row is a key. The lane's
+  // byte offset inside a tile is fixed; the tile's position goes into the
+  // (scalar) resource, whose end still turns rows past Nk into zeros.
+  uint32_t dma_off[DMA_PER_WAVE];
+#pragma unroll
+  for (int t = 0; t < DMA_PER_WAVE; ++t) {
+    const int u = min(wave + NW * t, T::LOADS - 1);
+    dma_off[t] = (uint32_t)T::dma_row(u, lane) * tokb + 16u * T::dma_chunk(u, lane);
+  }
+  const uint32_t ring_lds = lds_base(ring);
   auto issue = [&](int tile, char* dst, int t0 = 0, int t1 = 1 << 20) __attribute__((always_inline)) {
+    const uint32_t toff = (uint32_t)(tile * kFwdBC) * tokb;
+    const u32x4 rkt = rsrc_advance(rk, toff), rvt = rsrc_advance(rv, toff);
+    const uint32_t l0 = ring_lds + (uint32_t)(dst - ring);
 #pragma unroll
     for (int t = 0; t < DMA_PER_WAVE; ++t) {
       if (t < t0 || t >= t1) continue;
       const int u = wave + NW * t;
       if (T::LOADS < NW && u >= T::LOADS) break;  // fewer loads than waves: the rest issue none
-      const uint32_t off = row_off(tile * kFwdBC + T::dma_row(u, lane), Nk, tokb, 16u * T::dma_chunk(u, lane));
-      char* l = dst + T::dma_dst(u);
-      dma16(rk, l, off);
-      dma16(rv, l + TILE, off);
+      dma16_at(rkt, l0 + T::dma_dst(u), dma_off[t]);
+      dma16_at(rvt, l0 + T::dma_dst(u) + TILE, dma_off[t]);
     }
   };
 
