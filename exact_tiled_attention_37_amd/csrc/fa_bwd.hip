@@ -118,7 +118,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   __shared__ __attribute__((aligned(1024))) char vblk[TV::BYTES];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar registers
   const int g = lane >> 5, l32 = lane & 31, G = lane >> 4;
 
   const HeadRank hr = block_order<CAUSAL>(blockIdx.x, total_blocks / nkb, nkb, 2 * kCusPerXcd);
@@ -158,20 +158,30 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
     }
   }
 
+  // A lane's byte offset inside a Q/dO step is a fixed lane part plus a
+  // uniform per-load part; the step's position
+  // goes into the (scalar) resources, whose ends still turn rows past N into
+  // zeros.
+  const uint32_t lane_off = TQ::dma_lane_off(lane, tokb);
+  const uint32_t qbuf_lds = lds_base(&qbuf[0][0]);
+  const uint32_t rows_lds = lds_base(&rowbuf[0][0]);
   auto issue = [&](int step, char* dst, float* rows) __attribute__((always_inline)) {
     const int q0 = step * kQStep;
+    const uint32_t toff = (uint32_t)q0 * tokb;
+    const u32x4 rqt = rsrc_advance(rq, toff), rdot = rsrc_advance(rdo, toff);
+    const uint32_t l0 = qbuf_lds + (uint32_t)(dst - &qbuf[0][0]);
 #pragma unroll
     for (int t = 0; t < DMA_PER_WAVE; ++t) {
       const int u = wave + 4 * t;
-      const uint32_t off = row_off(q0 + TQ::dma_row(u, lane), N, tokb, 16u * TQ::dma_chunk(u, lane));
-      char* l = dst + TQ::dma_dst(u);
-      dma16(rq, l, off);
-      dma16(rdo, l + QT, off);
+      const uint32_t off = lane_off + TQ::dma_load_off(u, tokb);
+      dma16_at(rqt, l0 + TQ::dma_dst(u), off);
+      dma16_at(rdot, l0 + TQ::dma_dst(u) + QT, off);
     }
     if (wave == 0) {  // 64 row terms per load; the 32 past this step are unused
-      const uint32_t off = (uint32_t)(q0 + lane) * 4;
-      dma4(rl, rows, off);
-      dma4(rd, rows + 64, off);
+      const u32x4 rlt = rsrc_advance(rl, (uint32_t)q0 * 4), rdt = rsrc_advance(rd, (uint32_t)q0 * 4);
+      const uint32_t r0 = rows_lds + (uint32_t)((char*)rows - (char*)&rowbuf[0][0]);
+      dma4_at(rlt, r0, (uint32_t)lane * 4);
+      dma4_at(rdt, r0 + 64 * 4, (uint32_t)lane * 4);
     }
   };
 
@@ -300,7 +310,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   __shared__ __attribute__((aligned(1024))) char kvbuf[2][2 * TILE];  // per stage: K tile, then V tile
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar registers
   const int g = lane >> 5, l32 = lane & 31, G = lane >> 4;
 
   const HeadRank hr = block_order<CAUSAL>(blockIdx.x, total_blocks / nqb, nqb, 2 * kCusPerXcd);
@@ -338,14 +348,21 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
     }
   }
 
+  // A lane's byte offset inside a tile is a fixed lane part plus a uniform
+  // per-load part; the tile's position goes into the (scalar) resources,
+  // whose ends still turn rows past N into zeros.
+  const uint32_t lane_off = T::dma_lane_off(lane, tokb);
+  const uint32_t kv_lds = lds_base(&kvbuf[0][0]);
   auto issue = [&](int tile, char* dst) __attribute__((always_inline)) {
+    const uint32_t toff = (uint32_t)(tile * kKTile) * tokb;
+    const u32x4 rkt = rsrc_advance(rk, toff), rvt = rsrc_advance(rv, toff);
+    const uint32_t l0 = kv_lds + (uint32_t)(dst - &kvbuf[0][0]);
 #pragma unroll
     for (int t = 0; t < DMA_PER_WAVE; ++t) {
       const int u = wave + 4 * t;
-      const uint32_t off = row_off(tile * kKTile + T::dma_row(u, lane), N, tokb, 16u * T::dma_chunk(u, lane));
-      char* l = dst + T::dma_dst(u);
-      dma16(rk, l, off);
-      dma16(rv, l + TILE, off);
+      const uint32_t off = lane_off + T::dma_load_off(u, tokb);
+      dma16_at(rkt, l0 + T::dma_dst(u), off);
+      dma16_at(rvt, l0 + T::dma_dst(u) + TILE, off);
     }
   };
 

@@ -95,6 +95,16 @@ struct Tile {
     return (u % NCB) * 4 + ((lane & 3) ^ ((lane >> 2) >> 2));
   }
 
+  // Byte offset in memory (rows row_bytes apart) of what lane `lane` loads
+  // for whole-wave load u, split into a part that depends only on the lane
+  // and a part that depends only on u (wave-uniform).
+  __device__ static uint32_t dma_lane_off(int lane, uint32_t row_bytes) {
+    return (uint32_t)(lane >> 2) * row_bytes + 16u * (uint32_t)((lane & 3) ^ (lane >> 4));
+  }
+  __device__ static uint32_t dma_load_off(int u, uint32_t row_bytes) {
+    return (uint32_t)(u / NCB) * 16u * row_bytes + 64u * (uint32_t)(u % NCB);
+  }
+
   // Row read: chunk c (elements 8c..8c+7) of row `row`.
   __device__ static bf16x8 row8(const char* t, int row, int c) {
     return __builtin_bit_cast(bf16x8, lds_read16(t, addr(row, c)));
@@ -237,6 +247,12 @@ __device__ __forceinline__ u32x4 rsrc_advance(const u32x4& r, uint32_t off) {
 // dma16 with the LDS destination given as an LDS byte address (uniform).
 __device__ __forceinline__ void dma16_at(const u32x4& r, uint32_t lds_addr, uint32_t off) {
   asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(r),
+               "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr))
+               : "memory");
+}
+
+__device__ __forceinline__ void dma4_at(const u32x4& r, uint32_t lds_addr, uint32_t off) {
+  asm volatile("buffer_load_dword %0, %1, 0 offen lds" ::"v"(off), "s"(r),
                "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr))
                : "memory");
 }
