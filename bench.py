@@ -101,6 +101,32 @@ def time_calls(fn, n, stream):
     return start.elapsed_time(stop) / 1e3 / n
 
 
+def cold_call_roofline(fn, wl, reps, stream):
+    """Average duration of fn() with the caches flushed before each call
+    (a 512 MiB fill between calls, outside the events), against HBM bandwidth:
+    algorithmic bytes = Q, K, V read + O written (bf16) + logsumexp (fp32)."""
+    import torch
+
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    total = 0.0
+    for i in range(reps):
+        flush.fill_(i & 0xFF)
+        start = torch.cuda.Event(enable_timing=True)
+        stop = torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        fn()
+        stop.record(stream)
+        stop.synchronize()
+        total += start.elapsed_time(stop) / 1e3
+    del flush
+    s = total / reps
+    nbytes = 4 * wl.B * wl.N * wl.H * wl.d * 2 + wl.B * wl.H * wl.N * 4
+    return {"fwd_ms": round(s * 1e3, 4), "fwd_tflops": round(fwd_flops(wl) / s / 1e12, 2),
+            "roofline": {"bound": "hbm", "achieved": round(nbytes / s / 1e9, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(nbytes / s / 1e9 / PEAK_HBM_GBS, 4),
+                         "bytes_per_launch": nbytes}}
+
+
 RING_RANKS = 8
 
 
@@ -378,6 +404,12 @@ def main():
             sweep[name] = {"B": wl.B, "H": wl.H, "N": wl.N, "d": wl.d, "causal": wl.causal,
                            "fwd_ms": round(s * 1e3, 4), "fwd_tflops": round(tf, 2),
                            "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+            if wl.d == 64 and wl.N <= 512 and wl.B * wl.H >= 256:
+                # Short sequences are bound by memory traffic (Q, K, V in, O and the
+                # logsumexp out), so they are also timed with the caches flushed:
+                # a 512 MiB buffer (more than the L2s and the 256 MiB Infinity
+                # Cache) is overwritten before each call, outside its events.
+                sweep[name]["cold_l2"] = cold_call_roofline(call, wl, reps=20, stream=stream)
             del q2, k2, v2, o2, l2
         detail["fwd_sweep"] = sweep
 
