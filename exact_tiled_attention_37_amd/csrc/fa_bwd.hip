@@ -308,10 +308,14 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   constexpr int TILE = T::BYTES;
   constexpr int DMA_PER_WAVE = T::LOADS / 4;
   __shared__ __attribute__((aligned(1024))) char kvbuf[2][2 * TILE];  // per stage: K tile, then V tile
+  // dBias staging: each wave's 32 rows x 64 keys of dS (see store_dbias).
+  constexpr int RB = kKTile * 2;  // bytes per row of a tile's dS
+  __shared__ __attribute__((aligned(1024))) char dbias_lds[BIAS ? 4 * 32 * RB : 16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar registers
   const int g = lane >> 5, l32 = lane & 31, G = lane >> 4;
+  char* const dbw_lds = dbias_lds + (BIAS ? wave * 32 * RB : 0);
 
   const HeadRank hr = block_order<CAUSAL>(blockIdx.x, total_blocks / nqb, nqb, 2 * kCusPerXcd);
   const int head = hr.head;
@@ -370,6 +374,30 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
   for (int i = 0; i < DB; ++i) dqacc[i] = f32x16{};
 
+  // dBias of a tile from the staging slice, by whole rows: lane i stores
+  // 16-byte chunks c = i + 64 t (row c / 8, keys 8 (c % 8) .. + 7), so each
+  // store instruction writes 8 full 128-byte row segments. Only rows and
+  // keys below N are written. (A wave's LDS operations complete in order,
+  // so these reads see this tile's writes and precede the next tile's.)
+  auto store_dbias = [&](int key0) __attribute__((always_inline)) {
+    if (!dBias) return;
+#pragma unroll
+    for (int t = 0; t < 32 * RB / 16 / 64; ++t) {
+      const int c = lane + 64 * t, row = c >> 3, chunk = c & 7;
+      const u32x4 v = lds_read16(dbw_lds, row * RB + ((chunk ^ (row & 7)) << 4));
+      const int qrow = qw0 + row, key = key0 + 8 * chunk;
+      if (qrow < N) {
+        bf16* dst = dBias + ((long)head * N + qrow) * dbias_srow + key;
+        if (key + 8 <= N) {
+          *reinterpret_cast<u32x4*>(dst) = v;
+        } else {
+          const bf16x8 v8 = __builtin_bit_cast(bf16x8, v);
+          for (int e = 0; key + e < N; ++e) dst[e] = v8[e];
+        }
+      }
+    }
+  };
+
   // One tile of 64 keys, one 32-key half at a time. MASK: causal diagonal.
   auto compute = [&](int j, const char* kt, auto mask_tag) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
@@ -410,19 +438,15 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
         dsf[hh] = to_bf16x8(x);
       }
       if constexpr (BIAS) {
-        if (dbrow && myq < N) {
+        // dS of this half into the wave's staging slice in the accumulator
+        // layout: row l32, keys 32 kb + 8 rg + 4 g .. + 3 (16-byte chunk
+        // 4 kb + rg of the row, slot chunk ^ (row % 8)).
+        if (dBias) {
 #pragma unroll
           for (int rg = 0; rg < 4; ++rg) {
-            const int key = key0 + kb * 32 + 8 * rg + 4 * g;
-            const bf16x8 v8 = dsf[rg >> 1];
-            const int o = 4 * (rg & 1);
-            if (key + 3 < N) {
-              const bf16x4 v4 = {v8[o], v8[o + 1], v8[o + 2], v8[o + 3]};
-              *reinterpret_cast<bf16x4*>(dbrow + key) = v4;
-            } else {
-              for (int e = 0; e < 4; ++e)
-                if (key + e < N) dbrow[key + e] = v8[o + e];
-            }
+            const u32x4 w = __builtin_bit_cast(u32x4, dsf[rg >> 1]);
+            const u32x2 v2 = (rg & 1) ? u32x2{w[2], w[3]} : u32x2{w[0], w[1]};
+            lds_write8(dbw_lds, l32 * RB + (((4 * kb + rg) ^ (l32 & 7)) << 4) + 8 * g, v2);
           }
         }
       }
@@ -435,6 +459,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
           dqacc[db] = mfma32(a, dsf[hh], dqacc[db]);
         }
     }
+    if constexpr (BIAS) store_dbias(key0);
   };
 
   // Causal: tiles from jm on straddle the diagonal (masked); earlier tiles
