@@ -198,15 +198,16 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
     constexpr bool MASK = decltype(mask_tag)::value;
     const int q0 = step * kQStep;
     const char* dot = qt + QT;
-    // Bias of this lane's key for its 16 accumulator rows (queries).
-    // Rows past N fall beyond the resource and read as zeros (the library
-    // keeps (N + 64) * bias_srow * 2 below 2^32).
+    // Bias of this lane's key for its 16 accumulator rows (queries). The
+    // whole offset is in the per-lane (range-checked) operand, so rows past
+    // N fall beyond the resource and read as zeros (the library keeps
+    // (N + 64) * bias_srow * 2 below 2^32).
     uint32_t bb[BIAS ? 16 : 1];
     if constexpr (BIAS) {
       const uint32_t vq = ((uint32_t)(q0 + 4 * g) * (uint32_t)bias_srow + (uint32_t)mykey) * 2u;
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        bb[r] = buf_load2(rb, vq, (uint32_t)(8 * (r >> 2) + (r & 3)) * (uint32_t)bias_srow * 2u);
+        bb[r] = buf_load2(rb, vq + (uint32_t)(8 * (r >> 2) + (r & 3)) * (uint32_t)bias_srow * 2u);
     }
     f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
@@ -329,9 +330,22 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
 
   const int qw0 = qblk * kQBlock + wave * 32;
   const int myq = qw0 + l32;
-  const auto rb = make_rsrc(BIAS ? Bias + b * bias_sb + h * bias_sh : Q,
-                            BIAS ? (uint32_t)((long)N * bias_srow * 2) : 0u);
-  const uint32_t boff = BIAS ? ((uint32_t)min(myq, N) * (uint32_t)bias_srow + 4u * g) * 2u : 0u;
+  // Bias rows of this (batch, head): N rows of bias_srow elements; a tile's
+  // 32 rows x 64 keys per wave go straight into the wave's LDS slice (four
+  // whole-wave LDS-DMA loads; lane i fills 16-byte slot 64 t + i, i.e. row
+  // s / 8 and chunk (s % 8) ^ (row % 8)). Rows at or past N are clamped to
+  // N and keys past a row's end run beyond the resource for the last row:
+  // both read as zeros, and keys at or past N are masked anyway.
+  const u32x4 rbr = make_raw_rsrc(BIAS ? Bias + b * bias_sb + h * bias_sh : Q,
+                                  BIAS ? (uint32_t)((long)N * bias_srow * 2) : 0u);
+  uint32_t bias_off[BIAS ? 4 : 1];
+  if constexpr (BIAS) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int sl = 64 * t + lane, row = sl >> 3, chunk = (sl & 7) ^ (row & 7);
+      bias_off[t] = ((uint32_t)min(qw0 + row, N) * (uint32_t)bias_srow + 8u * chunk) * 2u;
+    }
+  }
   bf16* const dbrow = (BIAS && dBias) ? dBias + ((long)head * N + myq) * dbias_srow : nullptr;
 
   // This wave's Q and dO rows as B operands of S^T = K Q^T and dP^T = V dO^T.
@@ -398,6 +412,22 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
     }
   };
 
+  // The bias of tile j into the slice, issued after the barrier that ends
+  // tile j - 1 (whose slice reads are then complete) and before the next K/V
+  // tile's loads, so that waiting for it leaves those in flight.
+  const uint32_t dbw_lds_addr = lds_base(dbw_lds);
+  bool kv_prefetched = false;
+  auto bias_issue = [&](int j) __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) dma16_at(rbr, dbw_lds_addr + 1024u * t, bias_off[t] + (uint32_t)(j * RB));
+  };
+  auto bias_wait = [&]() __attribute__((always_inline)) {
+    if (kv_prefetched)
+      wait_vmem_leave<2 * DMA_PER_WAVE>();
+    else
+      wait_vmem();
+  };
+
   // One tile of 64 keys, one 32-key half at a time. MASK: causal diagonal.
   auto compute = [&](int j, const char* kt, auto mask_tag) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
@@ -405,16 +435,19 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
     const char* vt = kt + TILE;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      u32x2 bw[BIAS ? 4 : 1];  // this lane's bias: 4 groups of 4 consecutive keys
-      if constexpr (BIAS) {
-#pragma unroll
-        for (int rg = 0; rg < 4; ++rg) bw[rg] = buf_load8(rb, boff, (uint32_t)(key0 + kb * 32 + 8 * rg) * 2u);
-      }
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         s = mfma32(T::row8(kt, kb * 32 + l32, 2 * ks + g), qf[ks], s);
         dp = mfma32(T::row8(vt, kb * 32 + l32, 2 * ks + g), dof[ks], dp);
+      }
+      u32x2 bw[BIAS ? 4 : 1];  // this lane's bias: 4 groups of 4 consecutive keys
+      if constexpr (BIAS) {
+        if (kb == 0) bias_wait();
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg)
+          bw[rg] = *reinterpret_cast<const FA_LDS u32x2*>((const FA_LDS char*)dbw_lds + l32 * RB +
+                                                           (((4 * kb + rg) ^ (l32 & 7)) << 4) + 8 * g);
       }
       bf16x8 dsf[2];
 #pragma unroll
@@ -474,13 +507,17 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   __syncthreads();
   int j = 0;
   for (; j < jm; ++j) {
-    if (j + 1 < ntiles) issue(j + 1, kvbuf[(j + 1) & 1]);
+    if constexpr (BIAS) bias_issue(j);
+    kv_prefetched = j + 1 < ntiles;
+    if (kv_prefetched) issue(j + 1, kvbuf[(j + 1) & 1]);
     compute(j, kvbuf[j & 1], std::false_type{});
     wait_vmem();
     __syncthreads();
   }
   for (; j < ntiles; ++j) {
-    if (j + 1 < ntiles) issue(j + 1, kvbuf[(j + 1) & 1]);
+    if constexpr (BIAS) bias_issue(j);
+    kv_prefetched = j + 1 < ntiles;
+    if (kv_prefetched) issue(j + 1, kvbuf[(j + 1) & 1]);
     compute(j, kvbuf[j & 1], std::integral_constant<bool, CAUSAL || BIAS>{});
     wait_vmem();
     __syncthreads();

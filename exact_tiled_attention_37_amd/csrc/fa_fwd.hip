@@ -206,7 +206,7 @@ __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD))) v
   auto bias_fetch = [&](int j) __attribute__((always_inline)) {
 #pragma unroll
     for (int t = 0; t < BL; ++t)
-      bst[t] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, (int)bgo[t], j * RB, 0));
+      bst[t] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, (int)(bgo[t] + (uint32_t)(j * RB)), 0, 0));
   };
   auto bias_store = [&]() __attribute__((always_inline)) {
 #pragma unroll
