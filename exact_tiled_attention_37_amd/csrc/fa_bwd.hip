@@ -12,8 +12,16 @@
 // No N x N matrix is stored anywhere: every tile of P and dS exists only in
 // registers.
 //
-// Three kernels on the caller's stream:
-//   1. pre-pass: per query row, D = rowsum(dO * O) and L * log2(e).
+// Two kernels on the caller's stream:
+//   1. dQ: one workgroup per (block of 128 query rows, head, batch), laid out
+//      like the forward pass; each wave owns 32 rows and keeps their Q, dO
+//      rows and the dQ accumulator in registers while K/V tiles stream
+//      through LDS. Its prologue also forms the row terms of its rows,
+//      D = rowsum(dO * O) and L * log2(e), and writes them for kernel 2.
+//      Per tile:
+//        S^T = K Q^T, dP^T = V dO^T        (lane l owns query row l % 32)
+//        P^T, dS^T elementwise             (L, D of the lane's own row)
+//        dQ^T += K^T dS^T                  (K^T by LDS transpose reads)
 //   2. dK/dV: one workgroup per (block of 128 keys, head, batch); each of the
 //      4 wavefronts owns 32 keys and keeps their K, V rows and the dK, dV
 //      accumulators in registers, while 32-row blocks of Q and dO stream
@@ -21,13 +29,6 @@
 //        S = Q K^T, dP = dO V^T            (lane l owns key l % 32)
 //        P, dS elementwise                 (L, D per row from LDS)
 //        dV^T += dO^T P, dK^T += Q^T dS    (dO^T, Q^T by LDS transpose reads)
-//   3. dQ: one workgroup per (block of 128 query rows, head, batch), laid out
-//      like the forward pass; each wave owns 32 rows and keeps their Q, dO
-//      rows and the dQ accumulator in registers while K/V tiles stream
-//      through LDS. Per tile:
-//        S^T = K Q^T, dP^T = V dO^T        (lane l owns query row l % 32)
-//        P^T, dS^T elementwise             (L, D of the lane's own row)
-//        dQ^T += K^T dS^T                  (K^T by LDS transpose reads)
 // Splitting dQ from dK/dV costs two extra products per tile pair (S and dP
 // are formed in both kernels) but needs no atomics, no fp32 dQ accumulator in
 // memory, no exchange of dS through LDS and no cross-workgroup
@@ -57,47 +58,7 @@ constexpr int kQBlock = 128;   // query rows per dQ workgroup (4 waves x 32)
 constexpr int kKTile = 64;     // keys per dQ tile
 
 // ---------------------------------------------------------------------------
-// 1. D = rowsum(dO * O) and L * log2(e), [B, H, N] each. Eight lanes per row.
-template <int D>
-__global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16* __restrict__ O,
-                                                       const bf16* __restrict__ dO,
-                                                       const float* __restrict__ LSE,
-                                                       float* __restrict__ lse2,
-                                                       float* __restrict__ dsum, int N, int H,
-                                                       long rows) {
-  constexpr int PER = D / 8;  // elements per lane
-  const long t = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  const long r = t >> 3;      // token row (b, n, h), memory order
-  const int sub = threadIdx.x & 7;
-  if (r >= rows) return;      // all 8 lanes of a row leave together
-  const long off = r * D + sub * PER;
-  float acc = 0.f;
-#pragma unroll
-  for (int c = 0; c < PER / 8; ++c) {
-    const bf16x8 o8 = *reinterpret_cast<const bf16x8*>(O + off + 8 * c);
-    const bf16x8 d8 = *reinterpret_cast<const bf16x8*>(dO + off + 8 * c);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)o8[e], (float)d8[e], acc);
-  }
-  acc += __shfl_xor(acc, 1, 8);
-  acc += __shfl_xor(acc, 2, 8);
-  acc += __shfl_xor(acc, 4, 8);
-  if (sub == 0) {
-    const long bn = r / H;
-    const int h = (int)(r - bn * H);
-    const long b = bn / N;
-    const long n = bn - b * N;
-    const long i = (b * H + h) * N + n;
-    dsum[i] = acc;
-    // A row that saw no key (possible only with a -inf bias) has L = -inf;
-    // +inf here makes every recomputed probability exp2(x - inf) exactly 0.
-    const float L = LSE[i];
-    lse2[i] = L == -INFINITY ? INFINITY : L * kLog2e;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// 2. dK, dV.
+// 2. dK, dV (after the dQ kernel, which writes the row terms it reads).
 // BIAS: the bf16 additive bias enters the recomputed probabilities; element
 // (b, h, i, j) at Bias[b * bias_sb + h * bias_sh + i * bias_srow + j].
 template <int D, bool CAUSAL, bool BIAS = false>
@@ -291,7 +252,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
 }
 
 // ---------------------------------------------------------------------------
-// 3. dQ.
+// 1. dQ (and the row terms D, L * log2e of every query row).
 // BIAS: as in the dK/dV kernel; in addition, when dBias is given, this kernel
 // writes dBias = dS (bf16) at dBias[((b * H + h) * N + i) * dbias_srow + j]
 // for every query row i < N and key j < N: the tiles it visits write their
@@ -299,7 +260,8 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
 template <int D, bool CAUSAL, bool BIAS = false>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    const bf16* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ dsum,
+    const bf16* __restrict__ dO, const bf16* __restrict__ O, const float* __restrict__ LSE,
+    float* __restrict__ lse2, float* __restrict__ dsum,
     bf16* __restrict__ dQ, int N, int H, int nqb, int total_blocks, float c2, uint32_t q_sign,
     float dq_scale, const bf16* __restrict__ Bias = nullptr, long bias_sb = 0, long bias_sh = 0,
     int bias_srow = 0, bf16* __restrict__ dBias = nullptr, int dbias_srow = 0) {
@@ -348,21 +310,39 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   }
   bf16* const dbrow = (BIAS && dBias) ? dBias + ((long)head * N + myq) * dbias_srow : nullptr;
 
-  // This wave's Q and dO rows as B operands of S^T = K Q^T and dP^T = V dO^T.
+  // This wave's Q and dO rows as B operands of S^T = K Q^T and dP^T = V dO^T,
+  // and the row terms of its rows: D = rowsum(dO * O) (fp32 accumulation of
+  // the bf16 products; the two lanes of a row hold half of d each) and
+  // L * log2(e), which this kernel also writes for the dK/dV kernel that
+  // runs after it. A row that saw no key (possible only with a -inf bias)
+  // has L = -inf; +inf here makes every recomputed probability
+  // exp2(x - inf) exactly 0.
   bf16x8 qf[KS], dof[KS];
   float l2 = 0.f, dd = 0.f;
   {
     const auto rq = make_rsrc(Q + hoff, nrec);
     const auto rdo = make_rsrc(dO + hoff, nrec);
+    const auto ro = make_rsrc(O + hoff, nrec);
     const uint32_t qoff = row_off(myq, N, tokb, 16 * g);
+    float dpart = 0.f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       qf[ks] = __builtin_bit_cast(bf16x8, buf_load16(rq, qoff + 32 * ks) ^ q_sign);
       dof[ks] = __builtin_bit_cast(bf16x8, buf_load16(rdo, qoff + 32 * ks));
+      const bf16x8 of = __builtin_bit_cast(bf16x8, buf_load16(ro, qoff + 32 * ks));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dpart = __builtin_fmaf((float)of[e], (float)dof[ks][e], dpart);
     }
+    const float dsum_row = xhalf_sum(dpart);
     if (myq < N) {
-      l2 = lse2[(long)head * N + myq];
-      dd = dsum[(long)head * N + myq];
+      const long i = (long)head * N + myq;
+      const float L = LSE[i];
+      l2 = L == -INFINITY ? INFINITY : L * kLog2e;
+      dd = dsum_row;
+      if (g == 0) {
+        lse2[i] = l2;
+        dsum[i] = dd;
+      }
     }
   }
 
@@ -554,14 +534,24 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
 
 template <int D, bool CAUSAL>
 hipError_t launch_bwd(const BwdArgs& a) {
-  const long rows = (long)a.B * a.N * a.H;
   const float c2 = fabsf(a.scale) * kLog2e;
   const uint32_t sign = a.scale < 0.f ? 0x80008000u : 0u;
-  {
-    const unsigned grid = (unsigned)((rows * 8 + 255) / 256);
-    hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3(grid), dim3(256), 0, a.stream,
-                       static_cast<const bf16*>(a.o), static_cast<const bf16*>(a.dout), a.lse,
-                       a.lse2, a.dsum, a.N, a.H, rows);
+  {  // dQ first: it also writes the row terms (L * log2e, D) the dK/dV kernel reads
+    const int nqb = (a.N + kQBlock - 1) / kQBlock;
+    const int total = a.B * a.H * nqb;
+    if (a.bias)
+      hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, true>), dim3(total), dim3(kBwdThreads), 0, a.stream,
+                         static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k),
+                         static_cast<const bf16*>(a.v), static_cast<const bf16*>(a.dout),
+                         static_cast<const bf16*>(a.o), a.lse, a.lse2, a.dsum, static_cast<bf16*>(a.dq), a.N,
+                         a.H, nqb, total, c2, sign, a.scale, static_cast<const bf16*>(a.bias), a.bias_sb,
+                         a.bias_sh, a.bias_srow, static_cast<bf16*>(a.dbias), a.dbias_srow);
+    else
+      hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(total), dim3(kBwdThreads), 0, a.stream,
+                         static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k),
+                         static_cast<const bf16*>(a.v), static_cast<const bf16*>(a.dout),
+                         static_cast<const bf16*>(a.o), a.lse, a.lse2, a.dsum, static_cast<bf16*>(a.dq), a.N,
+                         a.H, nqb, total, c2, sign, a.scale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -581,24 +571,6 @@ hipError_t launch_bwd(const BwdArgs& a) {
                          static_cast<const bf16*>(a.v), static_cast<const bf16*>(a.dout), a.lse2,
                          a.dsum, static_cast<bf16*>(a.dk), static_cast<bf16*>(a.dv), a.N, a.H, nkb,
                          total, c2, sign, a.scale);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  {
-    const int nqb = (a.N + kQBlock - 1) / kQBlock;
-    const int total = a.B * a.H * nqb;
-    if (a.bias)
-      hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, true>), dim3(total), dim3(kBwdThreads), 0, a.stream,
-                         static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k),
-                         static_cast<const bf16*>(a.v), static_cast<const bf16*>(a.dout), a.lse2,
-                         a.dsum, static_cast<bf16*>(a.dq), a.N, a.H, nqb, total, c2, sign, a.scale,
-                         static_cast<const bf16*>(a.bias), a.bias_sb, a.bias_sh, a.bias_srow,
-                         static_cast<bf16*>(a.dbias), a.dbias_srow);
-    else
-      hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(total), dim3(kBwdThreads), 0, a.stream,
-                         static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k),
-                         static_cast<const bf16*>(a.v), static_cast<const bf16*>(a.dout), a.lse2,
-                         a.dsum, static_cast<bf16*>(a.dq), a.N, a.H, nqb, total, c2, sign, a.scale);
     return hipGetLastError();
   }
 }
