@@ -460,7 +460,7 @@ def main():
                    "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
                    "global_batch": w.B, "seq_len": w.N, "parallelism": "single GPU"},
         "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
-        "roofline": roof(bf, bwd_s, "fa_bwd call (bwd_pre_kernel + bwd_dkdv_kernel + bwd_dq_kernel)", "fa_bwd"),
+        "roofline": roof(bf, bwd_s, "fa_bwd call (bwd_dq_kernel, which also forms the row terms, + bwd_dkdv_kernel)", "fa_bwd"),
         "roofline_fwd": roof(ff, fwd_s, "fwd_kernel", "fa_fwd"),
         "cpu_baseline": cpu,
         "detail": detail,
