@@ -20,7 +20,7 @@
 // tile streams in while the current one is used. Rows past the end of the
 // sequence come back as zeros from the buffer range check.
 //
-// Per wave and K/V tile (64 keys at d = 128, 32 at d = 64):
+// Per wave and K/V tile of 64 keys:
 //   S^T = K Q^T     (MFMA; lane l owns query row l % 32, so a row's scores
 //                    sit in two lanes: l and l ^ 32)
 //   online softmax in the log2 domain: c2 = |scale| * log2(e) is folded into
@@ -48,8 +48,10 @@ namespace {
 
 // Per head dimension: query rows per workgroup (32 per wave), keys per K/V
 // tile, LDS stages of the K/V ring and waves per SIMD. Both use 128 rows
-// (4 waves) per workgroup and a double-buffered ring; d = 128 takes 64-key
-// tiles at two workgroups per CU, d = 64 32-key tiles at three. (256-row
+// (4 waves) per workgroup, 64-key tiles and a double-buffered ring; d = 128
+// runs two workgroups per CU, d = 64 three (its softmax work per matrix
+// instruction is twice that of d = 128, so a third wave hides more of it;
+// 64-key rather than 32-key tiles halve its per-tile fixed work). (256-row
 // workgroups and deeper rings were measured slower: one workgroup per CU
 // leaves each workgroup's start and end exposed.)
 template <int D_, int BR_, int BC_, int STAGES_, int WAVES_PER_SIMD_>
@@ -57,7 +59,7 @@ struct KernelCfg {
   static constexpr int D = D_, BR = BR_, BC = BC_, STAGES = STAGES_, WAVES_PER_SIMD = WAVES_PER_SIMD_;
 };
 template <int D> struct FwdCfg;
-template <> struct FwdCfg<64> : KernelCfg<64, 128, 32, 2, 3> {};
+template <> struct FwdCfg<64> : KernelCfg<64, 128, 64, 2, 3> {};
 template <> struct FwdCfg<128> : KernelCfg<128, 128, 64, 2, 2> {};
 // Decode-shaped calls (a few query rows against a long key history) are
 // bound by streaming K and V from memory, and their parallelism comes from
