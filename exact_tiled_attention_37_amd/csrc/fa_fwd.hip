@@ -61,6 +61,13 @@ struct KernelCfg {
 template <int D> struct FwdCfg;
 template <> struct FwdCfg<64> : KernelCfg<64, 128, 64, 2, 3> {};
 template <> struct FwdCfg<128> : KernelCfg<128, 128, 64, 2, 2> {};
+// d = 64 without a bias fits four workgroups per CU (128 registers, 32 KiB
+// of LDS each). Measured faster for key lengths up to 4096 (short and
+// mid-length sequences: more waves to hide the softmax, whole rounds of
+// workgroups) and slower at 16384 (more workgroups share each L2), so the
+// launch picks it by key length.
+struct FwdCfg64Short : KernelCfg<64, 128, 64, 2, 4> {};
+constexpr int kFwd64ShortMaxKeys = 4096;
 // Decode-shaped calls (a few query rows against a long key history) are
 // bound by streaming K and V from memory, and their parallelism comes from
 // splitting the keys, not from query blocks: one wave per workgroup holds
@@ -408,16 +415,30 @@ hipError_t launch_fwd(const FwdArgs& a) {
   const auto* q = static_cast<const bf16*>(a.q);
   const auto* k = static_cast<const bf16*>(a.k);
   const auto* v = static_cast<const bf16*>(a.v);
-  if (a.bias)
+  if (a.bias) {
     hipLaunchKernelGGL((fwd_kernel<FwdCfg<D>, CAUSAL, false, true>), dim3(total), dim3(BR * 2), 0, a.stream, q, k,
                        v, a.o, a.lse, a.Nq, a.Nk, a.delta, a.H, nqb, 1, a.Nk, 0L, 0L, total, c2, q_sign,
                        static_cast<const bf16*>(a.bias), a.bias_sb, a.bias_sh, a.bias_srow);
-  else if (a.f32_out)
-    hipLaunchKernelGGL((fwd_kernel<FwdCfg<D>, CAUSAL, true>), dim3(total), dim3(BR * 2), 0, a.stream, q, k, v,
-                       a.o, a.lse, a.Nq, a.Nk, a.delta, a.H, nqb, 1, a.Nk, 0L, 0L, total, c2, q_sign);
-  else
-    hipLaunchKernelGGL((fwd_kernel<FwdCfg<D>, CAUSAL, false>), dim3(total), dim3(BR * 2), 0, a.stream, q, k, v,
-                       a.o, a.lse, a.Nq, a.Nk, a.delta, a.H, nqb, 1, a.Nk, 0L, 0L, total, c2, q_sign);
+    return hipGetLastError();
+  }
+  auto plain = [&](auto cfg) {
+    using Cfg = decltype(cfg);
+    static_assert(Cfg::BR == BR, "one block size per head dimension");
+    if (a.f32_out)
+      hipLaunchKernelGGL((fwd_kernel<Cfg, CAUSAL, true>), dim3(total), dim3(BR * 2), 0, a.stream, q, k, v, a.o,
+                         a.lse, a.Nq, a.Nk, a.delta, a.H, nqb, 1, a.Nk, 0L, 0L, total, c2, q_sign);
+    else
+      hipLaunchKernelGGL((fwd_kernel<Cfg, CAUSAL, false>), dim3(total), dim3(BR * 2), 0, a.stream, q, k, v, a.o,
+                         a.lse, a.Nq, a.Nk, a.delta, a.H, nqb, 1, a.Nk, 0L, 0L, total, c2, q_sign);
+  };
+  if constexpr (D == 64) {
+    if (a.Nk <= kFwd64ShortMaxKeys)
+      plain(FwdCfg64Short{});
+    else
+      plain(FwdCfg<D>{});
+  } else {
+    plain(FwdCfg<D>{});
+  }
   return hipGetLastError();
 }
 

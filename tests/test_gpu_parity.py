@@ -322,3 +322,45 @@ def test_max_size_sampled_heads(causal):
         check(f"dV head {(b, h)}", sl(dv), rv)
     del q, k, v, do, o, lse, dq, dk, dv
     torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------
+# d = 64 past 4096 keys (the launch switches the d = 64 kernel configuration
+# by key count: four workgroups per CU up to 4096 keys, three beyond)
+
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_d64_long_keys_sampled_rows(causal):
+    B, N, H, d = 1, 5000, 2, 64
+    scale = d ** -0.5
+    announce(f"d64 long keys N={N} causal={causal}")
+    bits = si.draw(B, N, H, d, 61)
+    q, k, v, o, lse = gpu_fwd(bits, causal, scale)
+    o_np, l_np = f64(o), f64(lse)
+    assert np.all(np.isfinite(o_np)) and np.all(np.isfinite(l_np))
+    q64, k64, v64 = (si.bf16_bits_to_f64(bits[n]) for n in ("q", "k", "v"))
+    rows = [0, 1, 63, 64, 127, 128, 2047, 4095, 4096, 4097, 4223, 4224, 4900, 4999]
+    for h in range(H):
+        ro, rl = oracle.attention_forward_rows(q64, k64, v64, causal, scale, 0, h, rows)
+        check(f"O rows head {h}", o_np[0, rows, h, :], ro)
+        check(f"LSE rows head {h}", l_np[0, h, rows], rl, LSE_TOL, LSE_TOL)
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_d64_long_key_chunk(causal):
+    """A 256-row query chunk at positions 4800.. over a 5000-key chunk at
+    0.. (d = 64): the float32 chunk result against the oracle's chunk
+    attention."""
+    import torch
+
+    H, d, Nq, Nk, q0 = 2, 64, 256, 5000, 4800
+    scale = d ** -0.5
+    announce(f"d64 long key chunk Nq={Nq} Nk={Nk} causal={causal}")
+    qb = si.draw(1, Nq, H, d, 62)["q"]
+    kvb = si.draw(1, Nk, H, d, 63)
+    o, lse = fa.fa_fwd_chunk(dev(qb), dev(kvb["k"]), dev(kvb["v"]), causal, q_start=q0, k_start=0,
+                             softmax_scale=scale)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention_forward_chunk(si.bf16_bits_to_f64(qb), si.bf16_bits_to_f64(kvb["k"]),
+                                            si.bf16_bits_to_f64(kvb["v"]), causal, scale, q0, 0)
+    check("O_c", o.cpu().numpy().astype(np.float64), ro)
+    check("L_c", lse.cpu().numpy().astype(np.float64), rl, LSE_TOL, LSE_TOL)
