@@ -344,8 +344,10 @@ def main():
         e2.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    fwd_s = sum(e0.elapsed_time(e1) for e0, e1, _ in ev) / 1e3 / args.steps
-    bwd_s = sum(e1.elapsed_time(e2) for _, e1, e2 in ev) / 1e3 / args.steps
+    fwd_each = sorted(e0.elapsed_time(e1) for e0, e1, _ in ev)  # ms per call
+    bwd_each = sorted(e1.elapsed_time(e2) for _, e1, e2 in ev)
+    fwd_s = sum(fwd_each) / 1e3 / args.steps
+    bwd_s = sum(bwd_each) / 1e3 / args.steps
     step_s = ev[0][0].elapsed_time(ev[-1][2]) / 1e3 / args.steps
     peak_mem = torch.cuda.max_memory_allocated()
 
@@ -369,6 +371,10 @@ def main():
         "arch": torch.cuda.get_device_properties(0).gcnArchName,
         "fwd_ms": round(fwd_s * 1e3, 4),
         "bwd_ms": round(bwd_s * 1e3, 4),
+        "fwd_ms_median": round(fwd_each[len(fwd_each) // 2], 4),
+        "fwd_ms_min": round(fwd_each[0], 4),
+        "bwd_ms_median": round(bwd_each[len(bwd_each) // 2], 4),
+        "bwd_ms_min": round(bwd_each[0], 4),
         "fwd_tflops": round(ff / fwd_s / 1e12, 2),
         "bwd_tflops": round(bf / bwd_s / 1e12, 2),
         "fwd_frac_of_peak": round(ff / fwd_s / 1e12 / PEAK_BF16_TFLOPS, 4),
