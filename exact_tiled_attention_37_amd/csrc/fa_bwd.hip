@@ -77,6 +77,9 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   __shared__ __attribute__((aligned(1024))) char qbuf[2][2 * QT];  // per stage: Q tile, then dO tile
   __shared__ __attribute__((aligned(256))) float rowbuf[2][2 * 64];  // per stage: L*log2e, then D
   __shared__ __attribute__((aligned(1024))) char vblk[TV::BYTES];
+  // Bias of the current step for each wave's 32 keys: 32 query rows x 64
+  // bytes, row-major (see bias_dma / the transpose reads in compute).
+  __shared__ __attribute__((aligned(1024))) char bias_slice[BIAS ? 4 * kQStep * 64 : 16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar registers
@@ -97,10 +100,34 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   const int kb0 = kblk * kKvBlock;
   const int kw0 = kb0 + 32 * wave;
   const int mykey = kw0 + l32;
-  // Bias column of this lane's key (rows of bias_srow readable elements):
-  // rows at or past N read as zeros.
-  const auto rb = make_rsrc(BIAS ? Bias + b * bias_sb + h * bias_sh : Q,
-                            BIAS ? (uint32_t)((long)N * bias_srow * 2) : 0u);
+  // Bias rows of this (batch, head): N rows of bias_srow elements. Each step
+  // the wave's 32 rows x 32 keys (64 bytes per row) go into its LDS slice by
+  // two LDS-DMA loads (lane i of load u fills 16-byte slot 64 u + i: row
+  // 16 u + i / 4, keys 8 (i % 4) .. + 7 of the wave's 32). The whole offset
+  // is per lane, so rows at or past N and keys past the last row's end read
+  // as zeros (the library keeps (N + 64) * bias_srow * 2 below 2^32).
+  const u32x4 rbr = make_raw_rsrc(BIAS ? Bias + b * bias_sb + h * bias_sh : Q,
+                                  BIAS ? (uint32_t)((long)N * bias_srow * 2) : 0u);
+  uint32_t bias_dma_off[BIAS ? 2 : 1];
+  uint32_t bias_tr_addr = 0;
+  const uint32_t bslice_lds = BIAS ? lds_base(bias_slice + wave * kQStep * 64) : 0u;
+  if constexpr (BIAS) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      bias_dma_off[u] = ((uint32_t)(16 * u + (lane >> 2)) * (uint32_t)bias_srow +
+                         (uint32_t)(kb0 + 32 * wave + 8 * (lane & 3))) * 2u;
+    // Transpose reads (ds_read_b64_tr_b16): in each 16-lane group, lane t
+    // points at row R + t / 4, keys K0 + 4 (t % 4) .. + 3 (K0 = 16 for the
+    // groups holding keys 16..31); lane j then receives key K0 + j of rows
+    // R .. R + 3, i.e. its own key's bias for 4 consecutive accumulator rows.
+    const int t = lane & 15, k0 = 16 * ((lane >> 4) & 1);
+    bias_tr_addr = (uint32_t)((4 * g + (t >> 2)) * 64 + (k0 + 4 * (t & 3)) * 2);
+  }
+  auto bias_dma = [&](int step) __attribute__((always_inline)) {
+    const uint32_t qoff = (uint32_t)(step * kQStep) * (uint32_t)bias_srow * 2u;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) dma16_at(rbr, bslice_lds + 1024u * u, bias_dma_off[u] + qoff);
+  };
 
   // This wave's K rows as B operands of S = Q K^T (registers), and the
   // block's V rows (LDS, read as B operands of dP = dO V^T).
@@ -155,20 +182,18 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
 
   // One step of 32 query rows. MASK: the causal mask is applied (steps that
   // straddle the diagonal); the other steps have no per-element masking.
+  const int nqs = (N + kQStep - 1) / kQStep;  // 32-row query steps
   auto compute = [&](int step, const char* qt, const float* rows, auto mask_tag) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
     const int q0 = step * kQStep;
     const char* dot = qt + QT;
-    // Bias of this lane's key for its 16 accumulator rows (queries). The
-    // whole offset is in the per-lane (range-checked) operand, so rows past
-    // N fall beyond the resource and read as zeros (the library keeps
-    // (N + 64) * bias_srow * 2 below 2^32).
-    uint32_t bb[BIAS ? 16 : 1];
+    // Bias of this lane's key for its 16 accumulator rows (queries) from the
+    // slice: rows 8 rq + 4 g .. + 3 per transpose read.
+    i16x4 bt[BIAS ? 4 : 1];
     if constexpr (BIAS) {
-      const uint32_t vq = ((uint32_t)(q0 + 4 * g) * (uint32_t)bias_srow + (uint32_t)mykey) * 2u;
+      const char* const bsl = bias_slice + wave * kQStep * 64;
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        bb[r] = buf_load2(rb, vq + (uint32_t)(8 * (r >> 2) + (r & 3)) * (uint32_t)bias_srow * 2u);
+      for (int rq = 0; rq < 4; ++rq) bt[rq] = lds_read_tr(bsl, (int)bias_tr_addr + 512 * rq);
     }
     f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
@@ -187,12 +212,21 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
         const int r = 4 * rq4 + e;
         float p;
         if constexpr (BIAS)
-          p = fast_exp2(__builtin_fmaf(s[r], c2, __builtin_fmaf(bf16_bits_to_float(bb[r]), kLog2e, -l4[e])));
+          p = fast_exp2(__builtin_fmaf(
+              s[r], c2, __builtin_fmaf(bf16_bits_to_float((uint16_t)bt[rq4][e]), kLog2e, -l4[e])));
         else
           p = fast_exp2(__builtin_fmaf(s[r], c2, -l4[e]));
         if constexpr (MASK) p = (mykey > q0 + qi0 + e) ? 0.f : p;
         p8[r >> 3][r & 7] = p;
         ds8[r >> 3][r & 7] = p * (dp[r] - d4[e]);
+      }
+    }
+    if constexpr (BIAS) {
+      // The slice is read; the next step's bias may overwrite it (the wait
+      // orders the LDS-DMA writes after these reads).
+      if (step + 1 < nqs) {
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        bias_dma(step + 1);
       }
     }
     const bf16x8 pb[2] = {to_bf16x8(p8[0]), to_bf16x8(p8[1])};
@@ -211,10 +245,10 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   // of them straddle it and are masked, the rest need no mask. Step s lives
   // in stage (s - s0) % 2; each loop has a single exit, so the accumulators
   // keep their registers across the loop boundaries.
-  const int nqs = (N + kQStep - 1) / kQStep;
   const int s0 = CAUSAL ? kb0 / kQStep : 0;
   const int sm = CAUSAL ? min(nqs, s0 + kKvBlock / kQStep) : s0;  // masked steps: [s0, sm)
   issue(s0, qbuf[0], rowbuf[0]);
+  if constexpr (BIAS) bias_dma(s0);
   wait_vmem();
   __syncthreads();
   int step = s0;
