@@ -34,15 +34,19 @@ PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "train_causal_traffic.json")
 
 
+# Sources of the kernels the stored traffic describes (the forward and
+# backward calls of the training step and their launch path).
+TRAFFIC_SOURCES = ("fa_api.hip", "fa_bwd.hip", "fa_common.hpp", "fa_fwd.hip", "fa_launch.hpp", "fa_merge.hip")
+
+
 def kernel_source_hash() -> str:
-    """SHA-256 of the kernel sources; a stored traffic measurement is only
-    reported while the kernels it was taken on are unchanged."""
-    import glob
+    """SHA-256 of the sources of the measured kernels; a stored traffic
+    measurement is only reported while they are unchanged."""
     import hashlib
 
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "exact_tiled_attention_37_amd", "csrc")
-    for path in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.hpp"))):
+    for path in (os.path.join(csrc, name) for name in TRAFFIC_SOURCES):
         h.update(os.path.basename(path).encode())
         with open(path, "rb") as fh:
             h.update(fh.read())
