@@ -12,7 +12,7 @@
 // so long sequences with few heads still fill the chip; inside a workgroup
 // each of the 4 wavefronts owns 32 query rows and all of them share the K/V
 // tiles staged in LDS, so no partial results are exchanged between waves.
-// Two (d = 128) or three (d = 64) workgroups share a CU, so one wave's
+// Two (d = 128) or three to four (d = 64) workgroups share a CU, so one wave's
 // softmax arithmetic overlaps another's matrix instructions.
 //
 // K/V tiles move from memory straight into LDS with buffer loads
