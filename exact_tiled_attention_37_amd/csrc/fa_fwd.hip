@@ -13,7 +13,9 @@
 // each of the 4 wavefronts owns 32 query rows and all of them share the K/V
 // tiles staged in LDS, so no partial results are exchanged between waves.
 // Two (d = 128) or three to four (d = 64) workgroups share a CU, so one wave's
-// softmax arithmetic overlaps another's matrix instructions.
+// softmax arithmetic overlaps another's matrix instructions; a d = 128
+// launch too small for that (at most one workgroup per CU) overlaps them
+// inside each wave instead (software-pipelined tile loop).
 //
 // K/V tiles move from memory straight into LDS with buffer loads
 // that write LDS directly (no register staging), double-buffered: the next
@@ -57,6 +59,7 @@ namespace {
 template <int D_, int BR_, int BC_, int STAGES_, int WAVES_PER_SIMD_>
 struct KernelCfg {
   static constexpr int D = D_, BR = BR_, BC = BC_, STAGES = STAGES_, WAVES_PER_SIMD = WAVES_PER_SIMD_;
+  static constexpr bool PIPE = false;  // software-pipelined tile loop (below)
 };
 template <int D> struct FwdCfg;
 template <> struct FwdCfg<64> : KernelCfg<64, 128, 64, 2, 3> {};
@@ -68,6 +71,18 @@ template <> struct FwdCfg<128> : KernelCfg<128, 128, 64, 2, 2> {};
 // launch picks it by key length.
 struct FwdCfg64Short : KernelCfg<64, 128, 64, 2, 4> {};
 constexpr int kFwd64ShortMaxKeys = 4096;
+// A launch of at most one workgroup per CU (e.g. one 2048-row chunk of 16
+// heads) has a single wave per SIMD, so no second wave hides one wave's
+// softmax behind another's matrix instructions. This form does the overlap
+// inside the wave: the scores of the next tile are computed while the
+// softmax of the current one runs. Its launch bound still asks for two
+// waves per SIMD, which caps it at 256 registers: with more, the compiler
+// keeps the MFMA accumulators in the AGPR file and copies every value
+// between the two register files.
+struct FwdCfgPipe128 : KernelCfg<128, 128, 64, 2, 2> {
+  static constexpr bool PIPE = true;
+};
+constexpr int kNumCus = kNumXcd * kCusPerXcd;
 // Decode-shaped calls (a few query rows against a long key history) are
 // bound by streaming K and V from memory, and their parallelism comes from
 // splitting the keys, not from query blocks: one wave per workgroup holds
@@ -335,49 +350,225 @@ __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD))) v
     }
     wait_vmem();
   };
-#pragma unroll
-  for (int t = 0; t < STAGES - 1; ++t)
-    if (t < ntiles) issue(j0 + t, stage(t));
-  if (BIAS && j0 < j1) bias_fetch(j0);
-  wait_next(-1);
-  if (BIAS && j0 < j1) bias_store();
-  __syncthreads();
   // Tiles before jm need no mask for any wave of this workgroup; they run in
   // a loop of their own so that the masked variant never joins the hot loop.
   // (causal: the tiles whose last key is visible to the block's first row)
   const int jm_all = CAUSAL ? min(max(0, qblk * kFwdBR + delta + 1) / kFwdBC, Nk / kFwdBC) : Nk / kFwdBC;
   const int jm = min(max(jm_all, j0), j1);
-  int j = j0;
-  // In the unmasked causal loop half of a wave's loads of the next tile are
-  // issued before this tile's S product and half after it, so the LDS
-  // writes of the workgroup's loads do not arrive in one burst (long causal
-  // loops have the latency to spare; short non-causal ones do not).
-  // With a bias, iteration j also fetches the bias of tile j + 1 into
-  // registers and writes it to the wave's LDS slice after this tile's
-  // compute has read tile j's (a wave's LDS operations run in order).
-  constexpr int SPLIT = CAUSAL ? DMA_PER_WAVE / 2 : DMA_PER_WAVE;
-  for (; j < jm; ++j) {
-    const int t = j - j0;
-    const bool more = t + STAGES - 1 < ntiles;
-    if (more) issue(j + STAGES - 1, stage(t + STAGES - 1), 0, SPLIT);
-    if (BIAS && j + 1 < j1) bias_fetch(j + 1);
-    compute(j, stage(t), std::false_type{}, [&]() __attribute__((always_inline)) {
-      if (SPLIT < DMA_PER_WAVE && more) issue(j + STAGES - 1, stage(t + STAGES - 1), SPLIT, DMA_PER_WAVE);
-    });
-    wait_next(t);
-    if (BIAS && j + 1 < j1) bias_store();
+  if constexpr (Cfg::PIPE) {
+    static_assert(!BIAS && STAGES == 2, "the pipelined form has no bias and a two-stage ring");
+    // Iteration t computes the scores of tile t + 1 on the matrix unit while
+    // the vector unit takes the softmax of tile t, then O += P(t) V(t). The
+    // arithmetic is that of `compute`, in the same order; only the
+    // instruction schedule differs. K of tile t + 1 and V of tile t are in
+    // use together, so K is fetched two tiles ahead and V one: iteration t
+    // loads K of tile t + 2 into the slot that K of tile t was read from
+    // (in iteration t - 1, before its barrier) and V of tile t + 1.
+    auto issue_one = [&](const u32x4& r, int tile, uint32_t l0) __attribute__((always_inline)) {
+      const u32x4 rt = rsrc_advance(r, (uint32_t)(tile * kFwdBC) * tokb);
+#pragma unroll
+      for (int t = 0; t < DMA_PER_WAVE; ++t) {
+        const int u = wave + NW * t;
+        if (T::LOADS < NW && u >= T::LOADS) break;
+        dma16_at(rt, l0 + T::dma_dst(u), dma_off[t]);
+      }
+    };
+    auto k_lds = [&](int t) __attribute__((always_inline)) { return ring_lds + (uint32_t)((t & 1) * 2 * TILE); };
+    auto pipe_loads = [&](int t) __attribute__((always_inline)) {
+      if (t + 2 < ntiles) issue_one(rk, j0 + t + 2, k_lds(t));
+      if (t + 1 < ntiles) issue_one(rv, j0 + t + 1, k_lds(t + 1) + TILE);
+    };
+    auto s_product = [&](const char* kt, f32x16 (&s)[KB]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) s[kb] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) s[kb] = mfma32(T::row8(kt, kb * 32 + l32, 2 * ks + g), qf[ks], s[kb]);
+    };
+    // Softmax and P V of tile t from its scores sc; with AHEAD the scores of
+    // tile t + 1 go to sn first. The group barriers ask the scheduler to put
+    // up to six vector instructions of the softmax after each matrix
+    // instruction of the next tile's scores, and the row sums and bf16 packs
+    // between those of P V; the rarely taken rescale branch sits between the
+    // two groups (P is computed before it from the new maximum).
+    auto pipe_step = [&](int t, f32x16 (&sc)[KB], f32x16 (&sn)[KB], auto mask_tag, auto ahead_tag, auto&& loads)
+                         __attribute__((always_inline)) {
+      constexpr bool MASK = decltype(mask_tag)::value;
+      constexpr bool AHEAD = decltype(ahead_tag)::value;
+      loads();
+      const int key0 = (j0 + t) * kFwdBC;
+      if constexpr (AHEAD) s_product(stage(t + 1), sn);
+      if constexpr (MASK) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+            if ((CAUSAL && key > myq + delta) || key >= Nk) sc[kb][r] = -INFINITY;
+          }
+      }
+      float mx = max16(sc[0], -INFINITY);
+#pragma unroll
+      for (int kb = 1; kb < KB; ++kb) mx = max16(sc[kb], mx);
+      mx = xhalf_max(mx);
+      const float tile_m = (mx == -INFINITY) ? -INFINITY : mx * c2;
+      const bool grow = tile_m > m_run + kRescaleSlack;
+      const float m_new = grow ? tile_m : m_run;
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      f32x8 p[2 * KB];
+#pragma unroll
+      for (int ks = 0; ks < 2 * KB; ++ks)
+#pragma unroll
+        for (int s8 = 0; s8 < 8; ++s8) {
+          const float sv = sc[ks >> 1][8 * (ks & 1) + s8];
+          float e = fast_exp2(__builtin_fmaf(sv, c2, -m_use));
+          if constexpr (MASK) e = (sv == -INFINITY) ? 0.f : e;  // exact zero even when c2 = 0
+          p[ks][s8] = e;
+        }
+      // P is used only after the branch; without these the compiler sinks
+      // the exponentials past it, away from the matrix instructions.
+#pragma unroll
+      for (int ks = 0; ks < 2 * KB; ++ks) asm volatile("" : "+v"(p[ks]));
+      if constexpr (AHEAD && !MASK) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // LDS reads of K
+#pragma unroll
+        for (int i = 0; i < KS * KB; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // vector instructions
+          if (i + 4 < KS * KB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+      }
+      if (__builtin_amdgcn_ballot_w64(grow)) {  // wave-uniform, rarely taken
+        asm volatile("" ::: "memory");          // keep it a branch (no speculation)
+        const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+      }
+      m_run = m_new;
+      bf16x8 pf[2 * KB];
+#pragma unroll
+      for (int ks = 0; ks < 2 * KB; ++ks) {
+        l_run += sum8(p[ks]);
+        pf[ks] = to_bf16x8(p[ks]);
+      }
+      const char* vt = stage(t) + TILE;
+#pragma unroll
+      for (int ks = 0; ks < 2 * KB; ++ks)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const bf16x8 a = T::col8(vt, 16 * ks + 4 * g, 16 * ks + 8 + 4 * g, 32 * db + 16 * (G & 1), lane);
+          oacc[db] = mfma32(a, pf[ks], oacc[db]);
+        }
+      if constexpr (AHEAD && !MASK) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);  // transpose reads of V
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 1);
+#pragma unroll
+        for (int i = 0; i < 2 * KB * DB; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+          __builtin_amdgcn_sched_group_barrier(0x002, 3, 1);
+          if (i + 2 < 2 * KB * DB) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+        }
+      }
+      wait_vmem();
+      __syncthreads();
+    };
+    const int tm = jm - j0;  // tiles [0, tm) need no mask
+    // The tiles this wave needs form a prefix of the range (causal: those
+    // whose first key is visible to the wave's last row); every wave needs
+    // the first tm.
+    const int wlast = qw0 + 31 + delta;
+    const int nt_w = !CAUSAL ? ntiles : wlast < 0 ? 0 : min(ntiles, max(0, wlast / kFwdBC + 1 - j0));
+    if (ntiles > 0) {
+      issue_one(rk, j0, k_lds(0));
+      issue_one(rv, j0, k_lds(0) + TILE);
+    }
+    if (ntiles > 1) issue_one(rk, j0 + 1, k_lds(1));
+    wait_vmem();
     __syncthreads();
-  }
-  for (; j < j1; ++j) {
-    const int t = j - j0;
-    if (t + STAGES - 1 < ntiles) issue(j + STAGES - 1, stage(t + STAGES - 1));
-    if (BIAS && j + 1 < j1) bias_fetch(j + 1);
-    // A tile whose first key lies past this wave's last row is fully masked
-    // for it and contributes nothing.
-    if (!CAUSAL || j * kFwdBC <= qw0 + 31 + delta) compute(j, stage(t), std::true_type{}, []() {});
-    wait_next(t);
-    if (BIAS && j + 1 < j1) bias_store();
+    f32x16 sa[KB], sb[KB];
+    if (nt_w > 0) s_product(stage(0), sa);
+    __syncthreads();  // every wave has read K of tile 0 before iteration 0 refills its slot
+    int t = 0;
+    const int tu = min(tm, ntiles - 1);  // unmasked iterations that have a next tile
+    for (; t + 1 < tu; t += 2) {
+      pipe_step(t, sa, sb, std::false_type{}, std::true_type{}, [&]() __attribute__((always_inline)) { pipe_loads(t); });
+      pipe_step(t + 1, sb, sa, std::false_type{}, std::true_type{},
+                [&]() __attribute__((always_inline)) { pipe_loads(t + 1); });
+    }
+    if (t < tu) {
+      pipe_step(t, sa, sb, std::false_type{}, std::true_type{}, [&]() __attribute__((always_inline)) { pipe_loads(t); });
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) sa[kb] = sb[kb];
+      ++t;
+    }
+    if (t < tm) {  // the range's last tile, unmasked (then tm == ntiles)
+      pipe_step(t, sa, sb, std::false_type{}, std::false_type{}, [&]() __attribute__((always_inline)) { pipe_loads(t); });
+      ++t;
+    }
+    // The few masked tiles (the diagonal, the ragged end) run without the
+    // overlap, which would need more registers than the wave has: tile tm
+    // uses the scores computed ahead, later tiles compute theirs in the
+    // step. From here on iteration t loads K and V of tile t + 1 (K of tile
+    // tm + 1 was already fetched ahead); both slots of tile t + 1 last held
+    // tile t - 1, which was read before the previous barrier.
+    for (; t < ntiles; ++t) {
+      auto masked_loads = [&]() __attribute__((always_inline)) {
+        if (t + 1 < ntiles) {
+          if (t > tm) issue_one(rk, j0 + t + 1, k_lds(t + 1));
+          issue_one(rv, j0 + t + 1, k_lds(t + 1) + TILE);
+        }
+      };
+      if (t == tm && t < nt_w) {
+        pipe_step(t, sa, sb, std::true_type{}, std::false_type{}, masked_loads);
+      } else {  // a wave that does not need the tile only loads and meets the barrier
+        masked_loads();
+        if (t < nt_w) compute(j0 + t, stage(t), std::true_type{}, []() {});
+        wait_vmem();
+        __syncthreads();
+      }
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < STAGES - 1; ++t)
+      if (t < ntiles) issue(j0 + t, stage(t));
+    if (BIAS && j0 < j1) bias_fetch(j0);
+    wait_next(-1);
+    if (BIAS && j0 < j1) bias_store();
     __syncthreads();
+    int j = j0;
+    // In the unmasked causal loop half of a wave's loads of the next tile are
+    // issued before this tile's S product and half after it, so the LDS
+    // writes of the workgroup's loads do not arrive in one burst (long causal
+    // loops have the latency to spare; short non-causal ones do not).
+    // With a bias, iteration j also fetches the bias of tile j + 1 into
+    // registers and writes it to the wave's LDS slice after this tile's
+    // compute has read tile j's (a wave's LDS operations run in order).
+    constexpr int SPLIT = CAUSAL ? DMA_PER_WAVE / 2 : DMA_PER_WAVE;
+    for (; j < jm; ++j) {
+      const int t = j - j0;
+      const bool more = t + STAGES - 1 < ntiles;
+      if (more) issue(j + STAGES - 1, stage(t + STAGES - 1), 0, SPLIT);
+      if (BIAS && j + 1 < j1) bias_fetch(j + 1);
+      compute(j, stage(t), std::false_type{}, [&]() __attribute__((always_inline)) {
+        if (SPLIT < DMA_PER_WAVE && more) issue(j + STAGES - 1, stage(t + STAGES - 1), SPLIT, DMA_PER_WAVE);
+      });
+      wait_next(t);
+      if (BIAS && j + 1 < j1) bias_store();
+      __syncthreads();
+    }
+    for (; j < j1; ++j) {
+      const int t = j - j0;
+      if (t + STAGES - 1 < ntiles) issue(j + STAGES - 1, stage(t + STAGES - 1));
+      if (BIAS && j + 1 < j1) bias_fetch(j + 1);
+      // A tile whose first key lies past this wave's last row is fully masked
+      // for it and contributes nothing.
+      if (!CAUSAL || j * kFwdBC <= qw0 + 31 + delta) compute(j, stage(t), std::true_type{}, []() {});
+      wait_next(t);
+      if (BIAS && j + 1 < j1) bias_store();
+      __syncthreads();
+    }
   }
 
   // A row that saw no key (possible only with a causal offset that puts every
@@ -437,7 +628,10 @@ hipError_t launch_fwd(const FwdArgs& a) {
     else
       plain(FwdCfg<D>{});
   } else {
-    plain(FwdCfg<D>{});
+    if (total <= kNumCus)
+      plain(FwdCfgPipe128{});
+    else
+      plain(FwdCfg<D>{});
   }
   return hipGetLastError();
 }

@@ -364,3 +364,34 @@ def test_d64_long_key_chunk(causal):
                                             si.bf16_bits_to_f64(kvb["v"]), causal, scale, q0, 0)
     check("O_c", o.cpu().numpy().astype(np.float64), ro)
     check("L_c", lse.cpu().numpy().astype(np.float64), rl, LSE_TOL, LSE_TOL)
+
+
+# ---------------------------------------------------------------------------
+# d = 128 on both sides of the launch switch at one workgroup per CU: 16
+# heads of 2000 rows (16 blocks each, 256 workgroups) run the
+# software-pipelined loop, 17 heads (272 workgroups) the plain one. The two
+# compute the same arithmetic in the same order, so the shared heads must
+# agree bit for bit; both are checked against the oracle on sampled rows
+# (ragged end, diagonal tiles, first and last blocks).
+
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_launch_forms_agree(causal):
+    import torch
+
+    B, N, H, d = 1, 2000, 17, 128
+    scale = d ** -0.5
+    announce(f"launch forms N={N} H={H} vs {H - 1} causal={causal}")
+    bits = si.draw(B, N, H, d, 64)
+    q, k, v, o17, l17 = gpu_fwd(bits, causal, scale)
+    q16, k16, v16 = (x[:, :, : H - 1, :].contiguous() for x in (q, k, v))
+    o16, l16 = fa.fa_fwd(q16, k16, v16, causal, scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o16, o17[:, :, : H - 1, :]), "O differs between the two launch forms"
+    assert torch.equal(l16, l17[:, : H - 1, :]), "LSE differs between the two launch forms"
+    q64, k64, v64 = (si.bf16_bits_to_f64(bits[n]) for n in ("q", "k", "v"))
+    rows = [0, 1, 31, 32, 63, 64, 127, 128, 1023, 1919, 1920, 1983, 1984, 1999]
+    o_np, l_np = f64(o17), f64(l17)
+    for h in (0, H - 2, H - 1):
+        ro, rl = oracle.attention_forward_rows(q64, k64, v64, causal, scale, 0, h, rows)
+        check(f"O rows head {h}", o_np[0, rows, h, :], ro)
+        check(f"LSE rows head {h}", l_np[0, h, rows], rl, LSE_TOL, LSE_TOL)
