@@ -14,7 +14,12 @@
 // Memory-bound: per output row it reads C rows of d float32 plus C logsumexp
 // values and writes d bfloat16 plus one float. Rows are laid out [B, N, H]
 // in the outputs and in every chunk, so a wave reads whole contiguous rows;
-// D / 4 lanes cover one row with 16-byte loads.
+// D / 4 lanes cover one row with 16-byte loads. A lane's loads of the C
+// chunks are independent, and the chunk loops are unrolled so that eight of
+// them are in flight at once; few rows with many chunks (decode-shaped
+// calls) would otherwise wait on one load latency per pair of chunks.
+// Small row counts launch 64-thread workgroups, so that they still reach
+// every CU.
 
 #include "fa_common.hpp"
 #include "fa_launch.hpp"
@@ -23,7 +28,8 @@ namespace fa {
 
 namespace {
 
-constexpr int kMergeThreads = 256;
+constexpr int kMergeThreads = 256;       // threads per workgroup (64 for small launches)
+constexpr int kMergeSmallThreads = 64;
 
 template <int D>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __restrict__ Op,
@@ -31,8 +37,8 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __res
                                                                bf16* __restrict__ O, float* __restrict__ L,
                                                                int N, int H, long rows) {
   constexpr int LPR = D / 4;                     // lanes per row
-  constexpr int RPB = kMergeThreads / LPR;       // rows per block
-  const long r = (long)blockIdx.x * RPB + threadIdx.x / LPR;
+  const int rpb = (int)blockDim.x / LPR;         // rows per block
+  const long r = (long)blockIdx.x * rpb + threadIdx.x / LPR;
   const int c4 = threadIdx.x % LPR;
   if (r >= rows) return;
   const int h = (int)(r % H);
@@ -44,12 +50,13 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __res
   const long ostride = rows * D;                 // elements per chunk of O
 
   float m = -INFINITY;
+#pragma unroll 8
   for (int c = 0; c < C; ++c) m = fmaxf(m, Lp[c * lstride + lrow]);
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float tot = 0.f;
   if (m != -INFINITY) {
     const float* op = Op + r * D + 4 * c4;
-#pragma unroll 4
+#pragma unroll 8
     for (int c = 0; c < C; ++c) {
       const float w = fast_exp2((Lp[c * lstride + lrow] - m) * kLog2e);  // exp2(-inf) = 0
       const f32x4 x = *reinterpret_cast<const f32x4*>(op + c * ostride);
@@ -67,11 +74,16 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __res
 
 template <int D>
 hipError_t launch_merge(const MergeArgs& a) {
-  constexpr int RPB = kMergeThreads / (D / 4);
   const long rows = (long)a.B * a.N * a.H;
-  const unsigned grid = (unsigned)((rows + RPB - 1) / RPB);
-  hipLaunchKernelGGL((merge_kernel<D>), dim3(grid), dim3(kMergeThreads), 0, a.stream, a.o_parts, a.lse_parts,
-                     a.C, static_cast<bf16*>(a.o), a.lse, a.N, a.H, rows);
+  // Fewer than two full workgroups per CU: smaller workgroups spread the rows
+  // over more CUs.
+  const int threads =
+      (rows + kMergeThreads / (D / 4) - 1) / (kMergeThreads / (D / 4)) < 2 * kNumXcd * kCusPerXcd ? kMergeSmallThreads
+                                                                                                : kMergeThreads;
+  const int rpb = threads / (D / 4);
+  const unsigned grid = (unsigned)((rows + rpb - 1) / rpb);
+  hipLaunchKernelGGL((merge_kernel<D>), dim3(grid), dim3(threads), 0, a.stream, a.o_parts, a.lse_parts, a.C,
+                     static_cast<bf16*>(a.o), a.lse, a.N, a.H, rows);
   return hipGetLastError();
 }
 
