@@ -306,8 +306,8 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this benchmark runs on exactly one GPU; the multi-GPU path "
-                                   "is a design note only (see DESIGN.md)", "n_gpus": args.gpus}))
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; sharding the path over "
+                                   "several GPUs is designed but not built", "n_gpus": args.gpus}))
         sys.exit(2)
 
     import numpy as np
