@@ -142,14 +142,21 @@ def test_chunks_merge_to_full_attention(d, causal):
     check("merged LSE", f64(lse), rl, LSE_TOL, LSE_TOL)
 
 
+# (C, B, N, H): small launches take the chunks in batches of 16 (C = 21 ends
+# in a partial batch, C = 40 takes three); B*N*H = 9600 rows is a large
+# launch, which takes the plain loop.
+MERGE_CASES = [(5, 2, 37, 3), (21, 2, 37, 3), (40, 2, 19, 3), (3, 2, 600, 8)]
+
+
+@pytest.mark.parametrize("case", MERGE_CASES, ids=lambda c: "C%dB%dN%dH%d" % c)
 @pytest.mark.parametrize("d", [64, 128])
-def test_merge_against_oracle(d):
+def test_merge_against_oracle(d, case):
     """Random chunk results, including chunks and rows with lse = -inf."""
     import torch
 
-    C, B, N, H = 5, 2, 37, 3
-    announce(f"merge C={C} d={d}")
-    rng = np.random.Generator(np.random.PCG64(8800 + d))
+    C, B, N, H = case
+    announce(f"merge C={C} B={B} N={N} H={H} d={d}")
+    rng = np.random.Generator(np.random.PCG64(8800 + d + 7 * C))
     o_parts = rng.standard_normal((C, B, N, H, d)).astype(np.float32)
     lse_parts = (rng.standard_normal((C, B, H, N)) * 4.0).astype(np.float32)
     lse_parts[1] = -np.inf                 # an empty chunk
