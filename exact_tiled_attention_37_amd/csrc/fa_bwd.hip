@@ -85,7 +85,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar registers
   const int g = lane >> 5, l32 = lane & 31, G = lane >> 4;
 
-  const HeadRank hr = block_order<CAUSAL>(blockIdx.x, total_blocks / nkb, nkb, 2 * kCusPerXcd);
+  const HeadRank hr = block_order<CAUSAL>(blockIdx.x, total_blocks / nkb, nkb, 2 * kCusPerXcd, 2);
   const int head = hr.head;
   const int kblk = hr.rank;  // block 0 has the most causal work: it goes first
   const int b = head / H, h = head - b * H;
@@ -314,7 +314,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   const int g = lane >> 5, l32 = lane & 31, G = lane >> 4;
   char* const dbw_lds = dbias_lds + (BIAS ? wave * 32 * RB : 0);
 
-  const HeadRank hr = block_order<CAUSAL>(blockIdx.x, total_blocks / nqb, nqb, 2 * kCusPerXcd);
+  const HeadRank hr = block_order<CAUSAL>(blockIdx.x, total_blocks / nqb, nqb, 2 * kCusPerXcd, 2);
   const int head = hr.head;
   const int qblk = nqb - 1 - hr.rank;  // longest causal rows first
   const int b = head / H, h = head - b * H;

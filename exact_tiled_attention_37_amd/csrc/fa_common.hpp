@@ -286,20 +286,23 @@ __device__ __forceinline__ int xcd_remap(int bid, int total) {
 // (xcd_remap: one contiguous range per XCD) takes the heads in groups of G;
 // inside a group the blocks go rank-major (heaviest rank of every head of
 // the group first). Causal blocks of one head differ in work: with G chosen
-// so that a group holds at least as many blocks as an XCD runs at once
-// (`slots`), every XCD runs longest-first within the group (the head-by-head
-// order left a head's heavy blocks behind the previous head's light ones),
-// while only about G heads share the XCD's L2 at a time. Non-causal blocks
-// do equal work: G = 1, the blocks of a head run together and read their K
-// and V through one L2.
+// so that a group holds at least `rounds` times as many blocks as an XCD
+// runs at once (`slots`), every XCD runs longest-first within the group (the
+// head-by-head order left a head's heavy blocks behind the previous head's
+// light ones), while only about G heads share the XCD's L2 at a time. The
+// bf16 forward and backward take two rounds per group (one left the next
+// group's heavy blocks behind the current group's light ones), the FP8
+// forward and decode one (two measured slower there). Non-causal blocks do
+// equal work: G = 1, the blocks of a head run together and read their K and
+// V through one L2.
 struct HeadRank {
   int head, rank;
 };
 constexpr int kCusPerXcd = 32;  // MI355X: 256 CUs in 8 XCDs
 template <bool CAUSAL>
-__device__ __forceinline__ HeadRank block_order(int bid, int heads, int per_head, int slots) {
+__device__ __forceinline__ HeadRank block_order(int bid, int heads, int per_head, int slots, int rounds) {
   const int l = xcd_remap(bid, heads * per_head);
-  const int G = CAUSAL ? min(heads, max(1, (slots + per_head - 1) / per_head)) : 1;
+  const int G = CAUSAL ? min(heads, max(1, (rounds * slots + per_head - 1) / per_head)) : 1;
   const int gsize = G * per_head;
   const int g = l / gsize;
   const int within = l - g * gsize;

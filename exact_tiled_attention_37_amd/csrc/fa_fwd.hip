@@ -60,6 +60,7 @@ template <int D_, int BR_, int BC_, int STAGES_, int WAVES_PER_SIMD_>
 struct KernelCfg {
   static constexpr int D = D_, BR = BR_, BC = BC_, STAGES = STAGES_, WAVES_PER_SIMD = WAVES_PER_SIMD_;
   static constexpr bool PIPE = false;  // software-pipelined tile loop (below)
+  static constexpr int GROUP_ROUNDS = 2;  // block order: XCD rounds of blocks per head group
 };
 template <int D> struct FwdCfg;
 template <> struct FwdCfg<64> : KernelCfg<64, 128, 64, 2, 3> {};
@@ -90,8 +91,12 @@ constexpr int kNumCus = kNumXcd * kCusPerXcd;
 // d = 64 keeps two tiles in flight per wave (3 stages; its tiles are half
 // the size), d = 128 one (measured best).
 template <int D> struct DecCfg;
-template <> struct DecCfg<64> : KernelCfg<64, 32, kDecodeBC, 3, 2> {};
-template <> struct DecCfg<128> : KernelCfg<128, 32, kDecodeBC, 2, 2> {};
+template <> struct DecCfg<64> : KernelCfg<64, 32, kDecodeBC, 3, 2> {
+  static constexpr int GROUP_ROUNDS = 1;
+};
+template <> struct DecCfg<128> : KernelCfg<128, 32, kDecodeBC, 2, 2> {
+  static constexpr int GROUP_ROUNDS = 1;
+};
 constexpr float kRescaleSlack = 8.f;  // log2 units a row max may exceed the running max
 
 // Nq query rows attend to Nk key rows. With the causal mask key j is visible
@@ -133,7 +138,7 @@ __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD))) v
   const int g = lane >> 5, l32 = lane & 31, G = lane >> 4;
 
   const HeadRank hr = block_order<CAUSAL>(blockIdx.x, total_blocks / (nqb * nsplit), nqb * nsplit,
-                                          kCusPerXcd * Cfg::WAVES_PER_SIMD);
+                                          kCusPerXcd * Cfg::WAVES_PER_SIMD, Cfg::GROUP_ROUNDS);
   const int head = hr.head;                        // b * H + h
   const int qblk = nqb - 1 - hr.rank / nsplit;     // longest causal rows first
   const int split = hr.rank - (hr.rank / nsplit) * nsplit;
