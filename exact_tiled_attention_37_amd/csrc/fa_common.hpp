@@ -290,11 +290,10 @@ __device__ __forceinline__ int xcd_remap(int bid, int total) {
 // runs at once (`slots`), every XCD runs longest-first within the group (the
 // head-by-head order left a head's heavy blocks behind the previous head's
 // light ones), while only about G heads share the XCD's L2 at a time. The
-// bf16 forward and backward take two rounds per group (one left the next
-// group's heavy blocks behind the current group's light ones), the FP8
-// forward and decode one (two measured slower there). Non-causal blocks do
-// equal work: G = 1, the blocks of a head run together and read their K and
-// V through one L2.
+// forward and backward kernels take two rounds per group (one left the next
+// group's heavy blocks behind the current group's light ones), decode one.
+// Non-causal blocks do equal work: G = 1, the blocks of a head run together
+// and read their K and V through one L2.
 struct HeadRank {
   int head, rank;
 };
@@ -302,7 +301,22 @@ constexpr int kCusPerXcd = 32;  // MI355X: 256 CUs in 8 XCDs
 template <bool CAUSAL>
 __device__ __forceinline__ HeadRank block_order(int bid, int heads, int per_head, int slots, int rounds) {
   const int l = xcd_remap(bid, heads * per_head);
-  const int G = CAUSAL ? min(heads, max(1, (rounds * slots + per_head - 1) / per_head)) : 1;
+  int G = CAUSAL ? min(heads, max(1, (rounds * slots + per_head - 1) / per_head)) : 1;
+  // A group must not straddle two XCDs' ranges of heads: the XCD holding its
+  // first part would get only its heaviest blocks, the next one only its
+  // lightest. With whole heads per XCD, G becomes the heads per XCD when it
+  // is at least that many, else the smallest divisor of it not below G (if
+  // one is within 2 G).
+  if (CAUSAL && heads % kNumXcd == 0) {
+    const int hx = heads / kNumXcd;
+    if (G >= hx) {
+      G = hx;
+    } else {
+      int d = G;
+      while (d < 2 * G && hx % d) ++d;
+      if (hx % d == 0) G = d;
+    }
+  }
   const int gsize = G * per_head;
   const int g = l / gsize;
   const int within = l - g * gsize;

@@ -79,7 +79,7 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(3, 3
   const int lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31, G = lane >> 4, j16 = lane & 15;
 
-  const HeadRank hr = block_order<CAUSAL>(blockIdx.x, total_blocks / nqb, nqb, 3 * kCusPerXcd, 1);
+  const HeadRank hr = block_order<CAUSAL>(blockIdx.x, total_blocks / nqb, nqb, 3 * kCusPerXcd, 2);
   const int head = hr.head;                            // b * H + h
   const int qblk = nqb - 1 - hr.rank;                  // longest causal rows first
   const int b = head / H, h = head - b * H;
