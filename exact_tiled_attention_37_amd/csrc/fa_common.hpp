@@ -305,16 +305,19 @@ __device__ __forceinline__ HeadRank block_order(int bid, int heads, int per_head
   // A group must not straddle two XCDs' ranges of heads: the XCD holding its
   // first part would get only its heaviest blocks, the next one only its
   // lightest. With whole heads per XCD, G becomes the heads per XCD when it
-  // is at least that many, else the smallest divisor of it not below G (if
-  // one is within 2 G).
+  // is at least that many; a G that does not divide them becomes the next
+  // power of two if that divides them (or reaches them). Other counts keep
+  // G (one candidate only: this runs in every thread at the start).
   if (CAUSAL && heads % kNumXcd == 0) {
     const int hx = heads / kNumXcd;
     if (G >= hx) {
       G = hx;
-    } else {
-      int d = G;
-      while (d < 2 * G && hx % d) ++d;
-      if (hx % d == 0) G = d;
+    } else if (hx % G != 0) {  // then G > 1
+      const int p2 = 1 << (32 - __builtin_clz((unsigned)(G - 1)));
+      if (p2 >= hx)
+        G = hx;
+      else if (hx % p2 == 0)
+        G = p2;
     }
   }
   const int gsize = G * per_head;
