@@ -80,9 +80,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=80)
     ap.add_argument("--workload", default="train_causal")
-    ap.add_argument("--cpu-heads", type=int, default=64,
-                    help="(batch, head) pairs of the workload the CPU oracle baseline runs "
-                         "(0 = skip; the default, 64, is all of them: about 10 s on 16 threads)")
+    ap.add_argument("--cpu-heads", type=int, default=16,
+                    help="(batch, head) pairs of the workload whose forward+backward the CPU oracle "
+                         "baseline runs (0 = skip the CPU baseline; each workload's forward is also "
+                         "timed on a few pairs: about 20 s in all on 16 threads)")
     ap.add_argument("--no-sweep", action="store_true", help="skip the forward sweep over the other workloads")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-shaped calls")
     ap.add_argument("--no-bias", action="store_true", help="skip the additive-bias calls")
@@ -107,6 +108,47 @@ def time_calls(fn, n, stream):
     stop.record(stream)
     stop.synchronize()
     return start.elapsed_time(stop) / 1e3 / n
+
+
+def time_each(fn, n, stream):
+    """Durations (s) of n calls of fn(), each between its own pair of HIP
+    events on `stream` (recorded back to back). Returns them sorted."""
+    import torch
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    ev[-1][1].synchronize()
+    return sorted(a.elapsed_time(b) / 1e3 for a, b in ev)
+
+
+def cpu_info():
+    """The host CPU: model name, physical cores, logical CPUs and the CPUs
+    this process may run on."""
+    model, cores = None, set()
+    try:
+        phys = core = None
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                key, _, val = line.partition(":")
+                key, val = key.strip(), val.strip()
+                if key == "model name" and model is None:
+                    model = val
+                elif key == "physical id":
+                    phys = val
+                elif key == "core id":
+                    core = val
+                elif not key and phys is not None:
+                    cores.add((phys, core))
+                    phys = core = None
+            if phys is not None:
+                cores.add((phys, core))
+    except OSError:
+        pass
+    return {"model": model, "physical_cores": len(cores) or None, "logical_cpus": os.cpu_count(),
+            "cpus_available": len(os.sched_getaffinity(0))}
 
 
 def settle(fn, stream, seconds=0.1, max_calls=2000):
@@ -302,6 +344,59 @@ def fp8_leg(fa, si, torch, dev, stream):
     return out
 
 
+# (batch, head) pairs each workload's oracle forward is timed on (the
+# forward+backward of the step's workload takes --cpu-heads of its own).
+CPU_FWD_SAMPLE_HEADS = {"tiny": 2, "short_noncausal": 32, "short_causal": 32, "mid_causal": 8,
+                        "long_causal": 1, "train_causal": 8}
+
+
+def cpu_baseline_leg(args, w, bits, ff, bf, si):
+    """The fp64 oracle as it stands, timed on this host's cores: the step's
+    forward+backward on --cpu-heads (batch, head) pairs (the headline), and
+    per workload the forward alone on a few pairs (for the training workload
+    also the forward+backward, so the backward's share is their difference).
+    Each figure is also extrapolated to the whole workload."""
+    import oracle
+    from threadpoolctl import threadpool_info
+
+    def run(wl, b_, heads, backward):
+        x = {n: si.bf16_bits_to_f64(b_[n]) for n in (("q", "k", "v", "do") if backward else ("q", "k", "v"))}
+        pairs = [(i // wl.H, i % wl.H) for i in range(heads)]
+        t0 = time.perf_counter()
+        for b, h in pairs:
+            sl = (slice(b, b + 1), slice(None), slice(h, h + 1), slice(None))
+            if backward:
+                oracle.attention_backward(x["q"][sl], x["k"][sl], x["v"][sl], x["do"][sl], wl.causal, wl.scale)
+            else:
+                oracle.attention_forward(x["q"][sl], x["k"][sl], x["v"][sl], wl.causal, wl.scale)
+        return (time.perf_counter() - t0) / heads
+
+    heads = min(args.cpu_heads, w.B * w.H)
+    per_head_step = run(w, bits, heads, True)
+    threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    flops_head = (ff + bf) / (w.B * w.H)
+    per_config = {}
+    for name, wl in si.WORKLOADS.items():
+        n = min(CPU_FWD_SAMPLE_HEADS.get(name, 1), wl.B * wl.H)
+        b_ = bits if name == w.name else si.draw_workload(wl)
+        t = run(wl, b_, n, False)
+        f_head = fwd_flops(wl) / (wl.B * wl.H)
+        e = {"sample_heads": n, "heads": wl.B * wl.H, "fwd_s_per_head": round(t, 5),
+             "fwd_gflops": round(f_head / t / 1e9, 3), "fwd_s_whole_est": round(t * wl.B * wl.H, 2)}
+        if name == w.name:
+            tb = per_head_step - t
+            e.update({"fwd_bwd_sample_heads": heads, "fwd_bwd_s_per_head": round(per_head_step, 5),
+                      "bwd_s_per_head": round(tb, 5), "bwd_gflops": round(2.5 * f_head / tb / 1e9, 3),
+                      "bwd_s_whole_est": round(tb * wl.B * wl.H, 2)})
+        per_config[name] = e
+    return {"value": round(flops_head / per_head_step / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"fp64 oracle forward+backward of {heads} of the {w.B * w.H} (batch, head) pairs of "
+                      f"B={w.B} H={w.H} N={w.N} d={w.d} causal, {per_head_step * heads:.1f} s; NumPy/BLAS "
+                      f"with {threads} BLAS threads",
+            "cpu": cpu_info(), "per_config": per_config}
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -346,6 +441,10 @@ def main():
         fwd()
         bwd()
     torch.cuda.synchronize()
+    # However few warm-up steps were asked for, about 0.1 s of untimed steps
+    # follow, so that the timed window starts at a settled clock.
+    settle(lambda: (fwd(), bwd()), stream)
+    torch.cuda.synchronize()
 
     # Timed region: exactly K whole steps.
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
@@ -362,9 +461,11 @@ def main():
     wall = time.perf_counter() - t0
     fwd_each = sorted(e0.elapsed_time(e1) for e0, e1, _ in ev)  # ms per call
     bwd_each = sorted(e1.elapsed_time(e2) for _, e1, e2 in ev)
+    step_each = sorted(e0.elapsed_time(e2) for e0, _, e2 in ev)
     fwd_s = sum(fwd_each) / 1e3 / args.steps
     bwd_s = sum(bwd_each) / 1e3 / args.steps
-    step_s = ev[0][0].elapsed_time(ev[-1][2]) / 1e3 / args.steps
+    step_mean_s = ev[0][0].elapsed_time(ev[-1][2]) / 1e3 / args.steps
+    step_s = step_each[len(step_each) // 2] / 1e3  # the median step
     peak_mem = torch.cuda.max_memory_allocated()
 
     ff = fwd_flops(w)
@@ -394,6 +495,9 @@ def main():
         "fwd_tflops": round(ff / fwd_s / 1e12, 2),
         "bwd_tflops": round(bf / bwd_s / 1e12, 2),
         "fwd_frac_of_peak": round(ff / fwd_s / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "ms_per_step_mean": round(step_mean_s * 1e3, 4),
+        "ms_per_step_min": round(step_each[0], 4),
+        "value_from_mean_step": round((ff + bf) / step_mean_s / 1e12, 2),
         "wall_s_timed_region": round(wall, 4),
         "resident_bytes": int(resident),
         "peak_bytes_during_steps": int(peak_mem),
@@ -420,10 +524,14 @@ def main():
             time_calls(call, settle_calls(fwd_flops(wl)), stream)
             reps = 50 if wl.N * wl.N * wl.B * wl.H < (1 << 30) else 10
             s = time_calls(call, reps, stream)
+            each = time_each(call, reps, stream)
+            med = each[len(each) // 2]
             tf = fwd_flops(wl) / s / 1e12
             sweep[name] = {"B": wl.B, "H": wl.H, "N": wl.N, "d": wl.d, "causal": wl.causal,
                            "fwd_ms": round(s * 1e3, 4), "fwd_tflops": round(tf, 2),
-                           "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+                           "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                           "fwd_ms_median": round(med * 1e3, 4), "fwd_ms_min": round(each[0] * 1e3, 4),
+                           "frac_of_peak_median": round(fwd_flops(wl) / med / 1e12 / PEAK_BF16_TFLOPS, 4)}
             if wl.d == 64 and wl.N <= 512 and wl.B * wl.H >= 256:
                 # Short sequences are bound by memory traffic (Q, K, V in, O and the
                 # logsumexp out), so they are also timed with the caches flushed:
@@ -444,23 +552,7 @@ def main():
 
     cpu = None
     if args.cpu_heads > 0:
-        import oracle
-        from threadpoolctl import threadpool_info
-
-        heads = min(args.cpu_heads, w.B * w.H)
-        sel = [(i // w.H, i % w.H) for i in range(heads)]
-        q64, k64, v64, do64 = (si.bf16_bits_to_f64(bits[n]) for n in ("q", "k", "v", "do"))
-        t1 = time.perf_counter()
-        for b, h in sel:
-            sl = (slice(b, b + 1), slice(None), slice(h, h + 1), slice(None))
-            oracle.attention_backward(q64[sl], k64[sl], v64[sl], do64[sl], w.causal, w.scale)
-        cpu_s = time.perf_counter() - t1
-        per_head = (ff + bf) / (w.B * w.H)
-        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
-        cpu = {"value": round(per_head * heads / cpu_s / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
-               "kind": "oracle",
-               "sample": f"fp64 oracle forward+backward of {heads} of the {w.B * w.H} (batch, head) pairs "
-                         f"of B={w.B} H={w.H} N={w.N} d={w.d} causal; {cpu_s:.1f} s"}
+        cpu = cpu_baseline_leg(args, w, bits, ff, bf, si)
 
     line = {
         "metric": "attention fwd/bwd TFLOP/s at 1 MI355X; % of bf16 MFMA peak",

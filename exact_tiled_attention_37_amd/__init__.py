@@ -135,6 +135,18 @@ def _check_lse(t, B, N, H):
         raise ValueError(f"lse must be a contiguous float32 device tensor of shape {(B, H, N)}")
 
 
+def _check_workspace(ws, need: int, device):
+    """A caller-supplied workspace: a contiguous uint8 device tensor on
+    `device` with at least `need` bytes (the kernels write through its
+    pointer, so a host tensor would fault the GPU)."""
+    import torch
+
+    if ws.dtype != torch.uint8 or not ws.is_cuda or ws.device != device or not ws.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous uint8 tensor on {device}")
+    if ws.numel() < need:
+        raise ValueError(f"workspace holds {ws.numel()} bytes, {need} are needed")
+
+
 def _stream_handle(device) -> int:
     import torch
 
@@ -184,6 +196,7 @@ def fa_bwd(q, k, v, o, lse, do, causal: bool, softmax_scale: Optional[float] = N
     need = fa_bwd_workspace_bytes(B, N, H, d)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check_workspace(workspace, need, q.device)
     st = load_library().fa_bwd(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
         dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), workspace.numel(),
@@ -282,6 +295,8 @@ def fa_decode(q, k, v, causal: bool, softmax_scale: Optional[float] = None, out=
     need = fa_decode_workspace_bytes(B, Nq, Nk, H, d)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        _check_workspace(workspace, need, q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = load_library().fa_decode(
@@ -370,9 +385,12 @@ def fa_bwd_bias(q, k, v, bias, o, lse, do, causal: bool, softmax_scale: Optional
         if (dbias.dtype != torch.bfloat16 or tuple(dbias.shape) != (B, H, N, N) or dbias.stride(3) != 1
                 or dbias.stride(1) != N * dbias.stride(2) or dbias.stride(0) != H * N * dbias.stride(2)):
             raise ValueError("dbias must be a bf16 [B, H, N, N] view with unit key stride and packed rows")
+        if not dbias.is_cuda or dbias.device != q.device:
+            raise ValueError(f"dbias must be a device tensor on {q.device}")
     need = fa_bwd_workspace_bytes(B, N, H, d)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check_workspace(workspace, need, q.device)
     st = load_library().fa_bwd_bias(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), bp, sb, sh, sr, o.data_ptr(), lse.data_ptr(), do.data_ptr(),
         dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), dbias.data_ptr() if dbias is not None else None,

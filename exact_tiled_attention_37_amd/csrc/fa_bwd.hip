@@ -35,10 +35,13 @@
 // synchronisation, and dQ comes out deterministic.
 //
 // Rows past the end of the sequence are read as zeros (buffer range check).
-// They then contribute nothing: a zero Q or dO row makes that row's terms of
-// dK and dV vanish, and a zero K row makes its term of dQ vanish; outputs of
-// such rows are not stored. Causal: only blocks at or below the diagonal are
-// visited, waves skip fully masked blocks, only diagonal blocks are masked.
+// A zero Q or dO row makes that row's terms of dK and dV vanish (its
+// recomputed probabilities stay finite: its scores and row terms are 0);
+// keys past the end are masked in the dQ kernel's ragged last tile, since a
+// probability recomputed from a zero score and a very negative logsumexp can
+// overflow. Outputs of such rows are not stored. Causal: only blocks at or
+// below the diagonal are visited, waves skip fully masked blocks, only
+// diagonal blocks and the ragged end are masked.
 // A negative scale is handled by negating the register-resident operand (K
 // in dK/dV, Q in dQ) so that the scores keep the caller's sign.
 
@@ -476,9 +479,13 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
           else
             p = fast_exp2(__builtin_fmaf(s[r], c2, -l2));
           if constexpr (MASK) {
+            // Keys past N are masked explicitly: their K and V rows read as
+            // zero, but exp2(0 - L * log2e) overflows to +inf for a row whose
+            // logsumexp is below about -88, and inf * 0 in the dQ product
+            // would turn the row into NaN (with a bias their bias is row
+            // padding as well).
             const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-            // with a bias, keys past N are masked too (their bias is row padding)
-            p = ((CAUSAL && key > myq) || (BIAS && key >= N)) ? 0.f : p;
+            p = ((CAUSAL && key > myq) || key >= N) ? 0.f : p;
           }
           x[s8] = p * (dp[r] - dd);
         }
@@ -510,11 +517,10 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   };
 
   // Causal: tiles from jm on straddle the diagonal (masked); earlier tiles
-  // need no mask. Keys past N need none: their K and V rows read as zero.
+  // need no mask. A ragged last tile (keys past N) runs the masked variant.
   const int kv_len = CAUSAL ? min(N, (qblk + 1) * kQBlock) : N;
   const int ntiles = (kv_len + kKTile - 1) / kKTile;
-  // (with a bias a ragged last tile runs the masked variant: see above)
-  const int jm = CAUSAL ? qblk * (kQBlock / kKTile) : (BIAS ? N / kKTile : ntiles);
+  const int jm = CAUSAL ? min(qblk * (kQBlock / kKTile), N / kKTile) : N / kKTile;
   // Tile j lives in stage j % 2; single-exit loops as in the dK/dV kernel.
   issue(0, kvbuf[0]);
   wait_vmem();
@@ -532,7 +538,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
     if constexpr (BIAS) bias_issue(j);
     kv_prefetched = j + 1 < ntiles;
     if (kv_prefetched) issue(j + 1, kvbuf[(j + 1) & 1]);
-    compute(j, kvbuf[j & 1], std::integral_constant<bool, CAUSAL || BIAS>{});
+    compute(j, kvbuf[j & 1], std::true_type{});
     wait_vmem();
     __syncthreads();
   }

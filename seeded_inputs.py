@@ -219,3 +219,16 @@ def draw_fp8(B: int, N: int, H: int, d: int, seed: int):
         out[name + "_descale"] = desc
     return out
 
+
+def draw_negative_logsumexp(B: int, N: int, H: int, d: int, seed: int):
+    """Q, K, V, dO bits whose scores all sit far below zero: queries are
+    -4 + 0.5 z and keys 4 + 0.5 z in every column (z standard normal), so a
+    score is about -16 d times the softmax scale and every row's logsumexp
+    lies far below -88 (where exp of its negative overflows float32). V and
+    dO are standard normal. One PCG64 stream, draws in the order Q, K, V, dO."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    q = -4.0 + 0.5 * rng.standard_normal((B, N, H, d), dtype=np.float32)
+    k = 4.0 + 0.5 * rng.standard_normal((B, N, H, d), dtype=np.float32)
+    v = rng.standard_normal((B, N, H, d), dtype=np.float32)
+    do = rng.standard_normal((B, N, H, d), dtype=np.float32)
+    return {n: f32_to_bf16_bits(x) for n, x in zip(("q", "k", "v", "do"), (q, k, v, do))}

@@ -12,18 +12,27 @@ the output (2^-9 |O|, taken as 2^-8 |O|).
 import numpy as np
 
 
-def head_bound(q, k, v, causal, scale, rows=None):
+def head_bound(q, k, v, causal, scale, rows=None, chunk=2048):
     """Reference rows of one head (fp64 dequantized q, k, v [N, d]) and the
-    per-element error bound. Returns (O_ref [R, d], L_ref [R], bound [R, d])."""
+    per-element error bound, in chunks of `chunk` query rows (each holds
+    whole rows of scores). Returns (O_ref [R, d], L_ref [R], bound [R, d])."""
     N = k.shape[0]
     rows = np.arange(N) if rows is None else np.asarray(rows)
-    s = scale * (q[rows] @ k.T)
-    if causal:
-        s = np.where(np.arange(N)[None, :] > rows[:, None], -np.inf, s)
-    m = s.max(axis=1, keepdims=True)
-    p = np.exp(s - m)
-    l = p.sum(axis=1, keepdims=True)
-    o = (p @ v) / l
-    w = np.where(p > 0, np.maximum(p * 2.0 ** -4, 2.0 ** -14), 0.0)
-    bound = (w @ np.abs(v)) / l + 2.0 ** -8 * np.abs(o) + 1e-6
-    return o, (m + np.log(l))[:, 0], bound
+    o = np.empty((rows.size, v.shape[1]))
+    lse = np.empty(rows.size)
+    bound = np.empty((rows.size, v.shape[1]))
+    av = np.abs(v)
+    for c0 in range(0, rows.size, chunk):
+        rr = rows[c0 : c0 + chunk]
+        s = scale * (q[rr] @ k.T)
+        if causal:
+            s = np.where(np.arange(N)[None, :] > rr[:, None], -np.inf, s)
+        m = s.max(axis=1, keepdims=True)
+        p = np.exp(s - m)
+        l = p.sum(axis=1, keepdims=True)
+        oc = (p @ v) / l
+        w = np.where(p > 0, np.maximum(p * 2.0 ** -4, 2.0 ** -14), 0.0)
+        o[c0 : c0 + chunk] = oc
+        lse[c0 : c0 + chunk] = (m + np.log(l))[:, 0]
+        bound[c0 : c0 + chunk] = (w @ av) / l + 2.0 ** -8 * np.abs(oc) + 1e-6
+    return o, lse, bound

@@ -287,3 +287,16 @@ def test_fp8_errors(lib):
     assert fp8(lib, scale=float("nan")) == FA_ERR_SCALE
     assert fp8(lib, q=P + 8) == FA_ERR_ALIGN
     assert fp8(lib, kd=P + 2) == FA_ERR_ALIGN
+
+
+def test_binding_rejects_host_or_mistyped_workspace():
+    """A caller-supplied workspace must be a contiguous uint8 tensor on the
+    calling device with enough bytes; a host tensor (whose pointer the
+    kernels would write through) is refused before anything is launched."""
+    import torch
+
+    dev = torch.device("cuda", 0)
+    with pytest.raises(ValueError, match="workspace"):
+        fa._check_workspace(torch.empty(1024, dtype=torch.uint8), 512, dev)  # host memory
+    with pytest.raises(ValueError, match="workspace"):
+        fa._check_workspace(torch.empty(1024, dtype=torch.float32), 512, dev)  # not bytes

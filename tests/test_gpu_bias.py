@@ -200,24 +200,36 @@ def test_bias_causal_zero_fill():
 
 @pytest.mark.parametrize("name", list(si.BIAS_WORKLOADS))
 def test_bias_workload(name):
-    """The bias workload at full size (as the benchmark runs it); sampled
-    (batch, head) pairs are checked whole against the oracle."""
-    import torch
+    """The bias workload at full size (as the benchmark runs it): O, LSE,
+    dQ, dK, dV and dBias of every (batch, head) against the oracle (run head
+    by head in a thread pool)."""
+    from tests import oracle_heads as oh
 
     w = si.BIAS_WORKLOADS[name]
     announce(f"bias workload {name}: B={w.B} H={w.H} N={w.N} d={w.d} causal={w.causal}")
     bits = si.draw_with_bias(w.B, w.N, w.H, w.d, w.seed)
     out = run_case(bits, bits["bias"], w.causal, w.scale)
     got = {k: f64(v) for k, v in out.items()}
-    for b, h in ((0, 0), (w.B - 1, w.H - 1)):
-        sl = (slice(b, b + 1), slice(None), slice(h, h + 1), slice(None))
-        ref = oracle.attention_backward_bias(*(si.bf16_bits_to_f64(bits[n][sl]) for n in ("q", "k", "v")),
-                                             si.bf16_bits_to_f64(bits["bias"][b:b + 1, h:h + 1]),
-                                             si.bf16_bits_to_f64(bits["do"][sl]), w.causal, w.scale)
-        rq, rk, rv, rdb, ro, rl, _ = ref
-        check(f"O[{b},{h}]", got["o"][sl], ro)
-        check(f"LSE[{b},{h}]", got["lse"][b:b + 1, h:h + 1], rl, LSE_TOL, LSE_TOL)
-        check(f"dQ[{b},{h}]", got["dq"][sl], rq)
-        check(f"dK[{b},{h}]", got["dk"][sl], rk)
-        check(f"dV[{b},{h}]", got["dv"][sl], rv)
-        check_scaled(f"dBias[{b},{h}]", got["dbias"][b:b + 1, h:h + 1], rdb)
+    x = {n: si.bf16_bits_to_f64(bits[n]) for n in ("q", "k", "v", "do")}
+    bias = si.bf16_bits_to_f64(bits["bias"])
+    H = oh.head
+
+    def one(b, h):
+        rq, rk, rv, rdb, ro, rl, _ = oracle.attention_backward_bias(
+            H(x["q"], b, h), H(x["k"], b, h), H(x["v"], b, h), bias[b:b + 1, h:h + 1], H(x["do"], b, h),
+            w.causal, w.scale)
+        # dBias [1, 1, N, N] travels as a [1, N, 1, N] slice
+        return rq, rk, rv, ro, rl, rdb.transpose(0, 2, 1, 3)
+
+    rq, rk, rv, ro, rl, rdb = oh.by_head(one, w.B, w.H, ("bnhd", "bnhd", "bnhd", "bnhd", "bhn", "bnhd"))
+    rdb = rdb.transpose(0, 2, 1, 3)
+    for nm, g, r in (("O", got["o"], ro), ("dQ", got["dq"], rq), ("dK", got["dk"], rk), ("dV", got["dv"], rv),
+                     ("dBias", got["dbias"], rdb), ("LSE", got["lse"], rl)):
+        err = np.abs(g - r)
+        announce(f"[parity] {name} {nm}: max-abs {err.max():.3e} mean-abs {err.mean():.3e} over {err.size} elements")
+    check("O", got["o"], ro)
+    check("LSE", got["lse"], rl, LSE_TOL, LSE_TOL)
+    check("dQ", got["dq"], rq)
+    check("dK", got["dk"], rk)
+    check("dV", got["dv"], rv)
+    check_scaled("dBias", got["dbias"], rdb)

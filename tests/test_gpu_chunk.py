@@ -175,14 +175,17 @@ def test_merge_against_oracle(d, case):
 
 # One rank's share of the long sequence split over 8 ranks: 2048 query rows
 # at global position r * 2048 against the 2048-key chunks 0..r (causal),
-# merged. Sampled rows are compared with full causal attention over all
-# 16384 keys.
+# merged. Every row of every head is compared with full causal attention
+# over all 16384 keys (the oracle's chunk attention of the rank's rows over
+# the whole key sequence, at their global positions).
 RING_RANKS = 8
 
 
 @pytest.mark.parametrize("rank", [7, 2])
 def test_ring_rank_workload(rank):
     import torch
+
+    from tests import oracle_heads as oh
 
     w = si.WORKLOADS["long_causal"]
     n = w.N // RING_RANKS
@@ -198,11 +201,16 @@ def test_ring_rank_workload(rank):
     o, lse = fa.fa_merge(torch.stack([p[0] for p in parts]).contiguous(),
                          torch.stack([p[1] for p in parts]).contiguous())
     torch.cuda.synchronize()
-    rng = np.random.Generator(np.random.PCG64(9000 + rank))
-    rows = np.sort(rng.choice(n, size=12, replace=False))
-    rows[0] = 0
-    for h in (0, 9):
-        qh, kh, vh = (si.bf16_bits_to_f64(bits[t][:, :, h:h + 1]) for t in ("q", "k", "v"))
-        ro, rl = oracle.attention_forward_rows(qh, kh, vh, True, w.scale, 0, 0, rank * n + rows)
-        check(f"ring O h={h}", f64(o[0, rows, h]), ro)
-        check(f"ring LSE h={h}", f64(lse[0, h, rows]), rl, LSE_TOL, LSE_TOL)
+    o, lse = f64(o), f64(lse)
+    del q, k, v, qc, parts
+    x = {t: si.bf16_bits_to_f64(bits[t]) for t in ("q", "k", "v")}
+    qrows = x["q"][:, rank * n:(rank + 1) * n]
+    H = oh.head
+    ro, rl = oh.by_head(lambda b, h: oracle.attention_forward_chunk(H(qrows, b, h), H(x["k"], b, h),
+                                                                    H(x["v"], b, h), True, w.scale, rank * n, 0),
+                        w.B, w.H, ("bnhd", "bhn"))
+    err = np.abs(o - ro)
+    announce(f"[parity] ring rank {rank} O: max-abs {err.max():.3e} mean-abs {err.mean():.3e} over {err.size} "
+             f"elements; LSE max-abs {np.abs(lse - rl).max():.3e}")
+    check("ring O", o, ro)
+    check("ring LSE", lse, rl, LSE_TOL, LSE_TOL)

@@ -133,9 +133,11 @@ def test_decode_matches_prefill_rows():
 
 @pytest.mark.parametrize("name", list(si.DECODE_WORKLOADS))
 def test_decode_workloads(name):
-    """The decode workloads at full size, as the benchmark runs them;
-    sampled (batch, head) pairs are checked whole against the oracle."""
+    """The decode workloads at full size, as the benchmark runs them: every
+    (batch, head) against the oracle (run head by head in a thread pool)."""
     import torch
+
+    from tests import oracle_heads as oh
 
     w = si.DECODE_WORKLOADS[name]
     announce(f"decode workload {name}: B={w.B} H={w.H} Nq={w.Nq} Nk={w.Nk} d={w.d}")
@@ -143,8 +145,11 @@ def test_decode_workloads(name):
     o, lse = fa.fa_decode(dev(bits["q"]), dev(bits["k"]), dev(bits["v"]), w.causal, w.scale)
     torch.cuda.synchronize()
     o, lse = f64(o), f64(lse)
-    for b, h in ((0, 0), (w.B - 1, w.H - 1), (w.B // 2, 5)):
-        sl = (slice(b, b + 1), slice(None), slice(h, h + 1), slice(None))
-        ro, rl = oracle.attention_decode(*(si.bf16_bits_to_f64(bits[t][sl]) for t in ("q", "k", "v")),
-                                         w.causal, w.scale)
-        check_out(o[sl], lse[b:b + 1, h:h + 1], ro, rl)
+    x = {t: si.bf16_bits_to_f64(bits[t]) for t in ("q", "k", "v")}
+    H = oh.head
+    ro, rl = oh.by_head(lambda b, h: oracle.attention_decode(H(x["q"], b, h), H(x["k"], b, h), H(x["v"], b, h),
+                                                             w.causal, w.scale), w.B, w.H, ("bnhd", "bhn"))
+    err = np.abs(o - ro)
+    announce(f"[parity] {name} O: max-abs {err.max():.3e} mean-abs {err.mean():.3e} over {err.size} elements; "
+             f"LSE max-abs {np.abs(lse - rl).max():.3e}")
+    check_out(o, lse, ro, rl)
