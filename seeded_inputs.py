@@ -232,3 +232,20 @@ def draw_negative_logsumexp(B: int, N: int, H: int, d: int, seed: int):
     v = rng.standard_normal((B, N, H, d), dtype=np.float32)
     do = rng.standard_normal((B, N, H, d), dtype=np.float32)
     return {n: f32_to_bf16_bits(x) for n, x in zip(("q", "k", "v", "do"), (q, k, v, do))}
+
+
+BF16_NEG_INF = 0xFF80  # bfloat16 bits of -inf
+
+
+def draw_bias_with_holes(B: int, H: int, N: int, seed: int, holes: bool = True):
+    """A bf16 bias [B, H, N, N] of 1.5 z (z standard normal, PCG64(seed));
+    with holes, three -inf patterns: part of row 1 of (0, 0) removed, the
+    last row of (B-1, H-1) fully removed, and key 2 of (0, H-1) hidden from
+    every row."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    b = f32_to_bf16_bits((rng.standard_normal((B, H, N, N)) * 1.5).astype(np.float32))
+    if holes:
+        b[0, 0, min(1, N - 1), : max(1, N // 3)] = BF16_NEG_INF
+        b[-1, -1, N - 1, :] = BF16_NEG_INF
+        b[0, -1, :, min(2, N - 1)] = BF16_NEG_INF
+    return b

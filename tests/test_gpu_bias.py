@@ -20,6 +20,7 @@ import pytest
 import exact_tiled_attention_37_amd as fa
 import oracle
 import seeded_inputs as si
+from tests import parity_log
 
 pytestmark = pytest.mark.gpu
 
@@ -30,6 +31,12 @@ NEG_INF_BF16 = 0xFF80
 def announce(msg):
     sys.__stderr__.write(f"[gpu-case] {msg}\n")
     sys.__stderr__.flush()
+
+
+def report(msg):
+    """A whole-workload parity figure: printed now and in the session summary."""
+    announce(msg)
+    parity_log.record(msg)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -109,13 +116,7 @@ def compare(out, ref):
 
 
 def random_bias(B, H, N, seed, holes=True):
-    rng = np.random.Generator(np.random.PCG64(seed))
-    b = si.f32_to_bf16_bits((rng.standard_normal((B, H, N, N)) * 1.5).astype(np.float32))
-    if holes:
-        b[0, 0, min(1, N - 1), : max(1, N // 3)] = NEG_INF_BF16   # part of a row removed
-        b[-1, -1, N - 1, :] = NEG_INF_BF16                        # a row that sees nothing
-        b[0, -1, :, min(2, N - 1)] = NEG_INF_BF16                 # a key hidden from every row
-    return b
+    return si.draw_bias_with_holes(B, H, N, seed, holes)
 
 
 SMALL = [(1, 1, 1, 64), (1, 17, 2, 64), (2, 64, 2, 128), (1, 129, 3, 64), (1, 200, 2, 128), (2, 256, 1, 128)]
@@ -226,7 +227,7 @@ def test_bias_workload(name):
     for nm, g, r in (("O", got["o"], ro), ("dQ", got["dq"], rq), ("dK", got["dk"], rk), ("dV", got["dv"], rv),
                      ("dBias", got["dbias"], rdb), ("LSE", got["lse"], rl)):
         err = np.abs(g - r)
-        announce(f"[parity] {name} {nm}: max-abs {err.max():.3e} mean-abs {err.mean():.3e} over {err.size} elements")
+        report(f"[parity] {name} {nm}: max-abs {err.max():.3e} mean-abs {err.mean():.3e} over {err.size} elements")
     check("O", got["o"], ro)
     check("LSE", got["lse"], rl, LSE_TOL, LSE_TOL)
     check("dQ", got["dq"], rq)

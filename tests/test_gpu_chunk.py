@@ -16,6 +16,7 @@ import pytest
 import exact_tiled_attention_37_amd as fa
 import oracle
 import seeded_inputs as si
+from tests import parity_log
 
 pytestmark = pytest.mark.gpu
 
@@ -25,6 +26,12 @@ MAX_TOL, MEAN_TOL, LSE_TOL = 2e-2, 2e-3, 1e-3
 def announce(msg):
     sys.__stderr__.write(f"[gpu-case] {msg}\n")
     sys.__stderr__.flush()
+
+
+def report(msg):
+    """A whole-workload parity figure: printed now and in the session summary."""
+    announce(msg)
+    parity_log.record(msg)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -210,7 +217,7 @@ def test_ring_rank_workload(rank):
                                                                     H(x["v"], b, h), True, w.scale, rank * n, 0),
                         w.B, w.H, ("bnhd", "bhn"))
     err = np.abs(o - ro)
-    announce(f"[parity] ring rank {rank} O: max-abs {err.max():.3e} mean-abs {err.mean():.3e} over {err.size} "
+    report(f"[parity] ring rank {rank} O: max-abs {err.max():.3e} mean-abs {err.mean():.3e} over {err.size} "
              f"elements; LSE max-abs {np.abs(lse - rl).max():.3e}")
     check("ring O", o, ro)
     check("ring LSE", lse, rl, LSE_TOL, LSE_TOL)

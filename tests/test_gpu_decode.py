@@ -17,6 +17,7 @@ import pytest
 import exact_tiled_attention_37_amd as fa
 import oracle
 import seeded_inputs as si
+from tests import parity_log
 
 pytestmark = pytest.mark.gpu
 
@@ -26,6 +27,12 @@ MAX_TOL, MEAN_TOL, LSE_TOL = 2e-2, 2e-3, 1e-3
 def announce(msg):
     sys.__stderr__.write(f"[gpu-case] {msg}\n")
     sys.__stderr__.flush()
+
+
+def report(msg):
+    """A whole-workload parity figure: printed now and in the session summary."""
+    announce(msg)
+    parity_log.record(msg)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -150,6 +157,6 @@ def test_decode_workloads(name):
     ro, rl = oh.by_head(lambda b, h: oracle.attention_decode(H(x["q"], b, h), H(x["k"], b, h), H(x["v"], b, h),
                                                              w.causal, w.scale), w.B, w.H, ("bnhd", "bhn"))
     err = np.abs(o - ro)
-    announce(f"[parity] {name} O: max-abs {err.max():.3e} mean-abs {err.mean():.3e} over {err.size} elements; "
+    report(f"[parity] {name} O: max-abs {err.max():.3e} mean-abs {err.mean():.3e} over {err.size} elements; "
              f"LSE max-abs {np.abs(lse - rl).max():.3e}")
     check_out(o, lse, ro, rl)

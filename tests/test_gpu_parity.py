@@ -17,6 +17,8 @@ import pytest
 import exact_tiled_attention_37_amd as fa
 import oracle
 import seeded_inputs as si
+from tests import parity_log
+from tests import kernel_rounding as kr
 from tests import oracle_heads as oh
 
 pytestmark = pytest.mark.gpu
@@ -27,6 +29,12 @@ MAX_TOL, MEAN_TOL, LSE_TOL = 2e-2, 2e-3, 1e-3
 def announce(msg):
     sys.__stderr__.write(f"[gpu-case] {msg}\n")
     sys.__stderr__.flush()
+
+
+def report(msg):
+    """A whole-workload parity figure: printed now and in the session summary."""
+    announce(msg)
+    parity_log.record(msg)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -134,14 +142,29 @@ def test_other_scales(scale, d):
         check_rel("dV", f64(dv), rv)
 
 
+# A derived bound may exceed the rounding model's own error by this factor
+# (what the model leaves out: fp32 accumulation order, the running maximum's
+# lag moving rounding boundaries).
+MODEL_MARGIN = 1.5
+
+
 @pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
 @pytest.mark.parametrize("d", [64, 128])
 def test_very_negative_logsumexp_ragged_keys(d, causal):
     """Rows whose logsumexp is below -88 with a ragged last key tile (N = 100):
     a padded key's recomputed probability exp(0 - L) overflows float32, so
     the backward must mask keys past N rather than rely on their zero rows
-    (0 * inf is NaN). Gradients reach |dK| ~ 9, where bf16 output rounding
-    alone exceeds 2e-2, so they take the magnitude-scaled bound."""
+    (0 * inf is NaN). Every key shares a large component along -q and all
+    queries favour the same keys, so rounding errors add up coherently: the
+    bf16 roundings alone exceed the plain gradient bounds
+    (tests/test_rounding_bounds.py). The backward is therefore given the
+    oracle's O (rounded to bf16) and logsumexp, so that its own roundings are
+    the only error left, and each gradient is held to the larger of the
+    magnitude-scaled bound and MODEL_MARGIN times the error of the fp64
+    rounding model (tests/kernel_rounding.py) given the same O. The forward's
+    O and logsumexp are checked against the plain bounds."""
+    import torch
+
     B, N, H = 1, 100, 2
     scale = 1.0 / 8.0
     announce(f"very negative logsumexp d={d} causal={causal}")
@@ -152,10 +175,18 @@ def test_very_negative_logsumexp_ragged_keys(d, causal):
     q, k, v, o, lse = gpu_fwd(bits, causal, scale)
     check("O", f64(o), ro)
     check("LSE", f64(lse), rl, LSE_TOL, LSE_TOL)
-    dq, dk, dv = gpu_bwd(q, k, v, o, lse, bits["do"], causal, scale)
-    check_rel("dQ", f64(dq), rq)
-    check_rel("dK", f64(dk), rk)
-    check_rel("dV", f64(dv), rv)
+    o_bits = si.f32_to_bf16_bits(ro.astype(np.float32))
+    model = kr.emulate(q64, k64, v64, do64, causal, scale, o_in=si.bf16_bits_to_f64(o_bits))
+    o_in = dev(o_bits)
+    lse_in = torch.from_numpy(rl.astype(np.float32)).cuda()
+    dq, dk, dv = gpu_bwd(q, k, v, o_in, lse_in, bits["do"], causal, scale)
+    for name, got, ref in (("dQ", f64(dq), rq), ("dK", f64(dk), rk), ("dV", f64(dv), rv)):
+        mmax, mmean = kr.error(model[name.lower()], ref)
+        m = max(1.0, float(np.max(np.abs(ref))) / 2.0)
+        gmax, gmean = kr.error(got, ref)
+        report(f"[parity] negative-logsumexp d={d} causal={causal} {name}: max-abs {gmax:.3e} "
+               f"(model {mmax:.3e}), mean-abs {gmean:.3e} (model {mmean:.3e})")
+        check(name, got, ref, max(MAX_TOL * m, MODEL_MARGIN * mmax), max(MEAN_TOL * m, MODEL_MARGIN * mmean))
 
 
 # ---------------------------------------------------------------------------
@@ -245,7 +276,7 @@ def check_whole(name, got, ref, max_tol=MAX_TOL, mean_tol=MEAN_TOL, floor=True):
     (and the bf16 floor of the exact result) first."""
     err = np.abs(np.asarray(got, dtype=np.float64) - ref)
     fl = f", bf16 floor {bf16_floor(ref):.3e}" if floor else ""
-    announce(f"[parity] {name}: max-abs {err.max():.3e} mean-abs {err.mean():.3e}{fl} over {err.size} elements")
+    report(f"[parity] {name}: max-abs {err.max():.3e} mean-abs {err.mean():.3e}{fl} over {err.size} elements")
     check(name, got, ref, max_tol, mean_tol)
 
 
