@@ -30,6 +30,7 @@ __all__ = [
     "fa_merge",
     "fa_decode",
     "fa_decode_workspace_bytes",
+    "fa_decode_noalloc",
     "fa_fwd_bias",
     "fa_bwd_bias",
     "fa_fwd_fp8",
@@ -41,8 +42,8 @@ __all__ = [
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libfa_mi355x.so"
 EXPORTED_SYMBOLS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd_chunk", "fa_merge", "fa_decode",
-                    "fa_decode_workspace_bytes", "fa_fwd_bias", "fa_bwd_bias", "fa_fwd_fp8", "fa_status_string",
-                    "fa_version")
+                    "fa_decode_workspace_bytes", "fa_decode_noalloc", "fa_fwd_bias", "fa_bwd_bias", "fa_fwd_fp8",
+                    "fa_status_string", "fa_version")
 
 _lib = None
 
@@ -85,6 +86,8 @@ def load_library():
     lib.fa_decode.restype = i
     lib.fa_decode_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.fa_decode_workspace_bytes.restype = sz
+    lib.fa_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
+    lib.fa_decode_noalloc.restype = i
     lib.fa_fwd_bias.argtypes = [vp, vp, vp, vp, ll, ll, i, vp, vp, i, i, i, i, i, f, vp]
     lib.fa_fwd_bias.restype = i
     lib.fa_bwd_bias.argtypes = [vp, vp, vp, vp, ll, ll, i, vp, vp, vp, vp, vp, vp, vp, i, vp, sz, i, i, i, i, i, f, vp]
@@ -305,6 +308,37 @@ def fa_decode(q, k, v, causal: bool, softmax_scale: Optional[float] = None, out=
     )
     if st != 0:
         raise FaError(st, "fa_decode")
+    return out, lse
+
+
+def fa_decode_noalloc(q, k, v, causal: bool, softmax_scale: Optional[float] = None, out=None, lse=None):
+    """fa_decode without a workspace: the library keeps the key-split partial
+    results in its own static device scratch (32 MiB per device), so the call
+    allocates nothing when out and lse are given. Calls that may overlap on
+    one device must not be issued (they share that scratch). Returns
+    (o bf16 [B, Nq, H, d], lse float32 [B, H, Nq])."""
+    import torch
+
+    _check_bnhd("q", q)
+    B, Nq, H, d = q.shape
+    _check_bnhd("k", k)
+    Nk = k.shape[1]
+    if k.shape[0] != B or tuple(k.shape[2:]) != (H, d):
+        raise ValueError(f"k has shape {tuple(k.shape)}, expected [{B}, Nk, {H}, {d}]")
+    _check_bnhd("v", v, k.shape)
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        out = torch.empty_like(q)
+    _check_bnhd("out", out, q.shape)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    _check_lse(lse, B, Nq, H)
+    st = load_library().fa_decode_noalloc(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, Nq, Nk, H, d,
+        int(bool(causal)), scale, _stream_handle(q.device),
+    )
+    if st != 0:
+        raise FaError(st, "fa_decode_noalloc")
     return out, lse
 
 

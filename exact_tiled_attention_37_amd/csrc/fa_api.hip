@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "fa.h"
 #include "fa_launch.hpp"
@@ -55,6 +56,71 @@ fa_status dispatch(int d, int causal, F&& f) {
     e = causal ? f(std::integral_constant<int, 128>{}, std::true_type{})
                : f(std::integral_constant<int, 128>{}, std::false_type{});
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // namespace
+
+// Scratch of fa_decode_noalloc: the key-split partial results of a decode
+// call, in place of a caller-supplied workspace. Every device the library
+// runs on holds its own copy from module load until the process ends. Host
+// code never uses the array's name as an address: the device address comes
+// from hipGetSymbolAddress, taken once per device (with that device current)
+// and kept in g_scratch.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+namespace {
+
+// Validation shared by fa_decode and fa_decode_noalloc; on FA_OK *need holds
+// the workspace bytes of the call.
+fa_status check_decode(const void* q, const void* k, const void* v, const void* o, const float* lse, int B,
+                       int Nq, int Nk, int H, int d, float softmax_scale, size_t* need) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if (B < 1 || Nq < 1 || Nk < 1 || H < 1) return FA_ERR_SHAPE;
+  fa_status st = check_shape(B, Nq, H, d);
+  if (st != FA_OK || (st = check_shape(B, Nk, H, d)) != FA_OK) return st;
+  if (!std::isfinite(softmax_scale)) return FA_ERR_SCALE;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
+    return FA_ERR_ALIGN;
+  *need = fa::decode_workspace_bytes(B, Nq, Nk, H, d);
+  return FA_OK;
+}
+
+fa_status launch_decode_checked(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Nq,
+                                int Nk, int H, int d, int causal, float softmax_scale, void* workspace,
+                                hipStream_t stream) {
+  (void)hipGetLastError();
+  // The queries are the last Nq positions: key j is visible to query i iff
+  // j <= i + Nk - Nq (clamped as in fa_fwd_chunk; a single query sees all).
+  int delta = 0;
+  if (causal) {
+    const long long dl = (long long)Nk - Nq;
+    if (dl >= (long long)Nk - 1)
+      causal = 0;
+    else
+      delta = (int)(dl < -(long long)Nq ? -(long long)Nq : dl);
+  }
+  const fa::DecodeArgs a{q, k, v, o, lse, static_cast<float*>(workspace), B, Nq, Nk, H, delta, softmax_scale, stream};
+  return dispatch(d, causal, [&](auto D, auto C) { return fa::launch_decode<decltype(D)::value, decltype(C)::value>(a); });
+}
+
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];
+
+// This device's address of `scratch` (looked up on the first call per device).
+fa_status scratch_address(void** ptr) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return FA_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return FA_ERR_HIP;
+    g_scratch[dev] = p;
+  }
+  *ptr = g_scratch[dev];
+  return FA_OK;
 }
 
 }  // namespace
@@ -203,32 +269,27 @@ size_t fa_decode_workspace_bytes(int B, int Nq, int Nk, int H, int d) {
 fa_status fa_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Nq, int Nk,
                     int H, int d, int causal, float softmax_scale, void* workspace, size_t workspace_bytes,
                     hipStream_t stream) {
-  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
-  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
-  if (B < 1 || Nq < 1 || Nk < 1 || H < 1) return FA_ERR_SHAPE;
-  fa_status st = check_shape(B, Nq, H, d);
-  if (st != FA_OK || (st = check_shape(B, Nk, H, d)) != FA_OK) return st;
-  if (!std::isfinite(softmax_scale)) return FA_ERR_SCALE;
-  const size_t need = fa::decode_workspace_bytes(B, Nq, Nk, H, d);
+  size_t need = 0;
+  fa_status st = check_decode(q, k, v, o, lse, B, Nq, Nk, H, d, softmax_scale, &need);
+  if (st != FA_OK) return st;
   if (need > 0 && (!workspace || workspace_bytes < need)) return FA_ERR_WORKSPACE;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4) ||
-      (need > 0 && !aligned(workspace, 256)))
-    return FA_ERR_ALIGN;
+  if (need > 0 && !aligned(workspace, 256)) return FA_ERR_ALIGN;
   st = check_device();
   if (st != FA_OK) return st;
-  (void)hipGetLastError();
-  // The queries are the last Nq positions: key j is visible to query i iff
-  // j <= i + Nk - Nq (clamped as in fa_fwd_chunk; a single query sees all).
-  int delta = 0;
-  if (causal) {
-    const long long dl = (long long)Nk - Nq;
-    if (dl >= (long long)Nk - 1)
-      causal = 0;
-    else
-      delta = (int)(dl < -(long long)Nq ? -(long long)Nq : dl);
-  }
-  const fa::DecodeArgs a{q, k, v, o, lse, static_cast<float*>(workspace), B, Nq, Nk, H, delta, softmax_scale, stream};
-  return dispatch(d, causal, [&](auto D, auto C) { return fa::launch_decode<decltype(D)::value, decltype(C)::value>(a); });
+  return launch_decode_checked(q, k, v, o, lse, B, Nq, Nk, H, d, causal, softmax_scale, workspace, stream);
+}
+
+fa_status fa_decode_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Nq,
+                            int Nk, int H, int d, int causal, float softmax_scale, hipStream_t stream) {
+  size_t need = 0;
+  fa_status st = check_decode(q, k, v, o, lse, B, Nq, Nk, H, d, softmax_scale, &need);
+  if (st != FA_OK) return st;
+  if (need > kScratchBytes) return FA_ERR_SCRATCH;
+  st = check_device();
+  if (st != FA_OK) return st;
+  void* ws = nullptr;
+  if (need > 0 && (st = scratch_address(&ws)) != FA_OK) return st;
+  return launch_decode_checked(q, k, v, o, lse, B, Nq, Nk, H, d, causal, softmax_scale, ws, stream);
 }
 
 fa_status fa_merge(const float* o_parts, const float* lse_parts, int C, void* o, float* lse, int B, int N,
@@ -286,6 +347,7 @@ const char* fa_status_string(fa_status status) {
     case FA_ERR_WORKSPACE: return "workspace missing or smaller than fa_bwd_workspace_bytes()";
     case FA_ERR_HIP: return "a HIP runtime call or kernel launch failed";
     case FA_ERR_DEVICE: return "the current device is not a gfx950 (MI355X) GPU";
+    case FA_ERR_SCRATCH: return "the call needs more scratch than fa_decode_noalloc holds (32 MiB): use fa_decode";
   }
   return "unknown status";
 }

@@ -57,7 +57,9 @@ typedef enum fa_status {
     FA_ERR_SCALE = 5,     /* softmax_scale is not finite                        */
     FA_ERR_WORKSPACE = 6, /* workspace missing or smaller than required         */
     FA_ERR_HIP = 7,       /* a HIP runtime call or kernel launch failed         */
-    FA_ERR_DEVICE = 8     /* the current device is not a gfx950 (MI355X) GPU    */
+    FA_ERR_DEVICE = 8,    /* the current device is not a gfx950 (MI355X) GPU    */
+    FA_ERR_SCRATCH = 9    /* fa_decode_noalloc: the call needs more scratch than
+                             the library's static scratch holds                 */
 } fa_status;
 
 /*
@@ -258,6 +260,29 @@ FA_API size_t fa_decode_workspace_bytes(int B, int Nq, int Nk, int H, int d);
 FA_API fa_status fa_decode(const void* q, const void* k, const void* v, void* o, float* lse,
                     int B, int Nq, int Nk, int H, int d, int causal, float softmax_scale,
                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * fa_decode without a workspace argument and without any allocation: for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc). It computes exactly
+ * what fa_decode computes, with the same kernels; the key-split partial
+ * results go to a static device array of the library (32 MiB, held by every
+ * device the library runs on from module load until the process ends)
+ * instead of a caller-supplied workspace.
+ *
+ *   Arguments as for fa_decode, minus workspace and workspace_bytes.
+ *   FA_ERR_SCRATCH when the call would need more than 32 MiB of scratch,
+ *   i.e. fa_decode_workspace_bytes(B, Nq, Nk, H, d) > 32 MiB (nothing is
+ *   launched; fa_decode with a workspace handles such calls). Other errors
+ *   as for fa_decode. The library calls no hipMalloc, hipFree or other
+ *   allocating routine here.
+ *   Every call on one device shares that device's scratch: calls that may
+ *   overlap on one device (on different streams, or from several host
+ *   threads without ordering) race on it and must not be issued.
+ */
+FA_API fa_status fa_decode_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int B, int Nq, int Nk, int H, int d, int causal, float softmax_scale,
+                            hipStream_t stream);
 
 /* Human-readable text of a status code (a static string; never NULL). */
 FA_API const char* fa_status_string(fa_status status);

@@ -300,3 +300,19 @@ def test_binding_rejects_host_or_mistyped_workspace():
         fa._check_workspace(torch.empty(1024, dtype=torch.uint8), 512, dev)  # host memory
     with pytest.raises(ValueError, match="workspace"):
         fa._check_workspace(torch.empty(1024, dtype=torch.float32), 512, dev)  # not bytes
+
+
+def test_decode_noalloc_validation(lib):
+    """Checks before any device work: the usual argument errors, and
+    FA_ERR_SCRATCH for a call whose key-split partials exceed the 32 MiB
+    static scratch (fa_decode with a workspace takes such calls)."""
+    f = lib.fa_decode_noalloc
+    assert f(None, P, P, P, P, 1, 1, 10, 1, 64, 1, 0.1, None) == FA_ERR_NULL
+    assert f(P, P, P, P, P, 1, 1, 10, 1, 96, 1, 0.1, None) == FA_ERR_HEADDIM
+    assert f(P, P, P, P, P, 1, 1, 0, 1, 64, 1, 0.1, None) == FA_ERR_SHAPE
+    assert f(P, P, P, P, P, 1, 1, 10, 1, 64, 1, float("nan"), None) == FA_ERR_SCALE
+    assert f(P + 2, P, P, P, P, 1, 1, 10, 1, 64, 1, 0.1, None) == FA_ERR_ALIGN
+    B, Nq, Nk, H, d = 1, 32, 218560, 3, 128
+    assert fa.fa_decode_workspace_bytes(B, Nq, Nk, H, d) > 32 << 20
+    assert f(P, P, P, P, P, B, Nq, Nk, H, d, 1, 0.1, None) == 9
+    assert fa.fa_status_string(9).startswith("the call needs more scratch")
