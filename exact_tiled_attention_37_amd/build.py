@@ -21,6 +21,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfa_mi355x.so")
 SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_bwd.hip", "fa_merge.hip", "fa_fp8.hip"]
+# Per-source compiler flags (none at present).
+EXTRA_FLAGS = {}
 ARCH = "gfx950"
 
 
@@ -64,7 +66,7 @@ def build(verbose: bool = False) -> str:
     for src in SOURCES:
         obj = os.path.join(BUILD, src.replace(".hip", ".o"))
         objs.append(obj)
-        jobs.append([cc, *common_flags(), "-c", os.path.join(CSRC, src), "-o", obj])
+        jobs.append([cc, *common_flags(), *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
     workers = min(len(jobs), max(1, (os.cpu_count() or 1)))
     with concurrent.futures.ThreadPoolExecutor(workers) as ex:
         for f in [ex.submit(_run, j, verbose) for j in jobs]:

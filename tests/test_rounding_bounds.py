@@ -4,7 +4,8 @@ oracle: which tolerances the kernels' bf16 roundings alone require.
 The GPU parity tests hold O, dQ, dK, dV to max-abs 2e-2 and mean-abs 2e-3
 against the exact result. That fixed absolute bound assumes outputs of order
 one. Three kinds of GPU test use a bound derived here instead:
-  * softmax scales other than 1/sqrt(d), and dBias: bf16 roundings of P, dS
+  * softmax scales other than 1/sqrt(d) (gradients, and O on launches of
+    more than one workgroup per CU), and dBias: bf16 roundings of P, dS
     and of the outputs give errors proportional to the output magnitude
     M = max|ref|, and the tests use 2e-2 * max(1, M/2) (2e-3 * max(1, M/2)
     for the mean). The model's own errors must stay within three quarters
@@ -90,6 +91,25 @@ def test_scaled_bound_admits_the_roundings_at_other_scales(d):
                 assert mx <= HEADROOM * MAX_TOL * m and mn <= HEADROOM * MEAN_TOL * m, (scale, causal, n, mx, mn, m)
                 beyond_plain |= mx > MAX_TOL
     assert beyond_plain, "the plain bound would have sufficed: the widening is not needed"
+
+
+def test_scaled_bound_admits_the_roundings_of_o_at_other_scales():
+    """O at other scales, on the inputs of the GPU tests that hold it to the
+    magnitude-scaled bound (N = 150, H = 2, seed 77 + d; and B = 1, N = 700,
+    H = 50, d = 128, seed 3100): within three quarters of the bound. At
+    large scales the softmax is nearly one-hot and |O| reaches V's largest
+    entries, where one bf16 rounding is up to |O| 2^-9."""
+    cases = [(si.draw(1, 150, 2, d, 77 + d, backward=True), (-0.2, 0.0, 0.9, 2.5)) for d in (64, 128)]
+    cases.append((si.draw(1, 700, 50, 128, 3100, backward=True), (-0.2, 0.0, 0.9, 2.5)))
+    for bits, scales in cases:
+        x = {n: si.bf16_bits_to_f64(bits[n]) for n in bits}
+        for scale in scales:
+            for causal in (False, True):
+                got = kr.emulate(x["q"], x["k"], x["v"], x["do"], causal, scale)
+                ref = ref_backward(x, causal, scale)
+                mx, mn = kr.error(got["o"], ref["o"])
+                m = max(1.0, float(np.abs(ref["o"]).max()) / 2.0)
+                assert mx <= HEADROOM * MAX_TOL * m and mn <= HEADROOM * MEAN_TOL * m, (scale, causal, mx, mn, m)
 
 
 def test_scaled_bound_admits_the_roundings_of_dbias():
