@@ -14,8 +14,9 @@
 // tiles staged in LDS, so no partial results are exchanged between waves.
 // Two (d = 128) or three to four (d = 64) workgroups share a CU, so one wave's
 // softmax arithmetic overlaps another's matrix instructions; a d = 128
-// launch too small for that (at most one workgroup per CU) overlaps them
-// inside each wave instead (software-pipelined tile loop).
+// launch too small for that (at most one workgroup per CU) gives each
+// workgroup two groups of 4 waves that split the key tiles between them and
+// combine their partial results at the end.
 //
 // K/V tiles move from memory straight into LDS with buffer loads
 // that write LDS directly (no register staging), double-buffered: the next
@@ -50,21 +51,28 @@ namespace {
 
 // Per head dimension: query rows per workgroup (32 per wave), keys per K/V
 // tile, LDS stages of the K/V ring and waves per SIMD. Both use 128 rows
-// (4 waves) per workgroup, 64-key tiles and a double-buffered ring; d = 128
-// runs two workgroups per CU, d = 64 three (its softmax work per matrix
-// instruction is twice that of d = 128, so a third wave hides more of it;
-// 64-key rather than 32-key tiles halve its per-tile fixed work). (256-row
+// (4 waves) per workgroup and a double-buffered ring. d = 64 runs three
+// workgroups per CU on 64-key tiles (its softmax work per matrix instruction
+// is twice that of d = 128, so a third wave hides more of it; 64-key rather
+// than 32-key tiles halve its per-tile fixed work). d = 128 also runs three,
+// on 32-key tiles: 64-key ones take 64 KiB of LDS per workgroup, which
+// leaves room for only two, and a third wave per SIMD gains more than the
+// larger tiles' lower fixed work (measured 0.5-4% faster on causal 2k-16k
+// launches, the same non-causal). With a bias, d = 128 keeps 64-key tiles
+// and two workgroups per CU (its bias staging does not fit three). (256-row
 // workgroups and deeper rings were measured slower: one workgroup per CU
 // leaves each workgroup's start and end exposed.)
 template <int D_, int BR_, int BC_, int STAGES_, int WAVES_PER_SIMD_>
 struct KernelCfg {
   static constexpr int D = D_, BR = BR_, BC = BC_, STAGES = STAGES_, WAVES_PER_SIMD = WAVES_PER_SIMD_;
-  static constexpr bool PIPE = false;  // software-pipelined tile loop (below)
+  static constexpr int KSPLIT = 1;  // groups of waves that share a query block (below)
   static constexpr int GROUP_ROUNDS = 2;  // block order: XCD rounds of blocks per head group
 };
 template <int D> struct FwdCfg;
 template <> struct FwdCfg<64> : KernelCfg<64, 128, 64, 2, 3> {};
-template <> struct FwdCfg<128> : KernelCfg<128, 128, 64, 2, 2> {};
+template <> struct FwdCfg<128> : KernelCfg<128, 128, 32, 2, 3> {};
+template <int D> struct FwdBiasCfg : FwdCfg<D> {};
+template <> struct FwdBiasCfg<128> : KernelCfg<128, 128, 64, 2, 2> {};
 // d = 64 without a bias fits four workgroups per CU (128 registers, 32 KiB
 // of LDS each). Measured faster for key lengths up to 4096 (short and
 // mid-length sequences: more waves to hide the softmax, whole rounds of
@@ -73,15 +81,18 @@ template <> struct FwdCfg<128> : KernelCfg<128, 128, 64, 2, 2> {};
 struct FwdCfg64Short : KernelCfg<64, 128, 64, 2, 4> {};
 constexpr int kFwd64ShortMaxKeys = 4096;
 // A launch of at most one workgroup per CU (e.g. one 2048-row chunk of 16
-// heads) has a single wave per SIMD, so no second wave hides one wave's
-// softmax behind another's matrix instructions. This form does the overlap
-// inside the wave: the scores of the next tile are computed while the
-// softmax of the current one runs. Its launch bound still asks for two
-// waves per SIMD, which caps it at 256 registers: with more, the compiler
-// keeps the MFMA accumulators in the AGPR file and copies every value
-// between the two register files.
-struct FwdCfgPipe128 : KernelCfg<128, 128, 64, 2, 2> {
-  static constexpr bool PIPE = true;
+// heads) would leave a single wave per SIMD, so no second wave would hide
+// one wave's softmax behind another's matrix instructions. Such launches use
+// workgroups of 8 waves in two groups of 4 over the same 128 query rows: the
+// first group takes the even K/V tiles of the key range and the second the
+// odd ones, each with its own LDS ring, so every SIMD runs two waves. At the
+// end the second group hands its running max, row sums and partial output to
+// the first through LDS, which combines the two exactly (each part rescaled
+// to the larger max) and writes the result. (Measured 9-21% faster on such
+// launches than one group that overlaps the next tile's scores with the
+// current tile's softmax inside each wave.)
+struct FwdCfgSplit128 : KernelCfg<128, 128, 64, 2, 2> {
+  static constexpr int KSPLIT = 2;
 };
 constexpr int kNumCus = kNumXcd * kCusPerXcd;
 // Decode-shaped calls (a few query rows against a long key history) are
@@ -111,7 +122,7 @@ constexpr float kRescaleSlack = 8.f;  // log2 units a row max may exceed the run
 // of 8, the row base 16-byte aligned); keys past Nk are always masked so the
 // padding of a bias row is never used.
 template <typename Cfg, bool CAUSAL, bool F32OUT, bool BIAS = false>
-__global__ __launch_bounds__(Cfg::BR * 2)
+__global__ __launch_bounds__(Cfg::BR * 2 * Cfg::KSPLIT)
 __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD))) void fwd_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     void* __restrict__ O, float* __restrict__ LSE, int Nq, int Nk, int delta, int H, int nqb,
@@ -121,7 +132,9 @@ __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD))) v
   constexpr int kFwdBR = Cfg::BR;                  // query rows per workgroup
   constexpr int kFwdBC = Cfg::BC;                  // keys per K/V tile
   constexpr int STAGES = Cfg::STAGES;              // K/V tiles in the LDS ring
-  constexpr int NW = kFwdBR / 32;                  // waves per workgroup
+  constexpr int NW = kFwdBR / 32;                  // waves per group (one per 32 query rows)
+  constexpr int KSPLIT = Cfg::KSPLIT;              // groups of waves, each with every KSPLIT-th tile
+  static_assert(KSPLIT == 1 || !BIAS, "split groups: no bias");
   constexpr int KB = kFwdBC / 32;                  // 32-key score blocks per tile
   using T = Tile<kFwdBC, D>;                       // one K or V tile in LDS
   constexpr int TILE = T::BYTES;
@@ -129,16 +142,26 @@ __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD))) v
   constexpr int DMA_PER_WAVE = (T::LOADS + NW - 1) / NW;  // 1 KiB wave loads per tile per wave and tensor
   constexpr int KS = D / 16;                       // MFMA k-steps over d
   constexpr int DB = D / 32;                       // 32-wide output column blocks
-  __shared__ __attribute__((aligned(1024))) char ring[STAGES * 2 * TILE];  // per stage: K tile, V tile
+  // Per group and stage: K tile, V tile. With several groups the same memory
+  // later holds the partial results of groups 1.. for the combine (NX floats
+  // per lane).
+  constexpr int NX = D / 32 * 16 + 2;
+  constexpr int RING = KSPLIT * STAGES * 2 * TILE;
+  constexpr int XCHG = (KSPLIT - 1) * NW * NX * 64 * 4;
+  __shared__ __attribute__((aligned(1024))) char ring[RING > XCHG ? RING : XCHG];
   // Bias of the next tile for each wave's 32 rows (see bias_fetch below).
   __shared__ __attribute__((aligned(BIAS ? 1024 : 16))) char bias_lds[BIAS ? NW * 32 * kFwdBC * 2 : 16];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar registers
+  const int lane = tid & 63;
+  const int wave_id = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar registers
+  const int half = KSPLIT > 1 ? wave_id / NW : 0;  // this wave's group: tiles j0 + half, + KSPLIT, ...
+  const int wave = wave_id - half * NW;            // query rows 32 * wave .. of the block
   const int g = lane >> 5, l32 = lane & 31, G = lane >> 4;
+  char* const ring_h = ring + half * (STAGES * 2 * TILE);
 
   const HeadRank hr = block_order<CAUSAL>(blockIdx.x, total_blocks / (nqb * nsplit), nqb * nsplit,
-                                          kCusPerXcd * Cfg::WAVES_PER_SIMD, Cfg::GROUP_ROUNDS);
+                                          kCusPerXcd * Cfg::WAVES_PER_SIMD / KSPLIT, Cfg::GROUP_ROUNDS);
   const int head = hr.head;                        // b * H + h
   const int qblk = nqb - 1 - hr.rank / nsplit;     // longest causal rows first
   const int split = hr.rank - (hr.rank / nsplit) * nsplit;
@@ -178,11 +201,11 @@ __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD))) v
     const int u = min(wave + NW * t, T::LOADS - 1);
     dma_off[t] = (uint32_t)T::dma_row(u, lane) * tokb + 16u * T::dma_chunk(u, lane);
   }
-  const uint32_t ring_lds = lds_base(ring);
+  const uint32_t ring_lds = lds_base(ring_h);
   auto issue = [&](int tile, char* dst, int t0 = 0, int t1 = 1 << 20) __attribute__((always_inline)) {
     const uint32_t toff = (uint32_t)(tile * kFwdBC) * tokb;
     const u32x4 rkt = rsrc_advance(rk, toff), rvt = rsrc_advance(rv, toff);
-    const uint32_t l0 = ring_lds + (uint32_t)(dst - ring);
+    const uint32_t l0 = ring_lds + (uint32_t)(dst - ring_h);
 #pragma unroll
     for (int t = 0; t < DMA_PER_WAVE; ++t) {
       if (t < t0 || t >= t1) continue;
@@ -201,6 +224,10 @@ __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD))) v
   const int j0 = k_lo / kFwdBC;
   const int j1 = k_end > k_lo ? (k_end + kFwdBC - 1) / kFwdBC : j0;
   const int ntiles = j1 - j0;
+  // This group's tiles: j0 + KSPLIT * t + half for t < nth; all groups run
+  // nit iterations (one barrier each), a group without a tile idles in it.
+  const int nit = (ntiles + KSPLIT - 1) / KSPLIT;
+  const int nth = max(0, (ntiles - half + KSPLIT - 1) / KSPLIT);
 
   f32x16 oacc[DB];
 #pragma unroll
@@ -332,23 +359,24 @@ __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD))) v
         oacc[db] = mfma32(a, pf[ks], oacc[db]);
       }
   };
-  // The t-th tile of the range (tile j0 + t) lives in stage t % STAGES.
-  // Iteration t first refills the stage that tile t - 1 used (every wave
-  // finished it before the last barrier) with tile t + STAGES - 1, computes
-  // tile t, then waits for its own loads of tile t + 1 (the loads of later
-  // tiles may stay in flight) and meets the other waves at the barrier,
-  // after which tile t + 1 is complete in LDS.
-  auto stage = [&](int t) __attribute__((always_inline)) { return ring + (t % STAGES) * (2 * TILE); };
+  // The t-th tile of a group (tile j0 + KSPLIT * t + half) lives in stage
+  // t % STAGES of the group's ring. Iteration t first refills the stage that
+  // its tile t - 1 used (every wave finished it before the last barrier)
+  // with its tile t + STAGES - 1, computes tile t, then waits for its own
+  // loads of tile t + 1 (the loads of later tiles may stay in flight) and
+  // meets the other waves at the barrier, after which tile t + 1 is complete
+  // in LDS.
+  auto stage = [&](int t) __attribute__((always_inline)) { return ring_h + (t % STAGES) * (2 * TILE); };
   static_assert(STAGES >= 2 && STAGES <= 4, "K/V ring depth");
   auto wait_next = [&](int t) __attribute__((always_inline)) {
     if constexpr (STAGES >= 4) {
-      if (t + 3 < ntiles) {  // tiles t + 2 and t + 3 may stay in flight
+      if (t + 3 < nth) {  // tiles t + 2 and t + 3 may stay in flight
         wait_vmem_leave<4 * DMA_PER_WAVE>();
         return;
       }
     }
     if constexpr (STAGES >= 3) {
-      if (t + 2 < ntiles) {  // tile t + 2 may stay in flight
+      if (t + 2 < nth) {  // tile t + 2 may stay in flight
         wait_vmem_leave<2 * DMA_PER_WAVE>();
         return;
       }
@@ -360,220 +388,94 @@ __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD))) v
   // (causal: the tiles whose last key is visible to the block's first row)
   const int jm_all = CAUSAL ? min(max(0, qblk * kFwdBR + delta + 1) / kFwdBC, Nk / kFwdBC) : Nk / kFwdBC;
   const int jm = min(max(jm_all, j0), j1);
-  if constexpr (Cfg::PIPE) {
-    static_assert(!BIAS && STAGES == 2, "the pipelined form has no bias and a two-stage ring");
-    // Iteration t computes the scores of tile t + 1 on the matrix unit while
-    // the vector unit takes the softmax of tile t, then O += P(t) V(t). The
-    // arithmetic is that of `compute`, in the same order; only the
-    // instruction schedule differs. K of tile t + 1 and V of tile t are in
-    // use together, so K is fetched two tiles ahead and V one: iteration t
-    // loads K of tile t + 2 into the slot that K of tile t was read from
-    // (in iteration t - 1, before its barrier) and V of tile t + 1.
-    auto issue_one = [&](const u32x4& r, int tile, uint32_t l0) __attribute__((always_inline)) {
-      const u32x4 rt = rsrc_advance(r, (uint32_t)(tile * kFwdBC) * tokb);
 #pragma unroll
-      for (int t = 0; t < DMA_PER_WAVE; ++t) {
-        const int u = wave + NW * t;
-        if (T::LOADS < NW && u >= T::LOADS) break;
-        dma16_at(rt, l0 + T::dma_dst(u), dma_off[t]);
-      }
-    };
-    auto k_lds = [&](int t) __attribute__((always_inline)) { return ring_lds + (uint32_t)((t & 1) * 2 * TILE); };
-    auto pipe_loads = [&](int t) __attribute__((always_inline)) {
-      if (t + 2 < ntiles) issue_one(rk, j0 + t + 2, k_lds(t));
-      if (t + 1 < ntiles) issue_one(rv, j0 + t + 1, k_lds(t + 1) + TILE);
-    };
-    auto s_product = [&](const char* kt, f32x16 (&s)[KB]) __attribute__((always_inline)) {
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) s[kb] = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) s[kb] = mfma32(T::row8(kt, kb * 32 + l32, 2 * ks + g), qf[ks], s[kb]);
-    };
-    // Softmax and P V of tile t from its scores sc; with AHEAD the scores of
-    // tile t + 1 go to sn first. The group barriers ask the scheduler to put
-    // up to six vector instructions of the softmax after each matrix
-    // instruction of the next tile's scores, and the row sums and bf16 packs
-    // between those of P V; the rarely taken rescale branch sits between the
-    // two groups (P is computed before it from the new maximum).
-    auto pipe_step = [&](int t, f32x16 (&sc)[KB], f32x16 (&sn)[KB], auto mask_tag, auto ahead_tag, auto&& loads)
-                         __attribute__((always_inline)) {
-      constexpr bool MASK = decltype(mask_tag)::value;
-      constexpr bool AHEAD = decltype(ahead_tag)::value;
-      loads();
-      const int key0 = (j0 + t) * kFwdBC;
-      if constexpr (AHEAD) s_product(stage(t + 1), sn);
-      if constexpr (MASK) {
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-            if ((CAUSAL && key > myq + delta) || key >= Nk) sc[kb][r] = -INFINITY;
-          }
-      }
-      float mx = max16(sc[0], -INFINITY);
-#pragma unroll
-      for (int kb = 1; kb < KB; ++kb) mx = max16(sc[kb], mx);
-      mx = xhalf_max(mx);
-      const float tile_m = (mx == -INFINITY) ? -INFINITY : mx * c2;
-      const bool grow = tile_m > m_run + kRescaleSlack;
-      const float m_new = grow ? tile_m : m_run;
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      f32x8 p[2 * KB];
-#pragma unroll
-      for (int ks = 0; ks < 2 * KB; ++ks)
-#pragma unroll
-        for (int s8 = 0; s8 < 8; ++s8) {
-          const float sv = sc[ks >> 1][8 * (ks & 1) + s8];
-          float e = fast_exp2(__builtin_fmaf(sv, c2, -m_use));
-          if constexpr (MASK) e = (sv == -INFINITY) ? 0.f : e;  // exact zero even when c2 = 0
-          p[ks][s8] = e;
-        }
-      // P is used only after the branch; without these the compiler sinks
-      // the exponentials past it, away from the matrix instructions.
-#pragma unroll
-      for (int ks = 0; ks < 2 * KB; ++ks) asm volatile("" : "+v"(p[ks]));
-      if constexpr (AHEAD && !MASK) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // LDS reads of K
-#pragma unroll
-        for (int i = 0; i < KS * KB; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-          __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // vector instructions
-          if (i + 4 < KS * KB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-      }
-      if (__builtin_amdgcn_ballot_w64(grow)) {  // wave-uniform, rarely taken
-        asm volatile("" ::: "memory");          // keep it a branch (no speculation)
-        const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
-      }
-      m_run = m_new;
-      bf16x8 pf[2 * KB];
-#pragma unroll
-      for (int ks = 0; ks < 2 * KB; ++ks) {
-        l_run += sum8(p[ks]);
-        pf[ks] = to_bf16x8(p[ks]);
-      }
-      const char* vt = stage(t) + TILE;
-#pragma unroll
-      for (int ks = 0; ks < 2 * KB; ++ks)
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const bf16x8 a = T::col8(vt, 16 * ks + 4 * g, 16 * ks + 8 + 4 * g, 32 * db + 16 * (G & 1), lane);
-          oacc[db] = mfma32(a, pf[ks], oacc[db]);
-        }
-      if constexpr (AHEAD && !MASK) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);  // transpose reads of V
-        __builtin_amdgcn_sched_group_barrier(0x002, 4, 1);
-#pragma unroll
-        for (int i = 0; i < 2 * KB * DB; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-          __builtin_amdgcn_sched_group_barrier(0x002, 3, 1);
-          if (i + 2 < 2 * KB * DB) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
-        }
-      }
-      wait_vmem();
-      __syncthreads();
-    };
-    const int tm = jm - j0;  // tiles [0, tm) need no mask
-    // The tiles this wave needs form a prefix of the range (causal: those
-    // whose first key is visible to the wave's last row); every wave needs
-    // the first tm.
-    const int wlast = qw0 + 31 + delta;
-    const int nt_w = !CAUSAL ? ntiles : wlast < 0 ? 0 : min(ntiles, max(0, wlast / kFwdBC + 1 - j0));
-    if (ntiles > 0) {
-      issue_one(rk, j0, k_lds(0));
-      issue_one(rv, j0, k_lds(0) + TILE);
-    }
-    if (ntiles > 1) issue_one(rk, j0 + 1, k_lds(1));
-    wait_vmem();
+  for (int t = 0; t < STAGES - 1; ++t)
+    if (t < nth) issue(j0 + KSPLIT * t + half, stage(t));
+  if (BIAS && j0 < j1) bias_fetch(j0);
+  wait_next(-1);
+  if (BIAS && j0 < j1) bias_store();
+  __syncthreads();
+  int t = 0;
+  // In the unmasked causal loop half of a wave's loads of the next tile are
+  // issued before this tile's S product and half after it, so the LDS
+  // writes of the workgroup's loads do not arrive in one burst (long causal
+  // loops have the latency to spare; short non-causal ones do not).
+  // With a bias, iteration j also fetches the bias of tile j + 1 into
+  // registers and writes it to the wave's LDS slice after this tile's
+  // compute has read tile j's (a wave's LDS operations run in order).
+  constexpr int SPLIT = CAUSAL ? DMA_PER_WAVE / 2 : DMA_PER_WAVE;
+  // Unmasked iterations: every group's tile lies before jm.
+  const int tu = (jm - j0) / KSPLIT;
+  constexpr int AHEAD = KSPLIT * (STAGES - 1);  // tile distance of a refill
+  for (; t < tu; ++t) {
+    const int j = j0 + KSPLIT * t + half;
+    const bool more = t + STAGES - 1 < nth;
+    if (more) issue(j + AHEAD, stage(t + STAGES - 1), 0, SPLIT);
+    if (BIAS && j + 1 < j1) bias_fetch(j + 1);
+    compute(j, stage(t), std::false_type{}, [&]() __attribute__((always_inline)) {
+      if (SPLIT < DMA_PER_WAVE && more) issue(j + AHEAD, stage(t + STAGES - 1), SPLIT, DMA_PER_WAVE);
+    });
+    wait_next(t);
+    if (BIAS && j + 1 < j1) bias_store();
     __syncthreads();
-    f32x16 sa[KB], sb[KB];
-    if (nt_w > 0) s_product(stage(0), sa);
-    __syncthreads();  // every wave has read K of tile 0 before iteration 0 refills its slot
-    int t = 0;
-    const int tu = min(tm, ntiles - 1);  // unmasked iterations that have a next tile
-    for (; t + 1 < tu; t += 2) {
-      pipe_step(t, sa, sb, std::false_type{}, std::true_type{}, [&]() __attribute__((always_inline)) { pipe_loads(t); });
-      pipe_step(t + 1, sb, sa, std::false_type{}, std::true_type{},
-                [&]() __attribute__((always_inline)) { pipe_loads(t + 1); });
-    }
-    if (t < tu) {
-      pipe_step(t, sa, sb, std::false_type{}, std::true_type{}, [&]() __attribute__((always_inline)) { pipe_loads(t); });
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) sa[kb] = sb[kb];
-      ++t;
-    }
-    if (t < tm) {  // the range's last tile, unmasked (then tm == ntiles)
-      pipe_step(t, sa, sb, std::false_type{}, std::false_type{}, [&]() __attribute__((always_inline)) { pipe_loads(t); });
-      ++t;
-    }
-    // The few masked tiles (the diagonal, the ragged end) run without the
-    // overlap, which would need more registers than the wave has: tile tm
-    // uses the scores computed ahead, later tiles compute theirs in the
-    // step. From here on iteration t loads K and V of tile t + 1 (K of tile
-    // tm + 1 was already fetched ahead); both slots of tile t + 1 last held
-    // tile t - 1, which was read before the previous barrier.
-    for (; t < ntiles; ++t) {
-      auto masked_loads = [&]() __attribute__((always_inline)) {
-        if (t + 1 < ntiles) {
-          if (t > tm) issue_one(rk, j0 + t + 1, k_lds(t + 1));
-          issue_one(rv, j0 + t + 1, k_lds(t + 1) + TILE);
-        }
-      };
-      if (t == tm && t < nt_w) {
-        pipe_step(t, sa, sb, std::true_type{}, std::false_type{}, masked_loads);
-      } else {  // a wave that does not need the tile only loads and meets the barrier
-        masked_loads();
-        if (t < nt_w) compute(j0 + t, stage(t), std::true_type{}, []() {});
-        wait_vmem();
-        __syncthreads();
-      }
-    }
-  } else {
-#pragma unroll
-    for (int t = 0; t < STAGES - 1; ++t)
-      if (t < ntiles) issue(j0 + t, stage(t));
-    if (BIAS && j0 < j1) bias_fetch(j0);
-    wait_next(-1);
-    if (BIAS && j0 < j1) bias_store();
+  }
+  for (; t < nit; ++t) {
+    const int j = j0 + KSPLIT * t + half;
+    if (t + STAGES - 1 < nth) issue(j + AHEAD, stage(t + STAGES - 1));
+    if (BIAS && j + 1 < j1) bias_fetch(j + 1);
+    // A tile whose first key lies past this wave's last row is fully masked
+    // for it and contributes nothing (and a group may have no tile left).
+    if (t < nth && (!CAUSAL || j * kFwdBC <= qw0 + 31 + delta)) compute(j, stage(t), std::true_type{}, []() {});
+    wait_next(t);
+    if (BIAS && j + 1 < j1) bias_store();
     __syncthreads();
-    int j = j0;
-    // In the unmasked causal loop half of a wave's loads of the next tile are
-    // issued before this tile's S product and half after it, so the LDS
-    // writes of the workgroup's loads do not arrive in one burst (long causal
-    // loops have the latency to spare; short non-causal ones do not).
-    // With a bias, iteration j also fetches the bias of tile j + 1 into
-    // registers and writes it to the wave's LDS slice after this tile's
-    // compute has read tile j's (a wave's LDS operations run in order).
-    constexpr int SPLIT = CAUSAL ? DMA_PER_WAVE / 2 : DMA_PER_WAVE;
-    for (; j < jm; ++j) {
-      const int t = j - j0;
-      const bool more = t + STAGES - 1 < ntiles;
-      if (more) issue(j + STAGES - 1, stage(t + STAGES - 1), 0, SPLIT);
-      if (BIAS && j + 1 < j1) bias_fetch(j + 1);
-      compute(j, stage(t), std::false_type{}, [&]() __attribute__((always_inline)) {
-        if (SPLIT < DMA_PER_WAVE && more) issue(j + STAGES - 1, stage(t + STAGES - 1), SPLIT, DMA_PER_WAVE);
-      });
-      wait_next(t);
-      if (BIAS && j + 1 < j1) bias_store();
-      __syncthreads();
+  }
+
+  if constexpr (KSPLIT > 1) {
+    // Combine the groups. The loops end at a barrier, so the rings are free:
+    // each group h >= 1 stores, per lane, its partial output, running max and
+    // row-sum share (element i of wave w's lane at float
+    // ((h - 1) * NW + w) * NX * 64 + i * 64 + lane: conflict-free); a lane of
+    // group 0 holds the same row and keys of the same layout. Every part is
+    // rescaled to the largest max; a part that saw no key (max -inf) counts 0.
+    static_assert(NX == DB * 16 + 2, "exchange record: output, max, row sum");
+    FA_LDS float* const xs = (FA_LDS float*)ring + wave * NX * 64 + lane;
+    constexpr int XG = NW * NX * 64;  // floats per group
+    if (half > 0) {
+      FA_LDS float* const mine = xs + (half - 1) * XG;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mine[(db * 16 + r) * 64] = oacc[db][r];
+      mine[DB * 16 * 64] = m_run;
+      mine[(DB * 16 + 1) * 64] = l_run;
     }
-    for (; j < j1; ++j) {
-      const int t = j - j0;
-      if (t + STAGES - 1 < ntiles) issue(j + STAGES - 1, stage(t + STAGES - 1));
-      if (BIAS && j + 1 < j1) bias_fetch(j + 1);
-      // A tile whose first key lies past this wave's last row is fully masked
-      // for it and contributes nothing.
-      if (!CAUSAL || j * kFwdBC <= qw0 + 31 + delta) compute(j, stage(t), std::true_type{}, []() {});
-      wait_next(t);
-      if (BIAS && j + 1 < j1) bias_store();
-      __syncthreads();
+    __syncthreads();
+    if (half > 0) return;
+    float m = m_run;
+#pragma unroll
+    for (int p = 0; p < KSPLIT - 1; ++p) m = fmaxf(m, xs[p * XG + DB * 16 * 64]);
+    const float a0 = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m);
+    l_run *= a0;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) oacc[db] *= a0;
+    float ap[KSPLIT - 1];
+#pragma unroll
+    for (int p = 0; p < KSPLIT - 1; ++p) {
+      const float mp = xs[p * XG + DB * 16 * 64];
+      ap[p] = (mp == -INFINITY) ? 0.f : fast_exp2(mp - m);
+      l_run += xs[p * XG + (DB * 16 + 1) * 64] * ap[p];
     }
+    // One 32-column block at a time (keeps the loads in flight few).
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int p = 0; p < KSPLIT - 1; ++p)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] += xs[p * XG + (db * 16 + r) * 64] * ap[p];
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    m_run = m;
   }
 
   // A row that saw no key (possible only with a causal offset that puts every
@@ -604,6 +506,7 @@ __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD))) v
 template <int D, bool CAUSAL>
 hipError_t launch_fwd(const FwdArgs& a) {
   constexpr int BR = FwdCfg<D>::BR;
+  static_assert(FwdBiasCfg<D>::BR == BR, "one block size per head dimension");
   const int nqb = (a.Nq + BR - 1) / BR;
   const int total = a.B * a.H * nqb;
   const float c2 = fabsf(a.scale) * kLog2e;
@@ -612,7 +515,7 @@ hipError_t launch_fwd(const FwdArgs& a) {
   const auto* k = static_cast<const bf16*>(a.k);
   const auto* v = static_cast<const bf16*>(a.v);
   if (a.bias) {
-    hipLaunchKernelGGL((fwd_kernel<FwdCfg<D>, CAUSAL, false, true>), dim3(total), dim3(BR * 2), 0, a.stream, q, k,
+    hipLaunchKernelGGL((fwd_kernel<FwdBiasCfg<D>, CAUSAL, false, true>), dim3(total), dim3(BR * 2), 0, a.stream, q, k,
                        v, a.o, a.lse, a.Nq, a.Nk, a.delta, a.H, nqb, 1, a.Nk, 0L, 0L, total, c2, q_sign,
                        static_cast<const bf16*>(a.bias), a.bias_sb, a.bias_sh, a.bias_srow);
     return hipGetLastError();
@@ -620,12 +523,13 @@ hipError_t launch_fwd(const FwdArgs& a) {
   auto plain = [&](auto cfg) {
     using Cfg = decltype(cfg);
     static_assert(Cfg::BR == BR, "one block size per head dimension");
+    const dim3 block(BR * 2 * Cfg::KSPLIT);
     if (a.f32_out)
-      hipLaunchKernelGGL((fwd_kernel<Cfg, CAUSAL, true>), dim3(total), dim3(BR * 2), 0, a.stream, q, k, v, a.o,
-                         a.lse, a.Nq, a.Nk, a.delta, a.H, nqb, 1, a.Nk, 0L, 0L, total, c2, q_sign);
+      hipLaunchKernelGGL((fwd_kernel<Cfg, CAUSAL, true>), dim3(total), block, 0, a.stream, q, k, v, a.o, a.lse,
+                         a.Nq, a.Nk, a.delta, a.H, nqb, 1, a.Nk, 0L, 0L, total, c2, q_sign);
     else
-      hipLaunchKernelGGL((fwd_kernel<Cfg, CAUSAL, false>), dim3(total), dim3(BR * 2), 0, a.stream, q, k, v, a.o,
-                         a.lse, a.Nq, a.Nk, a.delta, a.H, nqb, 1, a.Nk, 0L, 0L, total, c2, q_sign);
+      hipLaunchKernelGGL((fwd_kernel<Cfg, CAUSAL, false>), dim3(total), block, 0, a.stream, q, k, v, a.o, a.lse,
+                         a.Nq, a.Nk, a.delta, a.H, nqb, 1, a.Nk, 0L, 0L, total, c2, q_sign);
   };
   if constexpr (D == 64) {
     if (a.Nk <= kFwd64ShortMaxKeys)
@@ -634,7 +538,7 @@ hipError_t launch_fwd(const FwdArgs& a) {
       plain(FwdCfg<D>{});
   } else {
     if (total <= kNumCus)
-      plain(FwdCfgPipe128{});
+      plain(FwdCfgSplit128{});
     else
       plain(FwdCfg<D>{});
   }
