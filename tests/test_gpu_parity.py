@@ -411,9 +411,10 @@ def test_d64_long_key_chunk(causal):
 
 # ---------------------------------------------------------------------------
 # d = 128 on both sides of the launch switch at one workgroup per CU: 16
-# heads of 2000 rows (16 blocks each, 256 workgroups) run the
-# software-pipelined loop, 17 heads (272 workgroups) the plain one. Both are
-# compared whole with the oracle and with each other.
+# heads of 2000 rows (16 blocks each, 256 workgroups) run the form whose
+# workgroups split the key tiles between two groups of waves and combine
+# them, 17 heads (272 workgroups) the plain one. Both are compared whole
+# with the oracle and with each other.
 
 @pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
 def test_launch_forms_agree(causal):
