@@ -111,14 +111,15 @@ def test_chunk_small(case, causal):
     check_chunk(f64(o), f64(lse), ro, rl)
 
 
-def test_empty_chunk():
+@pytest.mark.parametrize("d", [64, 128])
+def test_empty_chunk(d):
     import torch
 
-    announce("chunk Nk=0")
-    qb, _, _ = draw_chunk(1, 40, 1, 2, 64, 77)
+    announce(f"chunk Nk=0 d={d}")
+    qb, _, _ = draw_chunk(1, 40, 1, 2, d, 77)
     q = dev(qb)
-    k = torch.empty((1, 0, 2, 64), dtype=torch.bfloat16, device="cuda")
-    o = torch.full((1, 40, 2, 64), 7.0, device="cuda")
+    k = torch.empty((1, 0, 2, d), dtype=torch.bfloat16, device="cuda")
+    o = torch.full((1, 40, 2, d), 7.0, device="cuda")
     lse = torch.full((1, 2, 40), 7.0, device="cuda")
     fa.fa_fwd_chunk(q, k, k, True, 0, 0, 0.125, out=o, lse=lse)
     torch.cuda.synchronize()
