@@ -26,8 +26,14 @@
 //     block p / 16) meets byte p of its V^T operand, which four 8-bit
 //     transpose loads (ds_read_b64_tr_b8) deliver.
 //   * LDS tiles hold 64 rows of 128 bytes (d = 128); the 16-byte chunk c of
-//     row r sits at position c ^ (r & 7), which keeps both the row reads of
-//     K and the transpose reads of V free of bank conflicts.
+//     row r sits at position c ^ h(r), h(r) = 2 ((r / 2) % 4) + (r / 8) % 2.
+//     A row fills half of the 256 bytes the 64 banks serve per pass, so the
+//     16 rows one row read touches (16 lanes, same chunk) must spread over
+//     both halves and 8 positions: rows of equal parity need distinct h
+//     within 16 rows. The transpose reads of V (32 lanes: chunks c and c ^ 1
+//     of 8 consecutive rows) need distinct h / 2 among the 4 rows of equal
+//     parity within 8. This h gives both; h = r % 8 (rows r and r + 8 alike)
+//     made every K row read a two-way conflict.
 // O is written as bf16 (times the V descale), the logsumexp as fp32.
 
 #include <type_traits>
@@ -50,7 +56,8 @@ constexpr int kF8Tile = kF8BC * kF8D;      // bytes of one K or V tile
 constexpr float kF8Slack = 4.f;            // log2 units the running max may lag
 constexpr float kF8Shift = 4.f;            // P is scaled by 2^4 before rounding
 
-__device__ __forceinline__ constexpr int f8_slot(int r, int c) { return r * kF8D + ((c ^ (r & 7)) << 4); }
+__device__ __forceinline__ constexpr int f8_swz(int r) { return (((r >> 1) & 3) << 1) | ((r >> 3) & 1); }
+__device__ __forceinline__ constexpr int f8_slot(int r, int c) { return r * kF8D + ((c ^ f8_swz(r)) << 4); }
 // LDS row r of a V tile holds key row vperm(r) (bits 2 and 3 exchanged; an involution).
 __device__ __forceinline__ constexpr int vperm(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
@@ -116,7 +123,7 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(3, 3
     for (int t = 0; t < 2; ++t) {
       const int u = wave + 4 * t;
       const int r = 8 * u + (lane >> 3);
-      const uint32_t c16 = 16u * (uint32_t)((lane & 7) ^ (r & 7));
+      const uint32_t c16 = 16u * (uint32_t)((lane & 7) ^ f8_swz(r));
       dma16(rk, dst + u * 1024, row_off(tile * kF8BC + r, N, tokb, c16));
       dma16(rv, dst + kF8Tile + u * 1024, row_off(tile * kF8BC + vperm(r), N, tokb, c16));
     }
@@ -131,6 +138,18 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(3, 3
   float m_run = -INFINITY;
   float l_run = 0.f;
 
+  // Per-lane LDS offsets: K row reads (row l32 of a 32-key block, chunk
+  // 4 ks + 2 g + hi) and V transpose reads (row 8 g + j16 / 2 of a 16-key
+  // group, chunk 2 db + G % 2, byte half j16 % 2); the block and group add
+  // whole rows, which leave the swizzle unchanged (it reads row bits 1-3).
+  int koff[2][2], voff[4];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) koff[ks][hi] = f8_slot(l32, 4 * ks + 2 * g + hi);
+#pragma unroll
+  for (int db = 0; db < 4; ++db) voff[db] = f8_slot(8 * g + (j16 >> 1), 2 * db + (G & 1)) + 8 * (j16 & 1);
+
   i32x8 pf = {};  // P^T operand of the current tile (kept across tiles)
   auto compute = [&](int j, const char* kt, auto mask_tag) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
@@ -141,8 +160,7 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(3, 3
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const int row = kb * 32 + l32;
-        const i32x8 a = cat(lds_read16(kt, f8_slot(row, 4 * ks + 2 * g)), lds_read16(kt, f8_slot(row, 4 * ks + 2 * g + 1)));
+        const i32x8 a = cat(lds_read16(kt, koff[ks][0] + kb * 32 * kF8D), lds_read16(kt, koff[ks][1] + kb * 32 * kF8D));
         s[kb] = mfma_f8(a, qf[ks], s[kb]);
       }
     if constexpr (MASK) {
@@ -192,7 +210,7 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(3, 3
       i32x8 a;
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const i32x2 t = lds_read_tr8(vt, f8_slot(16 * q4 + 8 * g + (j16 >> 1), 2 * db + (G & 1)) + 8 * (j16 & 1));
+        const i32x2 t = lds_read_tr8(vt, voff[db] + 16 * q4 * kF8D);
         a[2 * q4] = t[0];
         a[2 * q4 + 1] = t[1];
       }
