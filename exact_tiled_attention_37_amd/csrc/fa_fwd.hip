@@ -27,12 +27,14 @@
 //   S^T = K Q^T     (MFMA; lane l owns query row l % 32, so a row's scores
 //                    sit in two lanes: l and l ^ 32)
 //   online softmax in the log2 domain: c2 = |scale| * log2(e) is folded into
-//   one FMA per score before exp2; the row max needs a single cross-half
-//   exchange; the running sum stays per lane until the epilogue; the
-//   division by the row sum is deferred to the epilogue; and the running
-//   max (with the rescale of the partial output) is only moved when a row's
-//   max grows by more than 2^8, which keeps every exponent <= 8 while
-//   skipping almost all rescales.
+//   one FMA per score before exp2; the running sum stays per lane until the
+//   epilogue; the division by the row sum is deferred to the epilogue; and
+//   the running max (with the rescale of the partial output) is only moved
+//   when a probability relative to it would exceed 2^8, which keeps every
+//   exponent <= 8 while skipping almost all rescales. That test needs no row
+//   maximum: P is taken from the current running max and each lane's sum of
+//   it compared with 2^8; only a tile that fails it (rare after the first)
+//   forms the row maxima (one cross-half exchange) and takes P again.
 //   O^T += V^T P^T  (MFMA; P^T is taken straight from the S^T accumulator
 //                    registers, V^T is read with LDS transpose loads)
 // Causal masking: tiles entirely above the diagonal are never visited, and a
@@ -109,6 +111,10 @@ template <> struct DecCfg<128> : KernelCfg<128, 32, kDecodeBC, 2, 2> {
   static constexpr int GROUP_ROUNDS = 1;
 };
 constexpr float kRescaleSlack = 8.f;  // log2 units a row max may exceed the running max
+constexpr float kPSumMax = 256.f;     // 2^kRescaleSlack
+// The running max of a row that has seen no key: finite, so that P taken
+// from it is +inf for any visible score and exactly 0 for a masked one.
+constexpr float kNoMax = -1e30f;
 
 // Nq query rows attend to Nk key rows. With the causal mask key j is visible
 // to query i iff j <= i + delta (delta = global position of query row 0 minus
@@ -232,7 +238,7 @@ __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD))) v
   f32x16 oacc[DB];
 #pragma unroll
   for (int i = 0; i < DB; ++i) oacc[i] = f32x16{};
-  float m_run = -INFINITY;  // running max of c2 * score (log2 domain), possibly stale by <= 8
+  float m_run = kNoMax;     // running max of c2 * score (log2 domain), possibly stale by <= 8
   float l_run = 0.f;        // this lane's share of the running sum
 
   // One K/V tile. MASK selects the variant for tiles that straddle the
@@ -271,10 +277,11 @@ __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD))) v
       lds_write16(bw_lds, row * RB + ((chunk ^ (row % CH)) << 4), bst[t]);
     }
   };
-  auto compute = [&](int j, const char* kt, auto mask_tag, auto&& mid) __attribute__((always_inline)) {
+  // The scores of a tile: S^T = K Q^T for the wave's rows, then (with a
+  // bias) c2 * s + bias * log2(e), then the mask.
+  auto scores = [&](f32x16 (&s)[KB], const char* kt, int key0, auto mask_tag, auto&& mid)
+                    __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
-    const int key0 = j * kFwdBC;
-    const char* vt = kt + TILE;
     u32x2 bw[BIAS ? KB : 1][4];
     if constexpr (BIAS) {
 #pragma unroll
@@ -287,7 +294,6 @@ __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD))) v
         }
     }
     // The KB accumulation chains are interleaved (independent MFMAs back to back).
-    f32x16 s[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) s[kb] = f32x16{};
 #pragma unroll
@@ -311,28 +317,15 @@ __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD))) v
           if ((CAUSAL && key > myq + delta) || key >= Nk) s[kb][r] = -INFINITY;
         }
     }
-    float mx = max16(s[0], -INFINITY);
-#pragma unroll
-    for (int kb = 1; kb < KB; ++kb) mx = max16(s[kb], mx);
-    mx = xhalf_max(mx);
-    const float tile_m = (mx == -INFINITY) ? -INFINITY : (BIAS ? mx : mx * c2);
-    const bool grow = tile_m > m_run + kRescaleSlack;
-    if (__builtin_amdgcn_ballot_w64(grow)) {  // wave-uniform, rarely taken
-      asm volatile("" ::: "memory");          // keep it a branch (no speculation)
-      const float m_new = grow ? tile_m : m_run;
-      // 0 when m_run = -inf, 1 when unchanged (and when no key was visible yet)
-      const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
-      m_run = m_new;
-    }
-    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-
-    // P in bf16 for the PV product; the row sum stays in fp32 (the
-    // logsumexp is checked against the exact value, so it must not inherit
-    // the bf16 rounding of P).
-    bf16x8 pf[2 * KB];
+  };
+  // P = exp2(c2 s - m) (with a bias exp2(s - m)) in bf16 for the PV product;
+  // returns this lane's fp32 sum of the tile's P (the row sum stays in fp32:
+  // the logsumexp is checked against the exact value, so it must not inherit
+  // the bf16 rounding of P).
+  auto probs = [&](const f32x16 (&s)[KB], float m, bf16x8 (&pf)[2 * KB], auto mask_tag)
+                   __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    float t = 0.f;
 #pragma unroll
     for (int ks = 0; ks < 2 * KB; ++ks) {
       f32x8 p;
@@ -341,16 +334,67 @@ __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD))) v
         const float sv = s[ks >> 1][8 * (ks & 1) + s8];
         float e;
         if constexpr (BIAS) {
-          e = fast_exp2(sv - m_use);  // -inf (masked or a -inf bias) gives exactly 0
+          e = fast_exp2(sv - m);  // -inf (masked or a -inf bias) gives exactly 0
         } else {
-          e = fast_exp2(__builtin_fmaf(sv, c2, -m_use));
+          e = fast_exp2(__builtin_fmaf(sv, c2, -m));
           if constexpr (MASK) e = (sv == -INFINITY) ? 0.f : e;  // exact zero even when c2 = 0
         }
         p[s8] = e;
       }
-      l_run += sum8(p);
+      t += sum8(p);
       pf[ks] = to_bf16x8(p);
     }
+    return t;
+  };
+  // One K/V tile. MASK selects the variant for tiles that straddle the
+  // causal diagonal or the end of the sequence; all other tiles run the
+  // variant without any per-element masking.
+  // The running max m_run only has to move when a probability relative to
+  // it would exceed 2^8 (kRescaleSlack). Without a bias the tile's P is
+  // first taken from the current m_run; since P >= 0, a lane whose sum of
+  // the tile's P stays <= 2^8 has every value <= 2^8, so if no lane of the
+  // wave exceeds that, P stands and the tile needs no row maximum at all.
+  // Otherwise (and on the first tile, and always with a bias) the scores are
+  // formed again (the first pass consumed them; the K tile is still in LDS),
+  // the row maxima taken, m_run moved to them, O and l rescaled, and P
+  // recomputed. A row that has seen no key has m_run = kNoMax, for which
+  // every visible score overflows to +inf and takes the second path.
+  auto compute = [&](int j, const char* kt, auto mask_tag, auto&& mid, bool first) __attribute__((always_inline)) {
+    const int key0 = j * kFwdBC;
+    const char* vt = kt + TILE;
+    f32x16 s[KB];
+    scores(s, kt, key0, mask_tag, mid);
+    bf16x8 pf[2 * KB];
+    float t = 0.f;
+    bool slow = true;  // wave-uniform
+    if (!BIAS && !first) {
+      t = probs(s, m_run, pf, mask_tag);
+      slow = __builtin_amdgcn_ballot_w64(!(t <= kPSumMax)) != 0;
+    }
+    if (slow) {
+      asm volatile("" ::: "memory");  // a branch; the scores below are loaded again
+      if (!BIAS && !first) scores(s, kt, key0, mask_tag, []() {});
+      float mx = max16(s[0], -INFINITY);
+#pragma unroll
+      for (int kb = 1; kb < KB; ++kb) mx = max16(s[kb], mx);
+      mx = xhalf_max(mx);
+      const float tile_m = (mx == -INFINITY) ? -INFINITY : (BIAS ? mx : mx * c2);
+      // With a bias, only a growth beyond the slack moves m_run (the same
+      // rule, taken from the maxima); without one, the second path moves
+      // it to the tile's maximum.
+      const bool grow = BIAS ? tile_m > m_run + kRescaleSlack : tile_m > m_run;
+      if (__builtin_amdgcn_ballot_w64(grow)) {  // wave-uniform
+        asm volatile("" ::: "memory");          // keep it a branch (no speculation)
+        const float m_new = grow ? tile_m : m_run;
+        const float alpha = fast_exp2(m_run - m_new);  // 0 from kNoMax, 1 when unchanged
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+        m_run = m_new;
+      }
+      t = probs(s, m_run, pf, mask_tag);
+    }
+    l_run += t;
 #pragma unroll
     for (int ks = 0; ks < 2 * KB; ++ks)
 #pragma unroll
@@ -412,9 +456,12 @@ __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD))) v
     const bool more = t + STAGES - 1 < nth;
     if (more) issue(j + AHEAD, stage(t + STAGES - 1), 0, SPLIT);
     if (BIAS && j + 1 < j1) bias_fetch(j + 1);
-    compute(j, stage(t), std::false_type{}, [&]() __attribute__((always_inline)) {
-      if (SPLIT < DMA_PER_WAVE && more) issue(j + AHEAD, stage(t + STAGES - 1), SPLIT, DMA_PER_WAVE);
-    });
+    compute(
+        j, stage(t), std::false_type{},
+        [&]() __attribute__((always_inline)) {
+          if (SPLIT < DMA_PER_WAVE && more) issue(j + AHEAD, stage(t + STAGES - 1), SPLIT, DMA_PER_WAVE);
+        },
+        t == 0);
     wait_next(t);
     if (BIAS && j + 1 < j1) bias_store();
     __syncthreads();
@@ -425,7 +472,7 @@ __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD))) v
     if (BIAS && j + 1 < j1) bias_fetch(j + 1);
     // A tile whose first key lies past this wave's last row is fully masked
     // for it and contributes nothing (and a group may have no tile left).
-    if (t < nth && (!CAUSAL || j * kFwdBC <= qw0 + 31 + delta)) compute(j, stage(t), std::true_type{}, []() {});
+    if (t < nth && (!CAUSAL || j * kFwdBC <= qw0 + 31 + delta)) compute(j, stage(t), std::true_type{}, []() {}, t == 0);
     wait_next(t);
     if (BIAS && j + 1 < j1) bias_store();
     __syncthreads();
@@ -437,7 +484,7 @@ __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD))) v
     // row-sum share (element i of wave w's lane at float
     // ((h - 1) * NW + w) * NX * 64 + i * 64 + lane: conflict-free); a lane of
     // group 0 holds the same row and keys of the same layout. Every part is
-    // rescaled to the largest max; a part that saw no key (max -inf) counts 0.
+    // rescaled to the largest max; a part that saw no key (max kNoMax) counts 0.
     static_assert(NX == DB * 16 + 2, "exchange record: output, max, row sum");
     FA_LDS float* const xs = (FA_LDS float*)ring + wave * NX * 64 + lane;
     constexpr int XG = NW * NX * 64;  // floats per group
@@ -455,7 +502,7 @@ __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD))) v
     float m = m_run;
 #pragma unroll
     for (int p = 0; p < KSPLIT - 1; ++p) m = fmaxf(m, xs[p * XG + DB * 16 * 64]);
-    const float a0 = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m);
+    const float a0 = fast_exp2(m_run - m);  // 0 for a part that saw no key (kNoMax)
     l_run *= a0;
 #pragma unroll
     for (int db = 0; db < DB; ++db) oacc[db] *= a0;
@@ -463,7 +510,7 @@ __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD))) v
 #pragma unroll
     for (int p = 0; p < KSPLIT - 1; ++p) {
       const float mp = xs[p * XG + DB * 16 * 64];
-      ap[p] = (mp == -INFINITY) ? 0.f : fast_exp2(mp - m);
+      ap[p] = fast_exp2(mp - m);
       l_run += xs[p * XG + (DB * 16 + 1) * 64] * ap[p];
     }
     // One 32-column block at a time (keeps the loads in flight few).
