@@ -15,9 +15,9 @@
 //     row (both operands use the same byte order, so the reduction pairs
 //     them correctly); the descales of Q and K fold into the exp2 scale.
 //   * P is rounded to e4m3 for the PV product. It is taken as
-//     2^4 * exp2(s - m) with the running max allowed to lag by at most 2^4,
-//     so every value is <= 2^8 (the format holds 448) and values down to
-//     2^-10 still land on normal e4m3 numbers. The row sum uses the fp32
+//     2^4 * exp2(s - m) with the running max m allowed to lag as long as
+//     every value stays <= 448 (the largest e4m3 number), so values down
+//     to 2^-10 of the row maximum still land on normal e4m3 numbers. The row sum uses the fp32
 //     values; the scale cancels in O = (P V) / l and is removed from the
 //     logsumexp.
 //   * P^T comes straight from the S^T accumulators: with the V rows of a
@@ -53,7 +53,8 @@ constexpr int kF8BR = 128;                 // query rows per workgroup (4 waves 
 constexpr int kF8BC = 64;                  // keys per K/V tile
 constexpr int kF8Threads = 256;
 constexpr int kF8Tile = kF8BC * kF8D;      // bytes of one K or V tile
-constexpr float kF8Slack = 4.f;            // log2 units the running max may lag
+constexpr float kF8PMax = 448.f;           // largest finite e4m3 value
+constexpr float kF8NoMax = -1e30f;         // running max of a row that has seen no key
 constexpr float kF8Shift = 4.f;            // P is scaled by 2^4 before rounding
 
 __device__ __forceinline__ constexpr int f8_swz(int r) { return (((r >> 1) & 3) << 1) | ((r >> 3) & 1); }
@@ -135,7 +136,7 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(3, 3
   f32x16 oacc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) oacc[i] = f32x16{};
-  float m_run = -INFINITY;
+  float m_run = kF8NoMax;
   float l_run = 0.f;
 
   // Per-lane LDS offsets: K row reads (row l32 of a 32-key block, chunk
@@ -151,11 +152,10 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(3, 3
   for (int db = 0; db < 4; ++db) voff[db] = f8_slot(8 * g + (j16 >> 1), 2 * db + (G & 1)) + 8 * (j16 & 1);
 
   i32x8 pf = {};  // P^T operand of the current tile (kept across tiles)
-  auto compute = [&](int j, const char* kt, auto mask_tag) __attribute__((always_inline)) {
+  auto scores = [&](f32x16 (&s)[2], const char* kt, int key0, auto mask_tag) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
-    const int key0 = j * kF8BC;
-    const char* vt = kt + kF8Tile;
-    f32x16 s[2] = {f32x16{}, f32x16{}};
+    s[0] = f32x16{};
+    s[1] = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
@@ -172,22 +172,15 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(3, 3
           if ((CAUSAL && key > myq) || key >= N) s[kb][r] = -INFINITY;
         }
     }
-    float mx = max16(s[1], max16(s[0], -INFINITY));
-    mx = xhalf_max(mx);
-    const float tile_m = (mx == -INFINITY) ? -INFINITY : mx * c2;
-    const bool grow = tile_m > m_run + kF8Slack;
-    if (__builtin_amdgcn_ballot_w64(grow)) {
-      asm volatile("" ::: "memory");
-      const float m_new = grow ? tile_m : m_run;
-      const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
-      m_run = m_new;
-    }
-    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-    const float bias = kF8Shift - m_use;
-    // P^T operand: byte p = 2^4 * exp2(s - m) of accumulator p % 16 of block p / 16.
+  };
+  // The P^T operand (byte p = 2^4 * exp2(s - m) of accumulator p % 16 of
+  // block p / 16) from the scores and bias = 2^4 / m in log2 units; returns
+  // this lane's fp32 sum of the tile's P and, in gmax, the largest sum of
+  // one of its groups of four values.
+  auto probs = [&](const f32x16 (&s)[2], float bias, auto mask_tag, float& gmax) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    float t = 0.f;
+    gmax = 0.f;
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
       float e[4];
@@ -198,12 +191,57 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(3, 3
         if constexpr (MASK) x = (sv == -INFINITY) ? 0.f : x;
         e[i] = x;
       }
-      l_run += (e[0] + e[1]) + (e[2] + e[3]);
+      const float ws = (e[0] + e[1]) + (e[2] + e[3]);
+      t += ws;
+      gmax = vmax(gmax, ws);
       // The two conversions write the low and the high half of the word; the
       // other half starts as the previous tile's value (no zeroing move).
       int d = __builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], pf[w], false);
       pf[w] = __builtin_amdgcn_cvt_pk_fp8_f32(e[2], e[3], d, true);
     }
+    return t;
+  };
+  // As in the bf16 forward, the running max only moves when a value of P
+  // would leave e4m3's range: P is first taken from the current running max,
+  // and it stands if every group of four values of every lane sums to at
+  // most 448 (then every value is at most 448, the largest e4m3 number; with
+  // the running max at the row maximum a group sums to at most 4 * 2^4).
+  // Otherwise (and on the first tile) the scores are formed again, the row
+  // maxima taken, O and l rescaled and P recomputed. A row that has seen no
+  // key holds the finite kF8NoMax, for which every visible score overflows
+  // to +inf and takes that path.
+  auto compute = [&](int j, const char* kt, auto mask_tag, bool first) __attribute__((always_inline)) {
+    const int key0 = j * kF8BC;
+    const char* vt = kt + kF8Tile;
+    f32x16 s[2];
+    scores(s, kt, key0, mask_tag);
+    float t = 0.f;
+    bool slow = true;  // wave-uniform
+    if (!first) {
+      float gmax;
+      t = probs(s, kF8Shift - m_run, mask_tag, gmax);
+      slow = __builtin_amdgcn_ballot_w64(!(gmax <= kF8PMax)) != 0;
+    }
+    if (slow) {
+      asm volatile("" ::: "memory");  // a branch; the scores below are loaded again
+      if (!first) scores(s, kt, key0, mask_tag);
+      float mx = max16(s[1], max16(s[0], -INFINITY));
+      mx = xhalf_max(mx);
+      const float tile_m = (mx == -INFINITY) ? -INFINITY : mx * c2;
+      const bool grow = tile_m > m_run;
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+        asm volatile("" ::: "memory");
+        const float m_new = grow ? tile_m : m_run;
+        const float alpha = fast_exp2(m_run - m_new);  // 0 from kF8NoMax, 1 when unchanged
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
+        m_run = m_new;
+      }
+      float gmax;
+      t = probs(s, kF8Shift - m_run, mask_tag, gmax);
+    }
+    l_run += t;
     // O^T += V^T P^T: for each 32-column block of d, four transpose loads.
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
@@ -225,7 +263,7 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(3, 3
   int j = 0;
   for (; j < jm; ++j) {
     if (j + 1 < ntiles) issue(j + 1, ring[(j + 1) & 1]);
-    compute(j, ring[j & 1], std::false_type{});
+    compute(j, ring[j & 1], std::false_type{}, j == 0);
     wait_vmem();
     __syncthreads();
   }
@@ -234,7 +272,7 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(3, 3
     // (Non-causal: always true here; as a branch it keeps the register
     // allocator from spilling around the masked tile, which it does when
     // the call is unconditional.)
-    if (j * kF8BC <= (CAUSAL ? qw0 + 31 : N - 1)) compute(j, ring[j & 1], std::true_type{});
+    if (j * kF8BC <= (CAUSAL ? qw0 + 31 : N - 1)) compute(j, ring[j & 1], std::true_type{}, j == 0);
     wait_vmem();
     __syncthreads();
   }

@@ -43,7 +43,10 @@ def test_exact_and_rounded_results_are_inside():
         q, k, v, _ = _inputs(300, 20, causal)
         ro, _, _ = head_bound(q, k, v, causal, 0.088)
         assert _ratio(ro, q, k, v, causal, 0.088) < 1e-3
-        for c in (4.0, 6.0, 8.0):        # every scale the lagging running max allows
+        # every scale the lagging running max allows: P = 2^c exp2(s - max)
+        # from c = 4 (running max at the row maximum) up to a largest value
+        # of 448, the largest e4m3 number (c = log2(448))
+        for c in (4.0, 6.0, 8.0, float(np.log2(448.0))):
             assert _ratio(_emulate(q, k, v, causal, 0.088, c), q, k, v, causal, 0.088) <= 1.0
 
 
