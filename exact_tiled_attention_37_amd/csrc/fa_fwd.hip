@@ -350,15 +350,18 @@ __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD))) v
   // causal diagonal or the end of the sequence; all other tiles run the
   // variant without any per-element masking.
   // The running max m_run only has to move when a probability relative to
-  // it would exceed 2^8 (kRescaleSlack). Without a bias the tile's P is
-  // first taken from the current m_run; since P >= 0, a lane whose sum of
-  // the tile's P stays <= 2^8 has every value <= 2^8, so if no lane of the
-  // wave exceeds that, P stands and the tile needs no row maximum at all.
-  // Otherwise (and on the first tile, and always with a bias) the scores are
-  // formed again (the first pass consumed them; the K tile is still in LDS),
-  // the row maxima taken, m_run moved to them, O and l rescaled, and P
-  // recomputed. A row that has seen no key has m_run = kNoMax, for which
-  // every visible score overflows to +inf and takes the second path.
+  // it would exceed 2^8 (kRescaleSlack). The tile's P is first taken from
+  // the current m_run; since P >= 0, a lane whose sum of the tile's P stays
+  // <= 2^8 has every value <= 2^8, so if no lane of the wave exceeds that,
+  // P stands and the tile needs no row maximum at all. Otherwise (and on
+  // the first tile) the scores are formed again (the first pass consumed
+  // them; the K tile and the tile's bias are still in LDS), the row maxima
+  // taken, m_run moved to them, O and l rescaled, and P recomputed. A row
+  // that has seen no key has m_run = kNoMax, for which every visible score
+  // overflows to +inf and takes the second path. (The d = 64 bias form
+  // keeps the per-tile maximum: the registers of both paths do not fit its
+  // three waves per SIMD.)
+  constexpr bool FAST = !BIAS || D == 128;
   auto compute = [&](int j, const char* kt, auto mask_tag, auto&& mid, bool first) __attribute__((always_inline)) {
     const int key0 = j * kFwdBC;
     const char* vt = kt + TILE;
@@ -367,22 +370,21 @@ __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD))) v
     bf16x8 pf[2 * KB];
     float t = 0.f;
     bool slow = true;  // wave-uniform
-    if (!BIAS && !first) {
+    if (FAST && !first) {
       t = probs(s, m_run, pf, mask_tag);
       slow = __builtin_amdgcn_ballot_w64(!(t <= kPSumMax)) != 0;
     }
     if (slow) {
       asm volatile("" ::: "memory");  // a branch; the scores below are loaded again
-      if (!BIAS && !first) scores(s, kt, key0, mask_tag, []() {});
+      if (FAST && !first) scores(s, kt, key0, mask_tag, []() {});
       float mx = max16(s[0], -INFINITY);
 #pragma unroll
       for (int kb = 1; kb < KB; ++kb) mx = max16(s[kb], mx);
       mx = xhalf_max(mx);
       const float tile_m = (mx == -INFINITY) ? -INFINITY : (BIAS ? mx : mx * c2);
-      // With a bias, only a growth beyond the slack moves m_run (the same
-      // rule, taken from the maxima); without one, the second path moves
-      // it to the tile's maximum.
-      const bool grow = BIAS ? tile_m > m_run + kRescaleSlack : tile_m > m_run;
+      // The second path moves m_run to the tile's maximum (the d = 64 bias
+      // form, which has no first path, keeps the slack rule).
+      const bool grow = FAST ? tile_m > m_run : tile_m > m_run + kRescaleSlack;
       if (__builtin_amdgcn_ballot_w64(grow)) {  // wave-uniform
         asm volatile("" ::: "memory");          // keep it a branch (no speculation)
         const float m_new = grow ? tile_m : m_run;
