@@ -17,7 +17,8 @@
 //      like the forward pass; each wave owns 32 rows and keeps their Q, dO
 //      rows and the dQ accumulator in registers while K/V tiles stream
 //      through LDS. Its prologue also forms the row terms of its rows,
-//      D = rowsum(dO * O) and L * log2(e), and writes them for kernel 2.
+//      D = rowsum(dO * O) and L * log2(e), and writes them (D negated) for
+//      kernel 2.
 //      Per tile:
 //        S^T = K Q^T, dP^T = V dO^T        (lane l owns query row l % 32)
 //        P^T, dS^T elementwise             (L, D of the lane's own row)
@@ -26,7 +27,8 @@
 //      4 wavefronts owns 32 keys and keeps their K, V rows and the dK, dV
 //      accumulators in registers, while 32-row blocks of Q and dO stream
 //      through double-buffered LDS (loaded straight into LDS). Per block:
-//        S = Q K^T, dP = dO V^T            (lane l owns key l % 32)
+//        S = Q K^T, dP - D = dO V^T - D    (lane l owns key l % 32; the dP
+//                                           accumulators start from -D)
 //        P, dS elementwise                 (L, D per row from LDS)
 //        dV^T += dO^T P, dK^T += Q^T dS    (dO^T, Q^T by LDS transpose reads)
 // Splitting dQ from dK/dV costs two extra products per tile pair (S and dP
@@ -198,7 +200,15 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) bt[rq] = lds_read_tr(bsl, (int)bias_tr_addr + 512 * rq);
     }
-    f32x16 s = f32x16{}, dp = f32x16{};
+    // dP starts from -D of the accumulator's rows (the row terms hold -D),
+    // so the products leave dP - D in it.
+    f32x16 s = f32x16{}, dp;
+#pragma unroll
+    for (int rq4 = 0; rq4 < 4; ++rq4) {
+      const f32x4 nd4 = *reinterpret_cast<const FA_LDS f32x4*>((const FA_LDS float*)rows + 64 + 8 * rq4 + 4 * g);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dp[4 * rq4 + e] = nd4[e];
+    }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       s = mfma32(TQ::row8(qt, l32, 2 * ks + g), kf[ks], s);
@@ -209,7 +219,6 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
     for (int rq4 = 0; rq4 < 4; ++rq4) {
       const int qi0 = 8 * rq4 + 4 * g;
       const f32x4 l4 = *reinterpret_cast<const FA_LDS f32x4*>((const FA_LDS float*)rows + qi0);
-      const f32x4 d4 = *reinterpret_cast<const FA_LDS f32x4*>((const FA_LDS float*)rows + 64 + qi0);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * rq4 + e;
@@ -221,7 +230,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
           p = fast_exp2(__builtin_fmaf(s[r], c2, -l4[e]));
         if constexpr (MASK) p = (mykey > q0 + qi0 + e) ? 0.f : p;
         p8[r >> 3][r & 7] = p;
-        ds8[r >> 3][r & 7] = p * (dp[r] - d4[e]);
+        ds8[r >> 3][r & 7] = p * dp[r];
       }
     }
     if constexpr (BIAS) {
@@ -378,7 +387,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
       dd = dsum_row;
       if (g == 0) {
         lse2[i] = l2;
-        dsum[i] = dd;
+        dsum[i] = -dd;  // -D: the dK/dV kernel starts its dP accumulators from it
       }
     }
   }
