@@ -461,7 +461,13 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
     const char* vt = kt + TILE;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      f32x16 s = f32x16{}, dp = f32x16{};
+      // Without a bias dP^T starts from -D (the lane's row term, a block the
+      // compiler keeps outside the loop as the first product's addend), so
+      // the products leave dP - D in it; the bias form, short of registers
+      // for that block, subtracts D per element.
+      f32x16 s = f32x16{}, dp;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dp[r] = BIAS ? 0.f : -dd;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         s = mfma32(T::row8(kt, kb * 32 + l32, 2 * ks + g), qf[ks], s);
@@ -496,7 +502,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
             const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
             p = ((CAUSAL && key > myq) || key >= N) ? 0.f : p;
           }
-          x[s8] = p * (dp[r] - dd);
+          x[s8] = p * (BIAS ? dp[r] - dd : dp[r]);
         }
         dsf[hh] = to_bf16x8(x);
       }
