@@ -338,6 +338,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
 
   const int qw0 = qblk * kQBlock + wave * 32;
   const int myq = qw0 + l32;
+  const int key_lim = CAUSAL ? min(myq, N - 1) : N - 1;  // the last key this lane's row sees
   // Bias rows of this (batch, head): N rows of bias_srow elements; a tile's
   // 32 rows x 64 keys per wave go straight into the wave's LDS slice (four
   // whole-wave LDS-DMA loads; lane i fills 16-byte slot 64 t + i, i.e. row
@@ -500,7 +501,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
             // would turn the row into NaN (with a bias their bias is row
             // padding as well).
             const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-            p = ((CAUSAL && key > myq) || key >= N) ? 0.f : p;
+            p = key > key_lim ? 0.f : p;
           }
           x[s8] = p * (BIAS ? dp[r] - dd : dp[r]);
         }

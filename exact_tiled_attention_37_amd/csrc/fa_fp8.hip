@@ -104,6 +104,7 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(3, 3
 
   const int qw0 = qblk * kF8BR + wave * 32;
   const int myq = qw0 + l32;
+  const int key_lim = CAUSAL ? min(myq, N - 1) : N - 1;  // the last key this lane's row sees
 
   // Q as the B operand: bytes 64 ks + 32 g .. +31 of row myq.
   i32x8 qf[2];
@@ -169,7 +170,7 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(3, 3
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-          if ((CAUSAL && key > myq) || key >= N) s[kb][r] = -INFINITY;
+          if (key > key_lim) s[kb][r] = -INFINITY;
         }
     }
   };

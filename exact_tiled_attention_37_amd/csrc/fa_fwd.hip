@@ -182,6 +182,8 @@ __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD))) v
 
   const int qw0 = qblk * kFwdBR + wave * 32;       // first query row of this wave
   const int myq = qw0 + l32;
+  // The last key this lane's row sees (masked tiles: one compare per score).
+  const int key_lim = CAUSAL ? min(myq + delta, Nk - 1) : Nk - 1;
 
   // Bias rows of this (batch, head), each bias_srow elements of readable
   // memory (the 8-byte loads of a row's last keys reach into its padding);
@@ -314,7 +316,7 @@ __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD))) v
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-          if ((CAUSAL && key > myq + delta) || key >= Nk) s[kb][r] = -INFINITY;
+          if (key > key_lim) s[kb][r] = -INFINITY;
         }
     }
   };
