@@ -212,11 +212,47 @@ def draw_fp8(B: int, N: int, H: int, d: int, seed: int):
     rng = np.random.Generator(np.random.PCG64(seed))
     out = {}
     for name in ("q", "k", "v"):
-        x = rng.standard_normal((B, N, H, d), dtype=np.float32)
-        amax = np.abs(x).max(axis=(1, 3)).astype(np.float32)            # [B, H]
-        desc = (amax / np.float32(FP8_INPUT_AMAX)).astype(np.float32)
-        out[name] = f64_to_e4m3_bits(x.astype(np.float64) / desc.astype(np.float64)[:, None, :, None])
-        out[name + "_descale"] = desc
+        out[name], out[name + "_descale"] = quantize_e4m3(rng.standard_normal((B, N, H, d), dtype=np.float32))
+    return out
+
+
+def quantize_e4m3(x: np.ndarray):
+    """float32 x [B, N, H, d] as e4m3 codes with one float32 descale per
+    (batch, head), D = max|x| / 224: returns (codes, D [B, H])."""
+    amax = np.abs(x).max(axis=(1, 3)).astype(np.float32)            # [B, H]
+    desc = (amax / np.float32(FP8_INPUT_AMAX)).astype(np.float32)
+    return f64_to_e4m3_bits(x.astype(np.float64) / desc.astype(np.float64)[:, None, :, None]), desc
+
+
+def growing_scores_f32(B: int, N: int, H: int, d: int, seed: int, span: float):
+    """Q, K, V, dO (float32) whose scores grow along the keys: queries are
+    1 + 0.1 z and key j is t_j + 0.1 z in every column, with t_j running
+    linearly from -span to +span over the N keys (z standard normal), so a
+    row's largest score keeps moving to later keys (by about span * d *
+    scale * 2 / N per key). V and dO are standard normal. One PCG64 stream,
+    draws in the order Q, K, V, dO."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    t = np.linspace(-span, span, N, dtype=np.float32)[None, :, None, None]
+    q = 1.0 + 0.1 * rng.standard_normal((B, N, H, d), dtype=np.float32)
+    k = t + 0.1 * rng.standard_normal((B, N, H, d), dtype=np.float32)
+    v = rng.standard_normal((B, N, H, d), dtype=np.float32)
+    do = rng.standard_normal((B, N, H, d), dtype=np.float32)
+    return {"q": q, "k": k.astype(np.float32), "v": v, "do": do}
+
+
+def draw_growing_scores(B: int, N: int, H: int, d: int, seed: int, span: float):
+    """growing_scores_f32 rounded to bf16 bits."""
+    x = growing_scores_f32(B, N, H, d, seed, span)
+    return {n: f32_to_bf16_bits(x[n]) for n in ("q", "k", "v", "do")}
+
+
+def draw_fp8_growing_scores(B: int, N: int, H: int, d: int, seed: int, span: float):
+    """Q, K, V of growing_scores_f32 as e4m3 codes with per-(batch, head)
+    descales (as in draw_fp8)."""
+    x = growing_scores_f32(B, N, H, d, seed, span)
+    out = {}
+    for name in ("q", "k", "v"):
+        out[name], out[name + "_descale"] = quantize_e4m3(x[name])
     return out
 
 

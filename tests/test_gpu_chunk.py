@@ -111,6 +111,26 @@ def test_chunk_small(case, causal):
     check_chunk(f64(o), f64(lse), ro, rl)
 
 
+@pytest.mark.parametrize("span", [4.0, 16.0], ids=["span4", "span16"])
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_chunk_growing_scores(causal, span):
+    """A chunk of scores that grow along the keys (the row maxima keep moving
+    to later tiles) at a causal offset, on the d = 128 form whose wave
+    groups split the key tiles and combine their running maxima."""
+    import torch
+
+    B, Nq, Nk, H, d, qs, ks = 1, 300, 700, 2, 128, 520, 17
+    scale = 1.0 / math.sqrt(d)
+    announce(f"chunk growing scores causal={causal} span={span}")
+    bits = si.draw_growing_scores(B, max(Nq, Nk), H, d, 7100 + int(span), span)
+    qb, kb, vb = bits["q"][:, :Nq].copy(), bits["k"][:, :Nk].copy(), bits["v"][:, :Nk].copy()
+    ro, rl = oracle.attention_forward_chunk(si.bf16_bits_to_f64(qb), si.bf16_bits_to_f64(kb),
+                                            si.bf16_bits_to_f64(vb), causal, scale, qs, ks)
+    o, lse = fa.fa_fwd_chunk(dev(qb), dev(kb), dev(vb), causal, qs, ks, scale)
+    torch.cuda.synchronize()
+    check_chunk(f64(o), f64(lse), ro, rl)
+
+
 @pytest.mark.parametrize("d", [64, 128])
 def test_empty_chunk(d):
     import torch

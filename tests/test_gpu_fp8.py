@@ -106,6 +106,26 @@ def test_fp8_small(shape, causal):
                        causal, scale, what=f"b{bb} h{h}")
 
 
+@pytest.mark.parametrize("span", [4.0, 16.0], ids=["span4", "span16"])
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_fp8_growing_scores(causal, span):
+    """Scores that grow along the keys: with span 16 a tile's P taken from
+    the running maximum leaves e4m3's range on nearly every tile and is taken
+    again from the tile's own row maxima; with span 4 it stays within 448
+    while the running maximum lags. Every element within the derived bound."""
+    B, N, H, d = 1, 1000, 2, 128
+    scale = 1.0 / math.sqrt(d)
+    announce(f"fp8 growing scores causal={causal} span={span}")
+    b8 = si.draw_fp8_growing_scores(B, N, H, d, 7200 + int(span), span)
+    o, lse = run(b8, causal, scale)
+    q, k, v = deq(b8, "q"), deq(b8, "k"), deq(b8, "v")
+    ro, rl = oracle.attention_forward_fp8(b8["q"], b8["k"], b8["v"], b8["q_descale"], b8["k_descale"],
+                                          b8["v_descale"], causal, scale)
+    for h in range(H):
+        check_head(o[0, :, h], lse[0, h], ro[0, :, h], rl[0, h], q[0, :, h], k[0, :, h], v[0, :, h],
+                   causal, scale, what=f"h{h}")
+
+
 @pytest.mark.parametrize("qd_sign", [1.0, -1.0], ids=["pos", "neg"])
 def test_fp8_descales(qd_sign):
     """Descales far from 1 and a negative Q descale (negates the scores)."""

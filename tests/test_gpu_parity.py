@@ -189,6 +189,51 @@ def test_very_negative_logsumexp_ragged_keys(d, causal):
         check(name, got, ref, max(MAX_TOL * m, MODEL_MARGIN * mmax), max(MEAN_TOL * m, MODEL_MARGIN * mmean))
 
 
+def tile_growth_share(q, k, causal, scale, tile=32):
+    """Share of (row, key tile) pairs, past a row's first tile, where the
+    row's running maximum of the scores (log2 units) grows by more than 8:
+    the tiles whose probabilities, taken from the previous maximum, would
+    exceed 2^8."""
+    s = np.einsum("bihc,bjhc->bhij", q, k) * scale / np.log(2.0)
+    N = k.shape[1]
+    if causal:
+        s = np.where(np.arange(N)[None, :] > np.arange(s.shape[2])[:, None], -np.inf, s)
+    nt = (N + tile - 1) // tile
+    tmax = np.stack([s[..., t * tile:(t + 1) * tile].max(axis=-1) for t in range(nt)], axis=-1)
+    run = np.maximum.accumulate(tmax, axis=-1)
+    grow = (tmax[..., 1:] > run[..., :-1] + 8.0) & np.isfinite(run[..., :-1])
+    seen = np.isfinite(run[..., :-1]) & np.isfinite(tmax[..., 1:])
+    return float(grow.sum() / max(1, seen.sum()))
+
+
+@pytest.mark.parametrize("H", [2, 34], ids=["H2", "H34"])
+@pytest.mark.parametrize("span", [4.0, 16.0], ids=["span4", "span16"])
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_growing_scores_forward(d, causal, span, H):
+    """Scores that grow along the keys, so each row's maximum keeps moving to
+    later tiles. With span 16 the probabilities a tile takes from the running
+    maximum overflow the 2^8 bound on nearly every tile, and the tile is
+    taken again from its own row maxima; with span 4 they stay within it
+    while the running maximum lags by several units. N = 1000 leaves a ragged
+    last tile; at d = 128, 2 heads (16 workgroups) run the form whose wave
+    groups split the keys and 34 heads (272) the plain one. O and the
+    logsumexp are compared whole with the oracle."""
+    B, N = 1, 1000
+    scale = 1.0 / math.sqrt(d)
+    seed = 7000 + d + 2 * int(causal) + int(span)
+    announce(f"growing scores d={d} causal={causal} span={span} H={H} seed={seed}")
+    bits = si.draw_growing_scores(B, N, H, d, seed, span)
+    q64, k64, v64 = (si.bf16_bits_to_f64(bits[n]) for n in ("q", "k", "v"))
+    share = tile_growth_share(q64[:, :, :1], k64[:, :, :1], causal, scale)
+    if span >= 16.0:
+        assert share > 0.5, f"input does not exercise the rescale path (share {share:.2f})"
+    ro, rl = oracle.attention_forward(q64, k64, v64, causal, scale)
+    _, _, _, o, lse = gpu_fwd(bits, causal, scale)
+    check("O", f64(o), ro)
+    check("LSE", f64(lse), rl, LSE_TOL, LSE_TOL)
+
+
 # ---------------------------------------------------------------------------
 # closed forms and exact properties on the GPU
 
