@@ -267,7 +267,9 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   for (; step < sm; ++step) {
     const int t = (step - s0) & 1;
     if (step + 1 < nqs) issue(step + 1, qbuf[t ^ 1], rowbuf[t ^ 1]);
-    compute(step, qbuf[t], rowbuf[t], std::true_type{});
+    // A wave whose keys all follow the step's queries has nothing to add
+    // (with a bias the step still runs: it issues the next step's bias).
+    if (BIAS || step * kQStep + kQStep - 1 >= kw0) compute(step, qbuf[t], rowbuf[t], std::true_type{});
     wait_vmem();
     __syncthreads();
   }
@@ -554,7 +556,9 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
     if constexpr (BIAS) bias_issue(j);
     kv_prefetched = j + 1 < ntiles;
     if (kv_prefetched) issue(j + 1, kvbuf[(j + 1) & 1]);
-    compute(j, kvbuf[j & 1], std::true_type{});
+    // A tile whose keys all follow this wave's rows adds nothing (with a
+    // bias it still runs: it writes the tile's dBias, zeros there).
+    if (BIAS || !CAUSAL || j * kKTile <= qw0 + 31) compute(j, kvbuf[j & 1], std::true_type{});
     wait_vmem();
     __syncthreads();
   }
