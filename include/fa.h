@@ -78,7 +78,7 @@ FA_API fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, fl
 
 /*
  * Bytes of device workspace fa_bwd needs for this problem size: two float32
- * [B, H, N] arrays (the row terms D = rowsum(dO * O) and L * log2(e)), each
+ * [B, H, N] arrays (the row terms -D = -rowsum(dO * O) and L * log2(e)), each
  * starting on a 256-byte boundary. Returns 0 for an invalid shape.
  */
 FA_API size_t fa_bwd_workspace_bytes(int B, int N, int H, int d);
