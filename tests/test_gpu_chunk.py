@@ -91,6 +91,8 @@ CHUNKS = [
     (1, 257, 129, 3, 128, 129, 64),
     (1, 33, 1, 1, 64, 5, 5),
     (2, 300, 700, 2, 128, 520, 17),
+    (1, 64, 20001, 2, 128, 30000, 0),  # d = 128, 2 workgroups: the split form over 313 tiles
+    (1, 64, 20001, 1, 128, 19950, 0),  # causal: the last ~50 keys partly hidden
 ]
 
 
