@@ -12,10 +12,14 @@ from .attention import (
     attention_forward,
     attention_forward_bias,
     attention_forward_fp8,
+    attention_forward_mxfp8,
     attention_forward_chunk,
     attention_forward_rows,
     dequantize_fp8,
+    dequantize_mx_cols,
+    dequantize_mx_rows,
     e4m3_decode,
+    e8m0_decode,
     merge_chunks,
 )
 
@@ -32,4 +36,8 @@ __all__ = [
     "e4m3_decode",
     "dequantize_fp8",
     "attention_forward_fp8",
+    "e8m0_decode",
+    "dequantize_mx_rows",
+    "dequantize_mx_cols",
+    "attention_forward_mxfp8",
 ]

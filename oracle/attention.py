@@ -403,3 +403,41 @@ def attention_forward_fp8(q8, k8, v8, q_descale, k_descale, v_descale, causal: b
     Returns (O [B, N, H, d], L [B, H, N]) in float64."""
     return attention_forward(dequantize_fp8(q8, q_descale), dequantize_fp8(k8, k_descale),
                              dequantize_fp8(v8, v_descale), causal, scale)
+
+
+# Microscaled FP8 inputs. The same abstract speaks of narrow-format matrix
+# units; the MI355X ones take, besides the FP8 codes, one power-of-two scale
+# per block of 32 consecutive elements along the reduction dimension (the OCP
+# Microscaling (MX) layout: the scale is an 8-bit exponent, E8M0, standing for
+# 2^(code - 127), code 255 being NaN). Reading: Q and K carry one scale per
+# 32 consecutive head-dimension elements of a token (the reduction of
+# Q K^T), V one per 32 consecutive tokens of a head-dimension column (the
+# reduction of P V); attention is computed exactly on the values the codes and
+# scales stand for.
+
+
+def e8m0_decode(codes):
+    """Values of E8M0 scale codes: 2^(code - 127) for codes 0..254, NaN for 255."""
+    c = np.asarray(codes, dtype=np.int64)
+    return np.where(c == 255, np.nan, np.exp2(c.astype(np.float64) - 127.0))
+
+
+def dequantize_mx_rows(codes, scales):
+    """codes [B, N, H, d] (e4m3) and scales [B, N, H, d / 32] (E8M0): element
+    (b, n, h, i) stands for e4m3(code) * 2^(scales[b, n, h, i // 32] - 127)."""
+    return e4m3_decode(codes) * np.repeat(e8m0_decode(scales), 32, axis=3)
+
+
+def dequantize_mx_cols(codes, scales):
+    """codes [B, N, H, d] (e4m3) and scales [B, ceil(N / 32), H, d] (E8M0):
+    element (b, n, h, i) stands for e4m3(code) * 2^(scales[b, n // 32, h, i] - 127)."""
+    n = np.asarray(codes).shape[1]
+    return e4m3_decode(codes) * np.repeat(e8m0_decode(scales), 32, axis=1)[:, :n]
+
+
+def attention_forward_mxfp8(q8, q_scale, k8, k_scale, v8, v_scale, causal: bool, scale: float):
+    """Attention on microscaled FP8 inputs: the plain forward on the values
+    the codes and block scales stand for. Returns (O [B, N, H, d], L [B, H, N])."""
+    return attention_forward(dequantize_mx_rows(q8, q_scale), dequantize_mx_rows(k8, k_scale),
+                             dequantize_mx_cols(v8, v_scale), causal, scale)
+

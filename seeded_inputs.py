@@ -102,6 +102,18 @@ FP8_WORKLOADS = {
 # the format holds), leaving headroom.
 FP8_INPUT_AMAX = 224.0
 
+# Microscaled FP8 forward workloads (the same shapes): Q, K, V as e4m3 codes
+# with one E8M0 scale per 32 consecutive elements along the reduction
+# dimension of the product each enters (Q and K: along d; V: along tokens).
+MXFP8_WORKLOADS = {
+    "mxfp8_train_causal": Workload("mxfp8_train_causal", 4, 16, 4096, 128, True, False, 12),
+    "mxfp8_long_causal": Workload("mxfp8_long_causal", 1, 16, 16384, 128, True, False, 13),
+}
+# Exponent of the largest power of two an e4m3 code holds (448 = 1.75 * 2^8):
+# the OCP MX rule scales a block so that its largest magnitude lands in
+# [2^8, 2^9) before rounding (values above 448 saturate).
+E4M3_EMAX = 8
+
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round fp32 to bfloat16 (round to nearest, ties to even); return uint16 bits.
@@ -222,6 +234,62 @@ def quantize_e4m3(x: np.ndarray):
     amax = np.abs(x).max(axis=(1, 3)).astype(np.float32)            # [B, H]
     desc = (amax / np.float32(FP8_INPUT_AMAX)).astype(np.float32)
     return f64_to_e4m3_bits(x.astype(np.float64) / desc.astype(np.float64)[:, None, :, None]), desc
+
+
+def mx_scale_codes(amax: np.ndarray) -> np.ndarray:
+    """E8M0 codes of the OCP MX shared scale for e4m3 blocks with largest
+    magnitude amax: X = floor(log2(amax)) - 8, code X + 127 (clamped to
+    0..254; an all-zero block takes code 0)."""
+    a = np.asarray(amax, dtype=np.float64)
+    x = np.floor(np.log2(np.where(a > 0, a, 1.0))) - E4M3_EMAX
+    return np.where(a > 0, np.clip(x + 127, 0, 254), 0).astype(np.uint8)
+
+
+def quantize_mx_rows(x: np.ndarray):
+    """float32 x [B, N, H, d] as e4m3 codes with one E8M0 scale per 32
+    consecutive elements of a token along d: returns (codes [B, N, H, d],
+    scales [B, N, H, d / 32])."""
+    B, N, H, d = x.shape
+    xb = x.astype(np.float64).reshape(B, N, H, d // 32, 32)
+    sc = mx_scale_codes(np.abs(xb).max(axis=4))
+    codes = f64_to_e4m3_bits(xb / np.exp2(sc.astype(np.float64) - 127.0)[..., None])
+    return codes.reshape(B, N, H, d), sc
+
+
+def quantize_mx_cols(x: np.ndarray):
+    """float32 x [B, N, H, d] as e4m3 codes with one E8M0 scale per 32
+    consecutive tokens of a column (the last block holds N % 32 tokens when
+    N is not a multiple of 32): returns (codes [B, N, H, d], scales
+    [B, ceil(N / 32), H, d])."""
+    B, N, H, d = x.shape
+    nb = (N + 31) // 32
+    xp = np.zeros((B, nb * 32, H, d))
+    xp[:, :N] = x
+    xb = xp.reshape(B, nb, 32, H, d)
+    sc = mx_scale_codes(np.abs(xb).max(axis=2))
+    codes = f64_to_e4m3_bits(xb / np.exp2(sc.astype(np.float64) - 127.0)[:, :, None])
+    return np.ascontiguousarray(codes.reshape(B, nb * 32, H, d)[:, :N]), sc
+
+
+def _mx_quantize(x):
+    q, qs = quantize_mx_rows(x["q"])
+    k, ks = quantize_mx_rows(x["k"])
+    v, vs = quantize_mx_cols(x["v"])
+    return {"q": q, "q_scale": qs, "k": k, "k_scale": ks, "v": v, "v_scale": vs}
+
+
+def draw_mxfp8(B: int, N: int, H: int, d: int, seed: int):
+    """Q, K, V drawn as in draw_fp8 (float32 N(0,1), one PCG64 stream, in the
+    order Q, K, V), quantized with block scales: Q and K by quantize_mx_rows,
+    V by quantize_mx_cols. Returns uint8 codes q, k, v and uint8 E8M0 scales
+    q_scale, k_scale, v_scale."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return _mx_quantize({n: rng.standard_normal((B, N, H, d), dtype=np.float32) for n in ("q", "k", "v")})
+
+
+def draw_mxfp8_growing_scores(B: int, N: int, H: int, d: int, seed: int, span: float):
+    """Q, K, V of growing_scores_f32 with block scales (as in draw_mxfp8)."""
+    return _mx_quantize(growing_scores_f32(B, N, H, d, seed, span))
 
 
 def growing_scores_f32(B: int, N: int, H: int, d: int, seed: int, span: float):

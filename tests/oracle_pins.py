@@ -679,6 +679,84 @@ def pin_fp8_forward(mod):
         _close(l2, lse, what="only the product of the Q and K descales matters")
 
 
+def pin_e8m0_decode(mod):
+    """The E8M0 scale decode against values fixed by the format (2^-127 at
+    code 0, 1 at 127, 2^127 at 254, NaN at 255) and, for all 256 codes,
+    against torch's independent float8_e8m0fnu implementation."""
+    import torch
+
+    dec = mod.e8m0_decode(np.arange(256))
+    fixed = {0: 2.0 ** -127, 1: 2.0 ** -126, 126: 0.5, 127: 1.0, 128: 2.0, 130: 8.0, 254: 2.0 ** 127}
+    for code, val in fixed.items():
+        assert dec[code] == val, f"code {code}: {dec[code]} != {val}"
+    assert np.isnan(dec[255])
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    both_nan = np.isnan(ref) & np.isnan(dec)
+    assert np.all(both_nan | (ref == dec)), "decode differs from torch float8_e8m0fnu"
+
+
+def _mx_values_by_loops(mod, codes, scales, along_tokens):
+    """Values of microscaled codes element by element (the block of element
+    (b, n, h, i) is i // 32 of its token, or n // 32 of its column)."""
+    B, N, H, d = codes.shape
+    out = np.empty((B, N, H, d))
+    for b in range(B):
+        for n in range(N):
+            for h in range(H):
+                for i in range(d):
+                    sc = scales[b, n // 32, h, i] if along_tokens else scales[b, n, h, i // 32]
+                    out[b, n, h, i] = float(mod.e4m3_decode(codes[b, n, h, i])) * 2.0 ** (int(sc) - 127)
+    return out
+
+
+def pin_mxfp8_forward(mod):
+    """Microscaled FP8 attention is the forward on the values the codes and
+    block scales stand for: checked against scalar loops (37 tokens: a short
+    last block of V; d = 64: two blocks per Q and K token). All scales at
+    2^0 reduce it to the per-head FP8 form with unit descales; one V block
+    scaled up by 2 adds exactly that block's share of P V once more; Q
+    scales raised by one double the scores; Q and K blocks shifted in
+    opposite directions leave the result unchanged."""
+    B, N, H, d = 1, 37, 2, 64
+    rng = np.random.Generator(np.random.PCG64(351))
+    codes = [rng.integers(0, 0x7F, (B, N, H, d)).astype(np.uint8) | (rng.integers(0, 2, (B, N, H, d)) * 0x80).astype(np.uint8)
+             for _ in range(3)]
+    qs = rng.integers(118, 124, (B, N, H, d // 32)).astype(np.uint8)
+    ks = rng.integers(118, 124, (B, N, H, d // 32)).astype(np.uint8)
+    vs = rng.integers(110, 140, (B, (N + 31) // 32, H, d)).astype(np.uint8)
+    for causal in (False, True):
+        o, lse = mod.attention_forward_mxfp8(codes[0], qs, codes[1], ks, codes[2], vs, causal, 0.5)
+        vals = [_mx_values_by_loops(mod, codes[0], qs, False), _mx_values_by_loops(mod, codes[1], ks, False),
+                _mx_values_by_loops(mod, codes[2], vs, True)]
+        ob, lseb = _brute_forward(*vals, causal, 0.5)
+        _close(o, ob, 1e-13, what="mxfp8 brute output")
+        _close(lse, lseb, 1e-13, what="mxfp8 brute lse")
+        one = lambda a: np.full(a.shape, 127, np.uint8)
+        o1, l1 = mod.attention_forward_mxfp8(codes[0], one(qs), codes[1], one(ks), codes[2], one(vs), causal, 0.5)
+        unit = np.ones((B, H))
+        of, lf = mod.attention_forward_fp8(*codes, unit, unit, unit, causal, 0.5)
+        _close(o1, of, 1e-13, what="unit block scales = per-head form")
+        _close(l1, lf, 1e-13, what="unit block scales = per-head form (lse)")
+        vs2 = vs.copy()
+        vs2[0, 1, :, 5] += 1
+        o2, l2 = mod.attention_forward_mxfp8(codes[0], qs, codes[1], ks, codes[2], vs2, causal, 0.5)
+        vblk = np.zeros_like(vals[2])
+        vblk[0, 32:, :, 5] = vals[2][0, 32:, :, 5]
+        extra, _ = mod.attention_forward(vals[0], vals[1], vblk, causal, 0.5)
+        _close(o2, o + extra, what="V block scale doubles that block's share")
+        _close(l2, lse, what="V scales leave the logsumexp")
+        o3, l3 = mod.attention_forward_mxfp8(codes[0], qs + 1, codes[1], ks, codes[2], vs, causal, 0.5)
+        o4, l4 = mod.attention_forward_mxfp8(codes[0], qs, codes[1], ks, codes[2], vs, causal, 1.0)
+        _close(o3, o4, what="Q scales + 1 = doubled softmax scale")
+        _close(l3, l4, what="Q scales + 1 = doubled softmax scale (lse)")
+        qs5, ks5 = qs.copy(), ks.copy()
+        qs5[..., 1] += 2
+        ks5[..., 1] -= 2
+        o5, l5 = mod.attention_forward_mxfp8(codes[0], qs5, codes[1], ks5, codes[2], vs, causal, 0.5)
+        _close(o5, o, 1e-13, what="opposite Q and K block shifts cancel")
+        _close(l5, lse, 1e-13, what="opposite Q and K block shifts cancel (lse)")
+
+
 FORWARD_PINS = [
     pin_rows_sum_to_one,
     pin_q_zero,
@@ -707,6 +785,8 @@ BIAS_PINS = [
 FP8_PINS = [
     pin_e4m3_decode,
     pin_fp8_forward,
+    pin_e8m0_decode,
+    pin_mxfp8_forward,
 ]
 BACKWARD_PINS = [
     pin_constant_v,

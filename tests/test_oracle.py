@@ -114,6 +114,12 @@ MUTATIONS = [
     ("fp8 Q takes the K descale", "return attention_forward(dequantize_fp8(q8, q_descale),",
      "return attention_forward(dequantize_fp8(q8, k_descale),"),
     ("fp8 V descale dropped", "dequantize_fp8(v8, v_descale), causal, scale)", "dequantize_fp8(v8, v_descale * 0 + 1), causal, scale)"),
+    ("e8m0 bias 128", "np.exp2(c.astype(np.float64) - 127.0))", "np.exp2(c.astype(np.float64) - 128.0))"),
+    ("e8m0 NaN code", "np.where(c == 255, np.nan,", "np.where(c == 254, np.nan,"),
+    ("mx V block offset", "np.repeat(e8m0_decode(scales), 32, axis=1)[:, :n]", "np.repeat(e8m0_decode(scales), 32, axis=1)[:, 1:n + 1]"),
+    ("mx row blocks interleaved", "np.repeat(e8m0_decode(scales), 32, axis=3)", "np.tile(e8m0_decode(scales), (1, 1, 1, 32))"),
+    ("mx K takes the Q scales", "dequantize_mx_rows(k8, k_scale)", "dequantize_mx_rows(k8, q_scale)"),
+    ("mx V scales dropped", "dequantize_mx_cols(v8, v_scale), causal, scale)", "dequantize_mx_cols(v8, v_scale * 0 + 127), causal, scale)"),
     ("head slice swapped", "sl = (slice(b, b + 1), slice(None), slice(h, h + 1), slice(None))",
      "sl = (slice(h, h + 1), slice(None), slice(b, b + 1), slice(None))"),
 ]
