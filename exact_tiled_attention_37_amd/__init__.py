@@ -34,6 +34,7 @@ __all__ = [
     "fa_fwd_bias",
     "fa_bwd_bias",
     "fa_fwd_fp8",
+    "fa_fwd_mxfp8",
     "fa_status_string",
     "fa_version",
     "EXPORTED_SYMBOLS",
@@ -43,7 +44,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libfa_mi355x.so"
 EXPORTED_SYMBOLS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd_chunk", "fa_merge", "fa_decode",
                     "fa_decode_workspace_bytes", "fa_decode_noalloc", "fa_fwd_bias", "fa_bwd_bias", "fa_fwd_fp8",
-                    "fa_status_string", "fa_version")
+                    "fa_fwd_mxfp8", "fa_status_string", "fa_version")
 
 _lib = None
 
@@ -94,6 +95,8 @@ def load_library():
     lib.fa_bwd_bias.restype = i
     lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
     lib.fa_fwd_fp8.restype = i
+    lib.fa_fwd_mxfp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
+    lib.fa_fwd_mxfp8.restype = i
     lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i]
     lib.fa_bwd_workspace_bytes.restype = sz
     lib.fa_status_string.argtypes = [i]
@@ -466,4 +469,41 @@ def fa_fwd_fp8(q8, k8, v8, q_descale, k_descale, v_descale, causal: bool, softma
     )
     if st != 0:
         raise FaError(st, "fa_fwd_fp8")
+    return out, lse
+
+
+def fa_fwd_mxfp8(q8, q_scale, k8, k_scale, v8, v_scale, causal: bool, softmax_scale: Optional[float] = None,
+                 out=None, lse=None):
+    """Microscaled FP8 forward: q8, k8, v8 are uint8 e4m3 codes [B, N, H, 128];
+    q_scale, k_scale uint8 E8M0 [B, N, H, 4] (one per 32 consecutive d of a
+    token); v_scale uint8 E8M0 [B, ceil(N / 32), H, 128] (one per 32
+    consecutive tokens of a column). Returns (o bf16 [B, N, H, 128], lse
+    float32 [B, H, N])."""
+    import torch
+
+    for name, t in (("q8", q8), ("k8", k8), ("v8", v8)):
+        if t.dtype != torch.uint8 or t.dim() != 4 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous uint8 device tensor [B, N, H, d]")
+        if tuple(t.shape) != tuple(q8.shape):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(q8.shape)}")
+    B, N, H, d = q8.shape
+    shapes = {"q_scale": (B, N, H, d // 32), "k_scale": (B, N, H, d // 32), "v_scale": (B, (N + 31) // 32, H, d)}
+    for name, t in (("q_scale", q_scale), ("k_scale", k_scale), ("v_scale", v_scale)):
+        if t.dtype != torch.uint8 or tuple(t.shape) != shapes[name] or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous uint8 device tensor of shape {shapes[name]}")
+        if t.device != q8.device:
+            raise ValueError(f"{name} is on {t.device}, expected {q8.device}")
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        out = torch.empty((B, N, H, d), dtype=torch.bfloat16, device=q8.device)
+    _check_bnhd("out", out, (B, N, H, d))
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
+    _check_lse(lse, B, N, H)
+    st = load_library().fa_fwd_mxfp8(
+        q8.data_ptr(), q_scale.data_ptr(), k8.data_ptr(), k_scale.data_ptr(), v8.data_ptr(), v_scale.data_ptr(),
+        out.data_ptr(), lse.data_ptr(), B, N, H, d, int(bool(causal)), scale, _stream_handle(q8.device),
+    )
+    if st != 0:
+        raise FaError(st, "fa_fwd_mxfp8")
     return out, lse

@@ -261,6 +261,28 @@ fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, const float* q
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+fa_status fa_fwd_mxfp8(const void* q, const void* q_scale, const void* k, const void* k_scale, const void* v,
+                       const void* v_scale, void* o, float* lse, int B, int N, int H, int d, int causal,
+                       float softmax_scale, hipStream_t stream) {
+  if (!q || !k || !v || !q_scale || !k_scale || !v_scale || !o || !lse) return FA_ERR_NULL;
+  if (d != 128) return FA_ERR_HEADDIM;
+  fa_status st = check_shape(B, N, H, d);
+  if (st != FA_OK) return st;
+  if (!std::isfinite(softmax_scale)) return FA_ERR_SCALE;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4) ||
+      !aligned(q_scale, 4) || !aligned(k_scale, 4) || !aligned(v_scale, 4))
+    return FA_ERR_ALIGN;
+  st = check_device();
+  if (st != FA_OK) return st;
+  (void)hipGetLastError();
+  fa::Fp8Args a{q, k, v, nullptr, nullptr, nullptr, o, lse, B, N, H, softmax_scale, stream};
+  a.q_scale = static_cast<const uint8_t*>(q_scale);
+  a.k_scale = static_cast<const uint8_t*>(k_scale);
+  a.v_scale = static_cast<const uint8_t*>(v_scale);
+  const hipError_t e = causal ? fa::launch_fwd_fp8<true>(a) : fa::launch_fwd_fp8<false>(a);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 size_t fa_decode_workspace_bytes(int B, int Nq, int Nk, int H, int d) {
   if (check_shape(B, Nq, H, d) != FA_OK || check_shape(B, Nk, H, d) != FA_OK) return 0;
   return fa::decode_workspace_bytes(B, Nq, Nk, H, d);

@@ -35,6 +35,22 @@
 //     parity within 8. This h gives both; h = r % 8 (rows r and r + 8 alike)
 //     made every K row read a two-way conflict.
 // O is written as bf16 (times the V descale), the logsumexp as fp32.
+//
+// Microscaled form (MX): instead of the per-head descales, one E8M0 scale
+// (2^(code - 127)) per 32 consecutive elements along each product's
+// reduction dimension, applied by the matrix instruction itself through its
+// per-lane scale operands. The instruction pairs a lane's scale with one
+// 32-deep block of its 64-deep reduction: bytes 0-15 of lanes m and m + 32
+// form block 0 (the scale of lane m), bytes 16-31 of both form block 1 (the
+// scale of lane m + 32). So in this form lane half g loads d = 64 ks + 16 g
+// .. + 15 into bytes 0-15 and d = 64 ks + 32 + 16 g .. + 15 into bytes
+// 16-31 of the Q and K operands, making block g of k-step ks the 32
+// consecutive d = 64 ks + 32 g ..; the P and V^T operands already hold key
+// block g of the tile in that position (key rows 8 g .. + 7 and 16 + 8 g ..
+// + 7 of each 32-key block, the V^T transpose reads above), so V's scale for
+// (column, 32-key block) is lane (column, g)'s. Each tile's K and V scales
+// come into LDS with the tile (one 4-byte LDS-DMA per lane and tensor); Q's
+// stay in a register. P's scale is 2^0.
 
 #include <type_traits>
 
@@ -76,12 +92,17 @@ __device__ __forceinline__ i32x8 cat(const u32x4& lo, const u32x4& hi) {
 
 // Three workgroups per CU (3 waves per SIMD, 168 registers, 96 KiB of LDS):
 // with the matrix time halved, a third wave hides more of the softmax.
-template <bool CAUSAL>
+// MX: block scales (q_scale, k_scale, v_scale) instead of the descales.
+template <bool CAUSAL, bool MX>
 __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(3, 3))) void fwd_fp8_kernel(
     const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, const uint8_t* __restrict__ V,
     const float* __restrict__ q_descale, const float* __restrict__ k_descale, const float* __restrict__ v_descale,
-    bf16* __restrict__ O, float* __restrict__ LSE, int N, int H, int nqb, int total_blocks, float scale) {
+    bf16* __restrict__ O, float* __restrict__ LSE, int N, int H, int nqb, int total_blocks, float scale,
+    const uint8_t* __restrict__ q_scale, const uint8_t* __restrict__ k_scale, const uint8_t* __restrict__ v_scale) {
   __shared__ __attribute__((aligned(1024))) char ring[2][2 * kF8Tile];  // per stage: K tile, V tile
+  // MX, per stage: the tile's K scales (64 keys x 4 blocks of d), then its V
+  // scales (2 key blocks x 128 columns).
+  __shared__ __attribute__((aligned(256))) char scl[MX ? 2 : 1][MX ? 512 : 16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -91,10 +112,10 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(3, 3
   const int head = hr.head;                            // b * H + h
   const int qblk = nqb - 1 - hr.rank;                  // longest causal rows first
   const int b = head / H, h = head - b * H;
-  const float qk = scale * q_descale[head] * k_descale[head];
+  const float qk = MX ? scale : scale * q_descale[head] * k_descale[head];
   const float c2 = fabsf(qk) * kLog2e;
   const uint32_t q_sign = qk < 0.f ? 0x80808080u : 0u;  // a negative factor negates Q
-  const float v_scale = v_descale[head];
+  const float v_mul = MX ? 1.f : v_descale[head];
   const long hoff = ((long)b * N * H + h) * kF8D;      // byte offset of token 0
   const uint32_t tokb = (uint32_t)H * kF8D;
   const uint32_t nrec = (uint32_t)(N - 1) * tokb + kF8D;
@@ -106,21 +127,41 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(3, 3
   const int myq = qw0 + l32;
   const int key_lim = CAUSAL ? min(myq, N - 1) : N - 1;  // the last key this lane's row sees
 
-  // Q as the B operand: bytes 64 ks + 32 g .. +31 of row myq.
+  // Q as the B operand: bytes 64 ks + 32 g .. +31 of row myq (MX: bytes
+  // 64 ks + 16 g .. + 15 and 64 ks + 32 + 16 g .. + 15, see above).
   i32x8 qf[2];
   {
-    const uint32_t qoff = row_off(myq, N, tokb, 32u * g);
+    const uint32_t qoff = row_off(myq, N, tokb, (MX ? 16u : 32u) * g);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const u32x4 lo = buf_load16(rq, qoff + 64 * ks) ^ q_sign;
-      const u32x4 hi = buf_load16(rq, qoff + 64 * ks + 16) ^ q_sign;
+      const u32x4 hi = buf_load16(rq, qoff + 64 * ks + (MX ? 32 : 16)) ^ q_sign;
       qf[ks] = cat(lo, hi);
     }
+  }
+  // MX: Q's scales of row myq (4 bytes, block i of d in byte i), shifted so
+  // that the block of k-step ks for this lane half (2 ks + g) is byte 2 ks.
+  // Block scales of a tile's keys and values: rows past N read as zeros.
+  // The tile's scales come from wave 0 (K: lane i, the 4 bytes of key row
+  // i) and wave 1 (V: lane i, bytes 4 (i % 32) .. + 3 of key block i / 32);
+  // the tile's position goes into the (scalar) resource, the lane's part
+  // stays fixed.
+  uint32_t qsw = 0;
+  u32x4 rks = {}, rvs = {};
+  const uint32_t srow = (uint32_t)H * 4;                   // bytes between tokens of q_scale / k_scale
+  const uint32_t vrow = (uint32_t)H * kF8D;                // bytes between key blocks of v_scale
+  if constexpr (MX) {
+    const long sbase = ((long)b * N * H + h) * 4;
+    const auto rqs = make_rsrc(q_scale + sbase, (uint32_t)(N - 1) * srow + 4);
+    qsw = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rqs, (int)((uint32_t)min(myq, N) * srow), 0, 0) >> (8 * g);
+    const int nvb = (N + 31) / 32;
+    rks = make_raw_rsrc(k_scale + sbase, (uint32_t)(N - 1) * srow + 4);
+    rvs = make_raw_rsrc(v_scale + ((long)b * nvb * H + h) * kF8D, (uint32_t)(nvb - 1) * vrow + kF8D);
   }
 
   // LDS-DMA of one tile: wave load u (0..7) fills LDS rows 8u .. 8u + 7;
   // lane i writes slot i, i.e. row 8u + i / 8 at chunk position i % 8.
-  auto issue = [&](int tile, char* dst) __attribute__((always_inline)) {
+  auto issue = [&](int tile, char* dst, char* sdst) __attribute__((always_inline)) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int u = wave + 4 * t;
@@ -128,6 +169,14 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(3, 3
       const uint32_t c16 = 16u * (uint32_t)((lane & 7) ^ f8_swz(r));
       dma16(rk, dst + u * 1024, row_off(tile * kF8BC + r, N, tokb, c16));
       dma16(rv, dst + kF8Tile + u * 1024, row_off(tile * kF8BC + vperm(r), N, tokb, c16));
+    }
+    if constexpr (MX) {
+      // (The tile starts below N, so the advanced resource keeps a positive
+      // record count: rows and key blocks past the end read as zeros.)
+      if (wave == 0)
+        dma4(rsrc_advance(rks, (uint32_t)tile * (kF8BC * srow)), sdst, (uint32_t)lane * srow);
+      else if (wave == 1)
+        dma4(rsrc_advance(rvs, (uint32_t)tile * (2 * vrow)), sdst + 256, (uint32_t)(lane >> 5) * vrow + 4u * (lane & 31));
     }
   };
 
@@ -148,21 +197,35 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(3, 3
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-    for (int hi = 0; hi < 2; ++hi) koff[ks][hi] = f8_slot(l32, 4 * ks + 2 * g + hi);
+    for (int hi = 0; hi < 2; ++hi) koff[ks][hi] = f8_slot(l32, MX ? 4 * ks + 2 * hi + g : 4 * ks + 2 * g + hi);
 #pragma unroll
   for (int db = 0; db < 4; ++db) voff[db] = f8_slot(8 * g + (j16 >> 1), 2 * db + (G & 1)) + 8 * (j16 & 1);
 
   i32x8 pf = {};  // P^T operand of the current tile (kept across tiles)
-  auto scores = [&](f32x16 (&s)[2], const char* kt, int key0, auto mask_tag) __attribute__((always_inline)) {
+  auto scores = [&](f32x16 (&s)[2], const char* kt, const char* st, int key0, auto mask_tag)
+                    __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
     s[0] = f32x16{};
     s[1] = f32x16{};
+    uint32_t ksw[2] = {0u, 0u};  // MX: K scales of this lane's key row in block kb, as qsw
+    if constexpr (MX) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        ksw[kb] = *reinterpret_cast<const FA_LDS uint32_t*>((const FA_LDS char*)st + (32 * kb + l32) * 4) >> (8 * g);
+    }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const i32x8 a = cat(lds_read16(kt, koff[ks][0] + kb * 32 * kF8D), lds_read16(kt, koff[ks][1] + kb * 32 * kF8D));
-        s[kb] = mfma_f8(a, qf[ks], s[kb]);
+        if constexpr (MX) {
+          if (ks == 0)
+            s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf[ks], s[kb], 0, 0, 0, (int)ksw[kb], 0, (int)qsw);
+          else
+            s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf[ks], s[kb], 0, 0, 2, (int)ksw[kb], 2, (int)qsw);
+        } else {
+          s[kb] = mfma_f8(a, qf[ks], s[kb]);
+        }
       }
     if constexpr (MASK) {
 #pragma unroll
@@ -211,11 +274,11 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(3, 3
   // maxima taken, O and l rescaled and P recomputed. A row that has seen no
   // key holds the finite kF8NoMax, for which every visible score overflows
   // to +inf and takes that path.
-  auto compute = [&](int j, const char* kt, auto mask_tag, bool first) __attribute__((always_inline)) {
+  auto compute = [&](int j, const char* kt, const char* st, auto mask_tag, bool first) __attribute__((always_inline)) {
     const int key0 = j * kF8BC;
     const char* vt = kt + kF8Tile;
     f32x16 s[2];
-    scores(s, kt, key0, mask_tag);
+    scores(s, kt, st, key0, mask_tag);
     float t = 0.f;
     bool slow = true;  // wave-uniform
     if (!first) {
@@ -225,7 +288,7 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(3, 3
     }
     if (slow) {
       asm volatile("" ::: "memory");  // a branch; the scores below are loaded again
-      if (!first) scores(s, kt, key0, mask_tag);
+      if (!first) scores(s, kt, st, key0, mask_tag);
       float mx = max16(s[1], max16(s[0], -INFINITY));
       mx = xhalf_max(mx);
       const float tile_m = (mx == -INFINITY) ? -INFINITY : mx * c2;
@@ -253,34 +316,41 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(3, 3
         a[2 * q4] = t[0];
         a[2 * q4 + 1] = t[1];
       }
-      oacc[db] = mfma_f8(a, pf, oacc[db]);
+      if constexpr (MX) {
+        // V's scale of column 32 db + l32 in key block g of the tile; P's is 2^0
+        const uint32_t vs = *((const FA_LDS uint8_t*)st + 256 + 128 * g + 32 * db + l32);
+        oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pf, oacc[db], 0, 0, 0, (int)vs, 0, 127);
+      } else {
+        oacc[db] = mfma_f8(a, pf, oacc[db]);
+      }
     }
   };
 
   const int jm = CAUSAL ? min(qblk * (kF8BR / kF8BC), N / kF8BC) : N / kF8BC;
-  issue(0, ring[0]);
+  auto sstage = [&](int j) __attribute__((always_inline)) { return scl[MX ? (j & 1) : 0]; };
+  issue(0, ring[0], sstage(0));
   wait_vmem();
   __syncthreads();
   int j = 0;
   for (; j < jm; ++j) {
-    if (j + 1 < ntiles) issue(j + 1, ring[(j + 1) & 1]);
-    compute(j, ring[j & 1], std::false_type{}, j == 0);
+    if (j + 1 < ntiles) issue(j + 1, ring[(j + 1) & 1], sstage(j + 1));
+    compute(j, ring[j & 1], sstage(j), std::false_type{}, j == 0);
     wait_vmem();
     __syncthreads();
   }
   for (; j < ntiles; ++j) {
-    if (j + 1 < ntiles) issue(j + 1, ring[(j + 1) & 1]);
+    if (j + 1 < ntiles) issue(j + 1, ring[(j + 1) & 1], sstage(j + 1));
     // (Non-causal: always true here; as a branch it keeps the register
     // allocator from spilling around the masked tile, which it does when
     // the call is unconditional.)
-    if (j * kF8BC <= (CAUSAL ? qw0 + 31 : N - 1)) compute(j, ring[j & 1], std::true_type{}, j == 0);
+    if (j * kF8BC <= (CAUSAL ? qw0 + 31 : N - 1)) compute(j, ring[j & 1], sstage(j), std::true_type{}, j == 0);
     wait_vmem();
     __syncthreads();
   }
 
   const float l_tot = xhalf_sum(l_run);
   const bool seen = l_tot > 0.f;
-  const float inv = seen ? v_scale / l_tot : 0.f;
+  const float inv = seen ? v_mul / l_tot : 0.f;
   if (myq < N) {
     if (g == 0) LSE[(long)head * N + myq] = seen ? (m_run - kF8Shift + log2f(l_tot)) * kLn2 : -INFINITY;
     bf16* orow = O + ((long)b * N * H + h) * kF8D + (long)myq * H * kF8D;
@@ -301,10 +371,16 @@ template <bool CAUSAL>
 hipError_t launch_fwd_fp8(const Fp8Args& a) {
   const int nqb = (a.N + kF8BR - 1) / kF8BR;
   const int total = a.B * a.H * nqb;
-  hipLaunchKernelGGL((fwd_fp8_kernel<CAUSAL>), dim3(total), dim3(kF8Threads), 0, a.stream,
-                     static_cast<const uint8_t*>(a.q), static_cast<const uint8_t*>(a.k),
-                     static_cast<const uint8_t*>(a.v), a.q_descale, a.k_descale, a.v_descale,
-                     static_cast<bf16*>(a.o), a.lse, a.N, a.H, nqb, total, a.scale);
+  if (a.q_scale)
+    hipLaunchKernelGGL((fwd_fp8_kernel<CAUSAL, true>), dim3(total), dim3(kF8Threads), 0, a.stream,
+                       static_cast<const uint8_t*>(a.q), static_cast<const uint8_t*>(a.k),
+                       static_cast<const uint8_t*>(a.v), nullptr, nullptr, nullptr, static_cast<bf16*>(a.o),
+                       a.lse, a.N, a.H, nqb, total, a.scale, a.q_scale, a.k_scale, a.v_scale);
+  else
+    hipLaunchKernelGGL((fwd_fp8_kernel<CAUSAL, false>), dim3(total), dim3(kF8Threads), 0, a.stream,
+                       static_cast<const uint8_t*>(a.q), static_cast<const uint8_t*>(a.k),
+                       static_cast<const uint8_t*>(a.v), a.q_descale, a.k_descale, a.v_descale,
+                       static_cast<bf16*>(a.o), a.lse, a.N, a.H, nqb, total, a.scale, nullptr, nullptr, nullptr);
   return hipGetLastError();
 }
 

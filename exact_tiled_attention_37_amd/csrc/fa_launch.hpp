@@ -70,8 +70,11 @@ hipError_t launch_bwd(const BwdArgs& a);
 template <int D>
 hipError_t launch_merge(const MergeArgs& a);
 
-// FP8 (e4m3) forward, d = 128: q, k, v are e4m3 codes [B, N, H, 128]; the
-// descales are float32 [B, H].
+// FP8 (e4m3) forward, d = 128: q, k, v are e4m3 codes [B, N, H, 128]. Either
+// one float32 descale per (batch, head) and tensor ([B, H]), or block scales
+// (E8M0 bytes): q_scale, k_scale [B, N, H, 4] (one per 32 consecutive d of a
+// token), v_scale [B, ceil(N / 32), H, 128] (one per 32 consecutive tokens of
+// a column).
 struct Fp8Args {
   const void* q;
   const void* k;
@@ -84,6 +87,9 @@ struct Fp8Args {
   int B, N, H;
   float scale;
   hipStream_t stream;
+  const uint8_t* q_scale = nullptr;  // block scales (all three set: the microscaled form)
+  const uint8_t* k_scale = nullptr;
+  const uint8_t* v_scale = nullptr;
 };
 
 template <bool CAUSAL>

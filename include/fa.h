@@ -231,6 +231,31 @@ FA_API fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, const f
                      hipStream_t stream);
 
 /*
+ * Microscaled FP8 forward (the same low-precision abstract on the Napkin
+ * related-papers list, read for matrix units that scale small blocks of
+ * narrow-format values): Q, K, V as OCP FP8 E4M3 codes, each block of 32
+ * consecutive elements along the reduction dimension of the product it enters
+ * sharing one scale 2^(e - 127) given as an E8M0 byte e (255 is NaN and is not
+ * checked for). Computes exact attention (as fa_fwd) on the values
+ * e4m3(code) * 2^(e - 127); the matrix instruction applies the scales.
+ *
+ *   q, k, v      [B, N, H, 128] uint8 e4m3 codes (16-byte aligned)
+ *   q_scale,     [B, N, H, 4] uint8 E8M0: block i covers d = 32 i .. 32 i + 31
+ *   k_scale        of one token
+ *   v_scale      [B, ceil(N / 32), H, 128] uint8 E8M0: block t of column d covers
+ *                tokens 32 t .. 32 t + 31 (the last block may be short)
+ *   o            [B, N, H, 128] bf16 output; lse [B, H, N] float32 (natural log
+ *                of the scaled scores of the values the codes stand for)
+ *
+ * The probabilities are rounded to e4m3 for the P V product as in
+ * fa_fwd_fp8, with the same per-element error bound. Errors as for
+ * fa_fwd_fp8 (FA_ERR_HEADDIM for d != 128).
+ */
+FA_API fa_status fa_fwd_mxfp8(const void* q, const void* q_scale, const void* k, const void* k_scale,
+                       const void* v, const void* v_scale, void* o, float* lse, int B, int N, int H, int d,
+                       int causal, float softmax_scale, hipStream_t stream);
+
+/*
  * Decode-shaped attention: a few new query rows against a long key/value
  * history. The IPLEX post (section "Document the implementation
  * difference") separates decoding from prefill as a workload with its own

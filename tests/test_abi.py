@@ -289,6 +289,40 @@ def test_fp8_errors(lib):
     assert fp8(lib, kd=P + 2) == FA_ERR_ALIGN
 
 
+def mxfp8(lib, q=P, qs=P, k=P, ks=P, v=P, vs=P, o=P, lse=P, B=1, N=9, H=2, d=128, causal=1, scale=0.1):
+    return lib.fa_fwd_mxfp8(q, qs, k, ks, v, vs, o, lse, B, N, H, d, causal, scale, None)
+
+
+@pytest.mark.parametrize("which", ["q", "qs", "k", "ks", "v", "vs", "o", "lse"])
+def test_mxfp8_null_pointer(lib, which):
+    assert mxfp8(lib, **{which: None}) == FA_ERR_NULL
+
+
+def test_mxfp8_errors(lib):
+    assert mxfp8(lib, d=64) == FA_ERR_HEADDIM
+    assert mxfp8(lib, N=0) == FA_ERR_SHAPE
+    assert mxfp8(lib, H=0) == FA_ERR_SHAPE
+    assert mxfp8(lib, scale=float("inf")) == FA_ERR_SCALE
+    assert mxfp8(lib, v=P + 8) == FA_ERR_ALIGN
+    assert mxfp8(lib, vs=P + 2) == FA_ERR_ALIGN
+    assert mxfp8(lib, lse=P + 2) == FA_ERR_ALIGN
+
+
+def test_binding_mxfp8_scale_shapes():
+    """The binding checks the block-scale shapes before anything reaches the
+    library (host tensors never get that far either)."""
+    import torch
+
+    q = torch.zeros(1, 40, 2, 128, dtype=torch.uint8)
+    qs = torch.zeros(1, 40, 2, 4, dtype=torch.uint8)
+    vs = torch.zeros(1, 2, 2, 128, dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        fa.fa_fwd_mxfp8(q, qs, q, qs, q, vs, causal=True)  # host tensors
+    if torch.cuda.is_available():  # pragma: no cover - GPU box only
+        return
+    assert fa.fa_fwd_mxfp8.__doc__ and "E8M0" in fa.fa_fwd_mxfp8.__doc__
+
+
 def test_binding_rejects_host_or_mistyped_workspace():
     """A caller-supplied workspace must be a contiguous uint8 tensor on the
     calling device with enough bytes; a host tensor (whose pointer the
