@@ -87,7 +87,7 @@ def parse():
     ap.add_argument("--no-sweep", action="store_true", help="skip the forward sweep over the other workloads")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-shaped calls")
     ap.add_argument("--no-bias", action="store_true", help="skip the additive-bias calls")
-    ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 forward calls")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 forward calls (per-head and microscaled)")
     ap.add_argument("--no-ring", action="store_true",
                     help="skip the key-chunk leg (one rank's share of the 16384-token sequence over 8 ranks)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -317,30 +317,39 @@ def bias_leg(fa, si, torch, dev, stream):
 
 
 def fp8_leg(fa, si, torch, dev, stream):
-    """FP8 (e4m3) forward on the FP8 workloads: TFLOP/s against the dense FP8
-    MFMA peak, with the bf16 forward of the same shape (random bf16 inputs)
-    timed beside it."""
+    """FP8 (e4m3) forward on the FP8 workloads: per-head descales (fa_fwd_fp8)
+    and E8M0 block scales (fa_fwd_mxfp8), TFLOP/s against the dense FP8 MFMA
+    peak, with the bf16 forward of the same shape (random bf16 inputs) timed
+    in the same window."""
     out = {}
-    for name, w in si.FP8_WORKLOADS.items():
+    for (name, w), (mname, mw) in zip(si.FP8_WORKLOADS.items(), si.MXFP8_WORKLOADS.items()):
+        assert (w.B, w.H, w.N, w.d, w.causal) == (mw.B, mw.H, mw.N, mw.d, mw.causal)
         b8 = si.draw_fp8(w.B, w.N, w.H, w.d, w.seed)
         t = {k: torch.from_numpy(v).to(dev) for k, v in b8.items()}
+        b8 = si.draw_mxfp8(mw.B, mw.N, mw.H, mw.d, mw.seed)
+        m = {k: torch.from_numpy(v).to(dev) for k, v in b8.items()}
         del b8
         o = torch.empty((w.B, w.N, w.H, w.d), dtype=torch.bfloat16, device=dev)
         lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
         call = lambda: fa.fa_fwd_fp8(t["q"], t["k"], t["v"], t["q_descale"], t["k_descale"], t["v_descale"],
                                      w.causal, w.scale, out=o, lse=lse)
+        mcall = lambda: fa.fa_fwd_mxfp8(m["q"], m["q_scale"], m["k"], m["k_scale"], m["v"], m["v_scale"],
+                                        w.causal, w.scale, out=o, lse=lse)
         bq = torch.randn((w.B, w.N, w.H, w.d), device=dev).to(torch.bfloat16)
         bk, bv = torch.randn_like(bq, dtype=torch.float32).to(torch.bfloat16), torch.randn_like(bq, dtype=torch.float32).to(torch.bfloat16)
         ref = lambda: fa.fa_fwd(bq, bk, bv, w.causal, w.scale, out=o, lse=lse)
-        time_calls(lambda: (call(), ref()), settle_calls(2 * fwd_flops(w)), stream)
+        time_calls(lambda: (call(), mcall(), ref()), settle_calls(2 * fwd_flops(w)), stream)
         reps = 10 if w.N * w.N * w.B * w.H >= (1 << 30) else 30
-        t8, t16 = time_calls(call, reps, stream), time_calls(ref, reps, stream)
+        t8, tm, t16 = time_calls(call, reps, stream), time_calls(mcall, reps, stream), time_calls(ref, reps, stream)
         ff = fwd_flops(w)
-        out[name] = {"B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal, "ms": round(t8 * 1e3, 4),
-                     "roofline": {"bound": "mfma", "achieved": round(ff / t8 / 1e12, 2), "peak": PEAK_FP8_TFLOPS,
-                                  "unit": "TFLOP/s", "frac": round(ff / t8 / 1e12 / PEAK_FP8_TFLOPS, 4)},
-                     "bf16_fwd_ms": round(t16 * 1e3, 4), "speedup_vs_bf16": round(t16 / t8, 3)}
-        del t, o, lse, bq, bk, bv
+        roof = lambda tt: {"bound": "mfma", "achieved": round(ff / tt / 1e12, 2), "peak": PEAK_FP8_TFLOPS,
+                           "unit": "TFLOP/s", "frac": round(ff / tt / 1e12 / PEAK_FP8_TFLOPS, 4)}
+        shape = {"B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal}
+        out[name] = {**shape, "ms": round(t8 * 1e3, 4), "roofline": roof(t8), "bf16_fwd_ms": round(t16 * 1e3, 4),
+                     "speedup_vs_bf16": round(t16 / t8, 3)}
+        out[mname] = {**shape, "ms": round(tm * 1e3, 4), "roofline": roof(tm), "bf16_fwd_ms": round(t16 * 1e3, 4),
+                      "speedup_vs_bf16": round(t16 / tm, 3), "time_vs_per_head_fp8": round(tm / t8, 3)}
+        del t, m, o, lse, bq, bk, bv
     return out
 
 

@@ -42,15 +42,17 @@
 // per-lane scale operands. The instruction pairs a lane's scale with one
 // 32-deep block of its 64-deep reduction: bytes 0-15 of lanes m and m + 32
 // form block 0 (the scale of lane m), bytes 16-31 of both form block 1 (the
-// scale of lane m + 32). So in this form lane half g loads d = 64 ks + 16 g
-// .. + 15 into bytes 0-15 and d = 64 ks + 32 + 16 g .. + 15 into bytes
-// 16-31 of the Q and K operands, making block g of k-step ks the 32
-// consecutive d = 64 ks + 32 g ..; the P and V^T operands already hold key
-// block g of the tile in that position (key rows 8 g .. + 7 and 16 + 8 g ..
-// + 7 of each 32-key block, the V^T transpose reads above), so V's scale for
-// (column, 32-key block) is lane (column, g)'s. Each tile's K and V scales
-// come into LDS with the tile (one 4-byte LDS-DMA per lane and tensor); Q's
-// stay in a register. P's scale is 2^0.
+// scale of lane m + 32). So in this form lane half g loads d = 32 ks + 16 g
+// .. + 15 into bytes 0-15 and d = 64 + 32 ks + 16 g .. + 15 into bytes
+// 16-31 of the Q and K operands: block 0 of k-step ks is d-block ks, block 1
+// is d-block 2 + ks, and lane half g needs d-blocks 2 g and 2 g + 1 (bytes
+// 2 g, 2 g + 1 of a token's four scale bytes) for its two k-steps, one
+// 16-bit read. The P and V^T operands already hold key block g of the tile
+// in that position (key rows 8 g .. + 7 and 16 + 8 g .. + 7 of each 32-key
+// block, the V^T transpose reads above), so V's scale for (column, 32-key
+// block) is lane (column, g)'s. Each tile's K and V scales come into LDS
+// with the tile (one 4-byte LDS-DMA per lane and tensor); Q's stay in a
+// register. P's scale is 2^0.
 
 #include <type_traits>
 
@@ -128,19 +130,19 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(3, 3
   const int key_lim = CAUSAL ? min(myq, N - 1) : N - 1;  // the last key this lane's row sees
 
   // Q as the B operand: bytes 64 ks + 32 g .. +31 of row myq (MX: bytes
-  // 64 ks + 16 g .. + 15 and 64 ks + 32 + 16 g .. + 15, see above).
+  // 32 ks + 16 g .. + 15 and 64 + 32 ks + 16 g .. + 15, see above).
   i32x8 qf[2];
   {
     const uint32_t qoff = row_off(myq, N, tokb, (MX ? 16u : 32u) * g);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const u32x4 lo = buf_load16(rq, qoff + 64 * ks) ^ q_sign;
-      const u32x4 hi = buf_load16(rq, qoff + 64 * ks + (MX ? 32 : 16)) ^ q_sign;
+      const u32x4 lo = buf_load16(rq, qoff + (MX ? 32 : 64) * ks) ^ q_sign;
+      const u32x4 hi = buf_load16(rq, qoff + (MX ? 64 + 32 * ks : 64 * ks + 16)) ^ q_sign;
       qf[ks] = cat(lo, hi);
     }
   }
-  // MX: Q's scales of row myq (4 bytes, block i of d in byte i), shifted so
-  // that the block of k-step ks for this lane half (2 ks + g) is byte 2 ks.
+  // MX: Q's scales of row myq (4 bytes, d-block i in byte i), shifted so that
+  // this lane half's block of k-step ks (2 g + ks) is byte ks.
   // Block scales of a tile's keys and values: rows past N read as zeros.
   // The tile's scales come from wave 0 (K: lane i, the 4 bytes of key row
   // i) and wave 1 (V: lane i, bytes 4 (i % 32) .. + 3 of key block i / 32);
@@ -153,7 +155,7 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(3, 3
   if constexpr (MX) {
     const long sbase = ((long)b * N * H + h) * 4;
     const auto rqs = make_rsrc(q_scale + sbase, (uint32_t)(N - 1) * srow + 4);
-    qsw = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rqs, (int)((uint32_t)min(myq, N) * srow), 0, 0) >> (8 * g);
+    qsw = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rqs, (int)((uint32_t)min(myq, N) * srow), 0, 0) >> (16 * g);
     const int nvb = (N + 31) / 32;
     rks = make_raw_rsrc(k_scale + sbase, (uint32_t)(N - 1) * srow + 4);
     rvs = make_raw_rsrc(v_scale + ((long)b * nvb * H + h) * kF8D, (uint32_t)(nvb - 1) * vrow + kF8D);
@@ -197,7 +199,7 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(3, 3
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-    for (int hi = 0; hi < 2; ++hi) koff[ks][hi] = f8_slot(l32, MX ? 4 * ks + 2 * hi + g : 4 * ks + 2 * g + hi);
+    for (int hi = 0; hi < 2; ++hi) koff[ks][hi] = f8_slot(l32, MX ? 4 * hi + 2 * ks + g : 4 * ks + 2 * g + hi);
 #pragma unroll
   for (int db = 0; db < 4; ++db) voff[db] = f8_slot(8 * g + (j16 >> 1), 2 * db + (G & 1)) + 8 * (j16 & 1);
 
@@ -207,11 +209,11 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(3, 3
     constexpr bool MASK = decltype(mask_tag)::value;
     s[0] = f32x16{};
     s[1] = f32x16{};
-    uint32_t ksw[2] = {0u, 0u};  // MX: K scales of this lane's key row in block kb, as qsw
+    uint32_t ksw[2] = {0u, 0u};  // MX: this lane half's two K scales of its key row in block kb, as qsw
     if constexpr (MX) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
-        ksw[kb] = *reinterpret_cast<const FA_LDS uint32_t*>((const FA_LDS char*)st + (32 * kb + l32) * 4) >> (8 * g);
+        ksw[kb] = *reinterpret_cast<const FA_LDS uint16_t*>((const FA_LDS char*)st + (32 * kb + l32) * 4 + 2 * g);
     }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
@@ -222,7 +224,7 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(3, 3
           if (ks == 0)
             s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf[ks], s[kb], 0, 0, 0, (int)ksw[kb], 0, (int)qsw);
           else
-            s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf[ks], s[kb], 0, 0, 2, (int)ksw[kb], 2, (int)qsw);
+            s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf[ks], s[kb], 0, 0, 1, (int)ksw[kb], 1, (int)qsw);
         } else {
           s[kb] = mfma_f8(a, qf[ks], s[kb]);
         }
@@ -307,6 +309,13 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(3, 3
     }
     l_run += t;
     // O^T += V^T P^T: for each 32-column block of d, four transpose loads.
+    // MX: V's scales of columns 32 db + l32 in key block g of the tile (read
+    // together ahead of the products); P's scale is 2^0.
+    uint32_t vsc[MX ? 4 : 1];
+    if constexpr (MX) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db) vsc[db] = *((const FA_LDS uint8_t*)st + 256 + 128 * g + 32 * db + l32);
+    }
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
       i32x8 a;
@@ -317,9 +326,7 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(3, 3
         a[2 * q4 + 1] = t[1];
       }
       if constexpr (MX) {
-        // V's scale of column 32 db + l32 in key block g of the tile; P's is 2^0
-        const uint32_t vs = *((const FA_LDS uint8_t*)st + 256 + 128 * g + 32 * db + l32);
-        oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pf, oacc[db], 0, 0, 0, (int)vs, 0, 127);
+        oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pf, oacc[db], 0, 0, 0, (int)vsc[db], 0, 127);
       } else {
         oacc[db] = mfma_f8(a, pf, oacc[db]);
       }
