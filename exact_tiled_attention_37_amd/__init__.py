@@ -441,9 +441,9 @@ def fa_bwd_bias(q, k, v, bias, o, lse, do, causal: bool, softmax_scale: Optional
 
 def fa_fwd_fp8(q8, k8, v8, q_descale, k_descale, v_descale, causal: bool, softmax_scale: Optional[float] = None,
                out=None, lse=None):
-    """FP8 forward: q8, k8, v8 are uint8 e4m3 codes [B, N, H, 128] and the
-    descales float32 [B, H]. Returns (o bf16 [B, N, H, 128], lse float32
-    [B, H, N])."""
+    """FP8 forward: q8, k8, v8 are uint8 e4m3 codes [B, N, H, d] (d = 64 or
+    128) and the descales float32 [B, H]. Returns (o bf16 [B, N, H, d], lse
+    float32 [B, H, N])."""
     import torch
 
     for name, t in (("q8", q8), ("k8", k8), ("v8", v8)):
@@ -474,10 +474,10 @@ def fa_fwd_fp8(q8, k8, v8, q_descale, k_descale, v_descale, causal: bool, softma
 
 def fa_fwd_mxfp8(q8, q_scale, k8, k_scale, v8, v_scale, causal: bool, softmax_scale: Optional[float] = None,
                  out=None, lse=None):
-    """Microscaled FP8 forward: q8, k8, v8 are uint8 e4m3 codes [B, N, H, 128];
-    q_scale, k_scale uint8 E8M0 [B, N, H, 4] (one per 32 consecutive d of a
-    token); v_scale uint8 E8M0 [B, ceil(N / 32), H, 128] (one per 32
-    consecutive tokens of a column). Returns (o bf16 [B, N, H, 128], lse
+    """Microscaled FP8 forward: q8, k8, v8 are uint8 e4m3 codes [B, N, H, d]
+    (d = 64 or 128); q_scale, k_scale uint8 E8M0 [B, N, H, d / 32] (one per 32
+    consecutive d of a token); v_scale uint8 E8M0 [B, ceil(N / 32), H, d] (one
+    per 32 consecutive tokens of a column). Returns (o bf16 [B, N, H, d], lse
     float32 [B, H, N])."""
     import torch
 

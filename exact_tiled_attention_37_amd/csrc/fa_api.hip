@@ -246,7 +246,7 @@ fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, const float* q
                      const float* v_descale, void* o, float* lse, int B, int N, int H, int d, int causal,
                      float softmax_scale, hipStream_t stream) {
   if (!q || !k || !v || !q_descale || !k_descale || !v_descale || !o || !lse) return FA_ERR_NULL;
-  if (d != 128) return FA_ERR_HEADDIM;
+  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
   fa_status st = check_shape(B, N, H, d);
   if (st != FA_OK) return st;
   if (!std::isfinite(softmax_scale)) return FA_ERR_SCALE;
@@ -256,7 +256,8 @@ fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, const float* q
   st = check_device();
   if (st != FA_OK) return st;
   (void)hipGetLastError();
-  const fa::Fp8Args a{q, k, v, q_descale, k_descale, v_descale, o, lse, B, N, H, softmax_scale, stream};
+  fa::Fp8Args a{q, k, v, q_descale, k_descale, v_descale, o, lse, B, N, H, softmax_scale, stream};
+  a.d = d;
   const hipError_t e = causal ? fa::launch_fwd_fp8<true>(a) : fa::launch_fwd_fp8<false>(a);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
@@ -265,7 +266,7 @@ fa_status fa_fwd_mxfp8(const void* q, const void* q_scale, const void* k, const 
                        const void* v_scale, void* o, float* lse, int B, int N, int H, int d, int causal,
                        float softmax_scale, hipStream_t stream) {
   if (!q || !k || !v || !q_scale || !k_scale || !v_scale || !o || !lse) return FA_ERR_NULL;
-  if (d != 128) return FA_ERR_HEADDIM;
+  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
   fa_status st = check_shape(B, N, H, d);
   if (st != FA_OK) return st;
   if (!std::isfinite(softmax_scale)) return FA_ERR_SCALE;
@@ -279,6 +280,7 @@ fa_status fa_fwd_mxfp8(const void* q, const void* q_scale, const void* k, const 
   a.q_scale = static_cast<const uint8_t*>(q_scale);
   a.k_scale = static_cast<const uint8_t*>(k_scale);
   a.v_scale = static_cast<const uint8_t*>(v_scale);
+  a.d = d;
   const hipError_t e = causal ? fa::launch_fwd_fp8<true>(a) : fa::launch_fwd_fp8<false>(a);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }

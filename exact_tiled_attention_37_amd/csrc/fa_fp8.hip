@@ -66,17 +66,28 @@ namespace {
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kF8D = 128;                  // head dimension = bytes per row
 constexpr int kF8BR = 128;                 // query rows per workgroup (4 waves x 32)
 constexpr int kF8BC = 64;                  // keys per K/V tile
 constexpr int kF8Threads = 256;
-constexpr int kF8Tile = kF8BC * kF8D;      // bytes of one K or V tile
 constexpr float kF8PMax = 448.f;           // largest finite e4m3 value
 constexpr float kF8NoMax = -1e30f;         // running max of a row that has seen no key
 constexpr float kF8Shift = 4.f;            // P is scaled by 2^4 before rounding
 
-__device__ __forceinline__ constexpr int f8_swz(int r) { return (((r >> 1) & 3) << 1) | ((r >> 3) & 1); }
-__device__ __forceinline__ constexpr int f8_slot(int r, int c) { return r * kF8D + ((c ^ f8_swz(r)) << 4); }
+// Position of 16-byte chunk c of row r in an LDS tile of D-byte rows (D = the
+// head dimension): c ^ h(r). d = 128 above; d = 64 (four rows per 256-byte
+// bank pass): rows of equal r % 4 among 16 consecutive rows need distinct h
+// (K row reads), and rows r and r + 4 need h differing in bit 1 (the V
+// transpose reads take chunks 2 db and 2 db + 1 of 8 consecutive rows):
+// h(r) = 2 ((r / 4) % 2) + (r / 8) % 2.
+template <int D>
+__device__ __forceinline__ constexpr int f8_swz(int r) {
+  if constexpr (D == 128)
+    return (((r >> 1) & 3) << 1) | ((r >> 3) & 1);
+  else
+    return (((r >> 2) & 1) << 1) | ((r >> 3) & 1);
+}
+template <int D>
+__device__ __forceinline__ constexpr int f8_slot(int r, int c) { return r * D + ((c ^ f8_swz<D>(r)) << 4); }
 // LDS row r of a V tile holds key row vperm(r) (bits 2 and 3 exchanged; an involution).
 __device__ __forceinline__ constexpr int vperm(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
@@ -95,16 +106,25 @@ __device__ __forceinline__ i32x8 cat(const u32x4& lo, const u32x4& hi) {
 // Three workgroups per CU (3 waves per SIMD, 168 registers, 96 KiB of LDS):
 // with the matrix time halved, a third wave hides more of the softmax.
 // MX: block scales (q_scale, k_scale, v_scale) instead of the descales.
-template <bool CAUSAL, bool MX>
+template <int D, bool CAUSAL, bool MX>
 __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(3, 3))) void fwd_fp8_kernel(
     const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, const uint8_t* __restrict__ V,
     const float* __restrict__ q_descale, const float* __restrict__ k_descale, const float* __restrict__ v_descale,
     bf16* __restrict__ O, float* __restrict__ LSE, int N, int H, int nqb, int total_blocks, float scale,
     const uint8_t* __restrict__ q_scale, const uint8_t* __restrict__ k_scale, const uint8_t* __restrict__ v_scale) {
-  __shared__ __attribute__((aligned(1024))) char ring[2][2 * kF8Tile];  // per stage: K tile, V tile
-  // MX, per stage: the tile's K scales (64 keys x 4 blocks of d), then its V
-  // scales (2 key blocks x 128 columns).
-  __shared__ __attribute__((aligned(256))) char scl[MX ? 2 : 1][MX ? 512 : 16];
+  constexpr int KS = D / 64;        // 64-deep k-steps of S over d
+  constexpr int DB = D / 32;        // 32-column blocks of the output
+  constexpr int CH = D / 16;        // 16-byte chunks per row
+  constexpr int TILE = kF8BC * D;   // bytes of one K or V tile
+  constexpr int RPL = 1024 / D;     // rows per whole-wave 1 KiB load
+  constexpr int LPW = D / 64;       // such loads per wave, tensor and tile
+  // MX at d = 128: the tile's scales go through LDS (below); at d = 64 a
+  // token's two scale bytes are read straight into registers.
+  constexpr bool SLDS = MX && D == 128;
+  __shared__ __attribute__((aligned(1024))) char ring[2][2 * TILE];  // per stage: K tile, V tile
+  // MX (d = 128), per stage: the tile's K scales (64 keys x 4 blocks of d),
+  // then its V scales (2 key blocks x 128 columns).
+  __shared__ __attribute__((aligned(256))) char scl[SLDS ? 2 : 1][SLDS ? 512 : 16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -118,9 +138,9 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(3, 3
   const float c2 = fabsf(qk) * kLog2e;
   const uint32_t q_sign = qk < 0.f ? 0x80808080u : 0u;  // a negative factor negates Q
   const float v_mul = MX ? 1.f : v_descale[head];
-  const long hoff = ((long)b * N * H + h) * kF8D;      // byte offset of token 0
-  const uint32_t tokb = (uint32_t)H * kF8D;
-  const uint32_t nrec = (uint32_t)(N - 1) * tokb + kF8D;
+  const long hoff = ((long)b * N * H + h) * D;         // byte offset of token 0
+  const uint32_t tokb = (uint32_t)H * D;
+  const uint32_t nrec = (uint32_t)(N - 1) * tokb + D;
   const auto rq = make_rsrc(Q + hoff, nrec);
   const u32x4 rk = make_raw_rsrc(K + hoff, nrec);
   const u32x4 rv = make_raw_rsrc(V + hoff, nrec);
@@ -130,19 +150,19 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(3, 3
   const int key_lim = CAUSAL ? min(myq, N - 1) : N - 1;  // the last key this lane's row sees
 
   // Q as the B operand: bytes 64 ks + 32 g .. +31 of row myq (MX: bytes
-  // 32 ks + 16 g .. + 15 and 64 + 32 ks + 16 g .. + 15, see above).
-  i32x8 qf[2];
+  // 32 ks + 16 g .. + 15 and 32 (KS + ks) + 16 g .. + 15, see above).
+  i32x8 qf[KS];
   {
     const uint32_t qoff = row_off(myq, N, tokb, (MX ? 16u : 32u) * g);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int ks = 0; ks < KS; ++ks) {
       const u32x4 lo = buf_load16(rq, qoff + (MX ? 32 : 64) * ks) ^ q_sign;
-      const u32x4 hi = buf_load16(rq, qoff + (MX ? 64 + 32 * ks : 64 * ks + 16)) ^ q_sign;
+      const u32x4 hi = buf_load16(rq, qoff + (MX ? 32 * (KS + ks) : 64 * ks + 16)) ^ q_sign;
       qf[ks] = cat(lo, hi);
     }
   }
-  // MX: Q's scales of row myq (4 bytes, d-block i in byte i), shifted so that
-  // this lane half's block of k-step ks (2 g + ks) is byte ks.
+  // MX: Q's scales of row myq (D / 32 bytes, d-block i in byte i), shifted so
+  // that this lane half's block of k-step ks (KS g + ks) is byte ks.
   // Block scales of a tile's keys and values: rows past N read as zeros.
   // The tile's scales come from wave 0 (K: lane i, the 4 bytes of key row
   // i) and wave 1 (V: lane i, bytes 4 (i % 32) .. + 3 of key block i / 32);
@@ -150,29 +170,54 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(3, 3
   // stays fixed.
   uint32_t qsw = 0;
   u32x4 rks = {}, rvs = {};
-  const uint32_t srow = (uint32_t)H * 4;                   // bytes between tokens of q_scale / k_scale
-  const uint32_t vrow = (uint32_t)H * kF8D;                // bytes between key blocks of v_scale
+  constexpr int SB = D / 32;                               // scale bytes per token of q_scale / k_scale
+  const uint32_t srow = (uint32_t)H * SB;                  // bytes between tokens of q_scale / k_scale
+  const uint32_t vrow = (uint32_t)H * D;                   // bytes between key blocks of v_scale
+  const int nvb = (N + 31) / 32;
   if constexpr (MX) {
-    const long sbase = ((long)b * N * H + h) * 4;
-    const auto rqs = make_rsrc(q_scale + sbase, (uint32_t)(N - 1) * srow + 4);
-    qsw = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rqs, (int)((uint32_t)min(myq, N) * srow), 0, 0) >> (16 * g);
-    const int nvb = (N + 31) / 32;
-    rks = make_raw_rsrc(k_scale + sbase, (uint32_t)(N - 1) * srow + 4);
-    rvs = make_raw_rsrc(v_scale + ((long)b * nvb * H + h) * kF8D, (uint32_t)(nvb - 1) * vrow + kF8D);
+    const long sbase = ((long)b * N * H + h) * SB;
+    const auto rqs = make_rsrc(q_scale + sbase, (uint32_t)(N - 1) * srow + SB);
+    const int qsoff = (int)((uint32_t)min(myq, N) * srow);
+    if constexpr (D == 128)
+      qsw = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rqs, qsoff, 0, 0) >> (16 * g);
+    else
+      qsw = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rqs, qsoff, 0, 0) >> (8 * g);
+    rks = make_raw_rsrc(k_scale + sbase, (uint32_t)(N - 1) * srow + SB);
+    rvs = make_raw_rsrc(v_scale + ((long)b * nvb * H + h) * D, (uint32_t)(nvb - 1) * vrow + D);
   }
+  // MX at d = 64: the next tile's scales, loaded into registers one tile
+  // ahead: K's two bytes of this lane's key row in each 32-key block, V's
+  // byte of column 32 db + l32 in key block g.
+  uint32_t ksn[2] = {0u, 0u}, vsn[2] = {0u, 0u}, ksc[2] = {0u, 0u}, vsv[2] = {0u, 0u};
+  const uint8_t* const ksb = MX ? k_scale + ((long)b * N * H + h) * SB : nullptr;
+  const uint8_t* const vsb = MX ? v_scale + ((long)b * nvb * H + h) * D : nullptr;
+  auto scale_loads = [&](int tile) __attribute__((always_inline)) {
+    if constexpr (MX && D == 64) {
+      // (the tile starts below N: both offsets stay inside the records)
+      const uint32_t ko = (uint32_t)tile * (kF8BC * srow), vo = (uint32_t)tile * (2 * vrow);
+      const auto rk2 = make_rsrc(ksb + ko, (uint32_t)(N - 1) * srow + SB - ko);
+      const auto rv2 = make_rsrc(vsb + vo, (uint32_t)(nvb - 1) * vrow + D - vo);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) ksn[kb] = buf_load2(rk2, (uint32_t)(32 * kb + l32) * srow);
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+        vsn[db] = (uint32_t)(uint8_t)__builtin_amdgcn_raw_buffer_load_b8(rv2, (int)((uint32_t)g * vrow + 32u * db + l32), 0, 0);
+    }
+  };
 
-  // LDS-DMA of one tile: wave load u (0..7) fills LDS rows 8u .. 8u + 7;
-  // lane i writes slot i, i.e. row 8u + i / 8 at chunk position i % 8.
+  // LDS-DMA of one tile: wave load u fills LDS rows RPL u .. RPL u + RPL - 1
+  // (d = 128: 8 rows of 8 chunks; d = 64: 16 rows of 4 chunks); lane i
+  // writes slot i, i.e. row RPL u + i / CH at chunk position i % CH.
   auto issue = [&](int tile, char* dst, char* sdst) __attribute__((always_inline)) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < LPW; ++t) {
       const int u = wave + 4 * t;
-      const int r = 8 * u + (lane >> 3);
-      const uint32_t c16 = 16u * (uint32_t)((lane & 7) ^ f8_swz(r));
+      const int r = RPL * u + lane / CH;
+      const uint32_t c16 = 16u * (uint32_t)((lane % CH) ^ f8_swz<D>(r));
       dma16(rk, dst + u * 1024, row_off(tile * kF8BC + r, N, tokb, c16));
-      dma16(rv, dst + kF8Tile + u * 1024, row_off(tile * kF8BC + vperm(r), N, tokb, c16));
+      dma16(rv, dst + TILE + u * 1024, row_off(tile * kF8BC + vperm(r), N, tokb, c16));
     }
-    if constexpr (MX) {
+    if constexpr (SLDS) {
       // (The tile starts below N, so the advanced resource keeps a positive
       // record count: rows and key blocks past the end read as zeros.)
       if (wave == 0)
@@ -185,9 +230,9 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(3, 3
   const int kv_len = CAUSAL ? min(N, (qblk + 1) * kF8BR) : N;
   const int ntiles = (kv_len + kF8BC - 1) / kF8BC;
 
-  f32x16 oacc[4];
+  f32x16 oacc[DB];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) oacc[i] = f32x16{};
+  for (int i = 0; i < DB; ++i) oacc[i] = f32x16{};
   float m_run = kF8NoMax;
   float l_run = 0.f;
 
@@ -195,13 +240,13 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(3, 3
   // 4 ks + 2 g + hi) and V transpose reads (row 8 g + j16 / 2 of a 16-key
   // group, chunk 2 db + G % 2, byte half j16 % 2); the block and group add
   // whole rows, which leave the swizzle unchanged (it reads row bits 1-3).
-  int koff[2][2], voff[4];
+  int koff[KS][2], voff[DB];
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks)
+  for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-    for (int hi = 0; hi < 2; ++hi) koff[ks][hi] = f8_slot(l32, MX ? 4 * hi + 2 * ks + g : 4 * ks + 2 * g + hi);
+    for (int hi = 0; hi < 2; ++hi) koff[ks][hi] = f8_slot<D>(l32, MX ? 2 * (hi * KS + ks) + g : 4 * ks + 2 * g + hi);
 #pragma unroll
-  for (int db = 0; db < 4; ++db) voff[db] = f8_slot(8 * g + (j16 >> 1), 2 * db + (G & 1)) + 8 * (j16 & 1);
+  for (int db = 0; db < DB; ++db) voff[db] = f8_slot<D>(8 * g + (j16 >> 1), 2 * db + (G & 1)) + 8 * (j16 & 1);
 
   i32x8 pf = {};  // P^T operand of the current tile (kept across tiles)
   auto scores = [&](f32x16 (&s)[2], const char* kt, const char* st, int key0, auto mask_tag)
@@ -209,17 +254,20 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(3, 3
     constexpr bool MASK = decltype(mask_tag)::value;
     s[0] = f32x16{};
     s[1] = f32x16{};
-    uint32_t ksw[2] = {0u, 0u};  // MX: this lane half's two K scales of its key row in block kb, as qsw
-    if constexpr (MX) {
+    uint32_t ksw[2] = {0u, 0u};  // MX: this lane half's K scales of its key row in block kb, as qsw
+    if constexpr (SLDS) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
         ksw[kb] = *reinterpret_cast<const FA_LDS uint16_t*>((const FA_LDS char*)st + (32 * kb + l32) * 4 + 2 * g);
+    } else if constexpr (MX) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) ksw[kb] = ksc[kb] >> (8 * g);
     }
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const i32x8 a = cat(lds_read16(kt, koff[ks][0] + kb * 32 * kF8D), lds_read16(kt, koff[ks][1] + kb * 32 * kF8D));
+        const i32x8 a = cat(lds_read16(kt, koff[ks][0] + kb * 32 * D), lds_read16(kt, koff[ks][1] + kb * 32 * D));
         if constexpr (MX) {
           if (ks == 0)
             s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf[ks], s[kb], 0, 0, 0, (int)ksw[kb], 0, (int)qsw);
@@ -278,7 +326,7 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(3, 3
   // to +inf and takes that path.
   auto compute = [&](int j, const char* kt, const char* st, auto mask_tag, bool first) __attribute__((always_inline)) {
     const int key0 = j * kF8BC;
-    const char* vt = kt + kF8Tile;
+    const char* vt = kt + TILE;
     f32x16 s[2];
     scores(s, kt, st, key0, mask_tag);
     float t = 0.f;
@@ -301,7 +349,7 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(3, 3
         const float alpha = fast_exp2(m_run - m_new);  // 0 from kF8NoMax, 1 when unchanged
         l_run *= alpha;
 #pragma unroll
-        for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
+        for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
         m_run = m_new;
       }
       float gmax;
@@ -311,17 +359,20 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(3, 3
     // O^T += V^T P^T: for each 32-column block of d, four transpose loads.
     // MX: V's scales of columns 32 db + l32 in key block g of the tile (read
     // together ahead of the products); P's scale is 2^0.
-    uint32_t vsc[MX ? 4 : 1];
-    if constexpr (MX) {
+    uint32_t vsc[MX ? DB : 1];
+    if constexpr (SLDS) {
 #pragma unroll
-      for (int db = 0; db < 4; ++db) vsc[db] = *((const FA_LDS uint8_t*)st + 256 + 128 * g + 32 * db + l32);
+      for (int db = 0; db < DB; ++db) vsc[db] = *((const FA_LDS uint8_t*)st + 256 + 128 * g + 32 * db + l32);
+    } else if constexpr (MX) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) vsc[db] = vsv[db];
     }
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
+    for (int db = 0; db < DB; ++db) {
       i32x8 a;
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const i32x2 t = lds_read_tr8(vt, voff[db] + 16 * q4 * kF8D);
+        const i32x2 t = lds_read_tr8(vt, voff[db] + 16 * q4 * D);
         a[2 * q4] = t[0];
         a[2 * q4 + 1] = t[1];
       }
@@ -334,24 +385,44 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(3, 3
   };
 
   const int jm = CAUSAL ? min(qblk * (kF8BR / kF8BC), N / kF8BC) : N / kF8BC;
-  auto sstage = [&](int j) __attribute__((always_inline)) { return scl[MX ? (j & 1) : 0]; };
+  auto sstage = [&](int j) __attribute__((always_inline)) { return scl[SLDS ? (j & 1) : 0]; };
+  // MX at d = 64: the next tile's loads (ksn, vsn) become the current
+  // tile's scales (ksc, vsv) after each tile's wait.
+  auto rotate = [&]() __attribute__((always_inline)) {
+    if constexpr (MX && D == 64) {
+      ksc[0] = ksn[0];
+      ksc[1] = ksn[1];
+      vsv[0] = vsn[0];
+      vsv[1] = vsn[1];
+    }
+  };
   issue(0, ring[0], sstage(0));
+  scale_loads(0);
   wait_vmem();
+  rotate();
   __syncthreads();
   int j = 0;
   for (; j < jm; ++j) {
-    if (j + 1 < ntiles) issue(j + 1, ring[(j + 1) & 1], sstage(j + 1));
+    if (j + 1 < ntiles) {
+      issue(j + 1, ring[(j + 1) & 1], sstage(j + 1));
+      scale_loads(j + 1);
+    }
     compute(j, ring[j & 1], sstage(j), std::false_type{}, j == 0);
     wait_vmem();
+    rotate();
     __syncthreads();
   }
   for (; j < ntiles; ++j) {
-    if (j + 1 < ntiles) issue(j + 1, ring[(j + 1) & 1], sstage(j + 1));
+    if (j + 1 < ntiles) {
+      issue(j + 1, ring[(j + 1) & 1], sstage(j + 1));
+      scale_loads(j + 1);
+    }
     // (Non-causal: always true here; as a branch it keeps the register
     // allocator from spilling around the masked tile, which it does when
     // the call is unconditional.)
     if (j * kF8BC <= (CAUSAL ? qw0 + 31 : N - 1)) compute(j, ring[j & 1], sstage(j), std::true_type{}, j == 0);
     wait_vmem();
+    rotate();
     __syncthreads();
   }
 
@@ -360,9 +431,9 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(3, 3
   const float inv = seen ? v_mul / l_tot : 0.f;
   if (myq < N) {
     if (g == 0) LSE[(long)head * N + myq] = seen ? (m_run - kF8Shift + log2f(l_tot)) * kLn2 : -INFINITY;
-    bf16* orow = O + ((long)b * N * H + h) * kF8D + (long)myq * H * kF8D;
+    bf16* orow = O + ((long)b * N * H + h) * D + (long)myq * H * D;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int rq4 = 0; rq4 < 4; ++rq4) {
         const f32x4 x = {oacc[db][4 * rq4] * inv, oacc[db][4 * rq4 + 1] * inv, oacc[db][4 * rq4 + 2] * inv,
@@ -378,16 +449,21 @@ template <bool CAUSAL>
 hipError_t launch_fwd_fp8(const Fp8Args& a) {
   const int nqb = (a.N + kF8BR - 1) / kF8BR;
   const int total = a.B * a.H * nqb;
-  if (a.q_scale)
-    hipLaunchKernelGGL((fwd_fp8_kernel<CAUSAL, true>), dim3(total), dim3(kF8Threads), 0, a.stream,
-                       static_cast<const uint8_t*>(a.q), static_cast<const uint8_t*>(a.k),
-                       static_cast<const uint8_t*>(a.v), nullptr, nullptr, nullptr, static_cast<bf16*>(a.o),
-                       a.lse, a.N, a.H, nqb, total, a.scale, a.q_scale, a.k_scale, a.v_scale);
-  else
-    hipLaunchKernelGGL((fwd_fp8_kernel<CAUSAL, false>), dim3(total), dim3(kF8Threads), 0, a.stream,
+  auto go = [&](auto dtag, auto mxtag) {
+    constexpr int D = decltype(dtag)::value;
+    constexpr bool MX = decltype(mxtag)::value;
+    hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL, MX>), dim3(total), dim3(kF8Threads), 0, a.stream,
                        static_cast<const uint8_t*>(a.q), static_cast<const uint8_t*>(a.k),
                        static_cast<const uint8_t*>(a.v), a.q_descale, a.k_descale, a.v_descale,
-                       static_cast<bf16*>(a.o), a.lse, a.N, a.H, nqb, total, a.scale, nullptr, nullptr, nullptr);
+                       static_cast<bf16*>(a.o), a.lse, a.N, a.H, nqb, total, a.scale, a.q_scale, a.k_scale,
+                       a.v_scale);
+  };
+  using D64 = std::integral_constant<int, 64>;
+  using D128 = std::integral_constant<int, 128>;
+  if (a.d == 64)
+    a.q_scale ? go(D64{}, std::true_type{}) : go(D64{}, std::false_type{});
+  else
+    a.q_scale ? go(D128{}, std::true_type{}) : go(D128{}, std::false_type{});
   return hipGetLastError();
 }
 

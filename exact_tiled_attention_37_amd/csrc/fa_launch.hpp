@@ -70,11 +70,11 @@ hipError_t launch_bwd(const BwdArgs& a);
 template <int D>
 hipError_t launch_merge(const MergeArgs& a);
 
-// FP8 (e4m3) forward, d = 128: q, k, v are e4m3 codes [B, N, H, 128]. Either
-// one float32 descale per (batch, head) and tensor ([B, H]), or block scales
-// (E8M0 bytes): q_scale, k_scale [B, N, H, 4] (one per 32 consecutive d of a
-// token), v_scale [B, ceil(N / 32), H, 128] (one per 32 consecutive tokens of
-// a column).
+// FP8 (e4m3) forward, d = 64 or 128: q, k, v are e4m3 codes [B, N, H, d].
+// Either one float32 descale per (batch, head) and tensor ([B, H]), or block
+// scales (E8M0 bytes): q_scale, k_scale [B, N, H, d / 32] (one per 32
+// consecutive d of a token), v_scale [B, ceil(N / 32), H, d] (one per 32
+// consecutive tokens of a column).
 struct Fp8Args {
   const void* q;
   const void* k;
@@ -82,7 +82,7 @@ struct Fp8Args {
   const float* q_descale;
   const float* k_descale;
   const float* v_descale;
-  void* o;      // bf16 [B, N, H, 128]
+  void* o;      // bf16 [B, N, H, d]
   float* lse;   // [B, H, N]
   int B, N, H;
   float scale;
@@ -90,6 +90,7 @@ struct Fp8Args {
   const uint8_t* q_scale = nullptr;  // block scales (all three set: the microscaled form)
   const uint8_t* k_scale = nullptr;
   const uint8_t* v_scale = nullptr;
+  int d = 128;                       // head dimension: 64 or 128
 };
 
 template <bool CAUSAL>

@@ -204,17 +204,17 @@ FA_API fa_status fa_bwd_bias(const void* q, const void* k, const void* v, const 
                       float softmax_scale, hipStream_t stream);
 
 /*
- * FP8 (e4m3) forward, d = 128 (low-precision attention on narrow-format
+ * FP8 (e4m3) forward, d = 64 or 128 (low-precision attention on narrow-format
  * matrix units: an abstract on the related-papers page for "FlashAttention
  * on a Napkin"; here the MI355X FP8 matrix unit). Same result definition as
  * fa_fwd, computed on the values the codes stand for:
  *
- *   q, k, v      uint8 OCP FP8 E4M3 codes, [B, N, H, 128], 16-byte aligned
+ *   q, k, v      uint8 OCP FP8 E4M3 codes, [B, N, H, d], 16-byte aligned
  *                (codes 0x7F / 0xFF are NaN and must not occur)
  *   q_descale,   float32 [B, H] each: the value of code c of (batch b, head h)
  *   k_descale,   is descale[b * H + h] * e4m3(c)
  *   v_descale
- *   o            [B, N, H, 128] bf16 output; lse [B, H, N] float32 (natural
+ *   o            [B, N, H, d] bf16 output; lse [B, H, N] float32 (natural
  *                log of the scaled scores of the dequantized inputs)
  *
  * Inside the kernel both products run on the FP8 matrix unit and the
@@ -222,8 +222,8 @@ FA_API fa_status fa_bwd_bias(const void* q, const void* k, const void* v, const 
  * logsumexp use their fp32 values). That rounding bounds the error of each
  * output element by about 2^-4 times the probability-weighted mean of |V| in
  * its column (plus 2^-14 per key for probabilities below 2^-10), a bound the
- * tests check element by element. Errors as for fa_fwd; FA_ERR_HEADDIM for
- * d != 128.
+ * tests check element by element. Errors as for fa_fwd (FA_ERR_HEADDIM for
+ * d other than 64 or 128).
  */
 FA_API fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, const float* q_descale,
                      const float* k_descale, const float* v_descale, void* o, float* lse,
@@ -239,17 +239,17 @@ FA_API fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, const f
  * checked for). Computes exact attention (as fa_fwd) on the values
  * e4m3(code) * 2^(e - 127); the matrix instruction applies the scales.
  *
- *   q, k, v      [B, N, H, 128] uint8 e4m3 codes (16-byte aligned)
- *   q_scale,     [B, N, H, 4] uint8 E8M0: block i covers d = 32 i .. 32 i + 31
+ *   q, k, v      [B, N, H, d] uint8 e4m3 codes (16-byte aligned), d = 64 or 128
+ *   q_scale,     [B, N, H, d / 32] uint8 E8M0: block i covers d = 32 i .. 32 i + 31
  *   k_scale        of one token
- *   v_scale      [B, ceil(N / 32), H, 128] uint8 E8M0: block t of column d covers
+ *   v_scale      [B, ceil(N / 32), H, d] uint8 E8M0: block t of column d covers
  *                tokens 32 t .. 32 t + 31 (the last block may be short)
- *   o            [B, N, H, 128] bf16 output; lse [B, H, N] float32 (natural log
+ *   o            [B, N, H, d] bf16 output; lse [B, H, N] float32 (natural log
  *                of the scaled scores of the values the codes stand for)
  *
  * The probabilities are rounded to e4m3 for the P V product as in
  * fa_fwd_fp8, with the same per-element error bound. Errors as for
- * fa_fwd_fp8 (FA_ERR_HEADDIM for d != 128).
+ * fa_fwd_fp8.
  */
 FA_API fa_status fa_fwd_mxfp8(const void* q, const void* q_scale, const void* k, const void* k_scale,
                        const void* v, const void* v_scale, void* o, float* lse, int B, int N, int H, int d,

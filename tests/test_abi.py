@@ -282,7 +282,8 @@ def test_fp8_null_pointer(lib, which):
 
 
 def test_fp8_errors(lib):
-    assert fp8(lib, d=64) == FA_ERR_HEADDIM
+    assert fp8(lib, d=96) == FA_ERR_HEADDIM
+    assert fp8(lib, d=256) == FA_ERR_HEADDIM
     assert fp8(lib, N=0) == FA_ERR_SHAPE
     assert fp8(lib, scale=float("nan")) == FA_ERR_SCALE
     assert fp8(lib, q=P + 8) == FA_ERR_ALIGN
@@ -299,7 +300,8 @@ def test_mxfp8_null_pointer(lib, which):
 
 
 def test_mxfp8_errors(lib):
-    assert mxfp8(lib, d=64) == FA_ERR_HEADDIM
+    assert mxfp8(lib, d=32) == FA_ERR_HEADDIM
+    assert mxfp8(lib, d=96) == FA_ERR_HEADDIM
     assert mxfp8(lib, N=0) == FA_ERR_SHAPE
     assert mxfp8(lib, H=0) == FA_ERR_SHAPE
     assert mxfp8(lib, scale=float("inf")) == FA_ERR_SCALE

@@ -87,12 +87,12 @@ def deq(b8, name):
 SMALL = [(1, 1, 1), (1, 17, 2), (2, 64, 2), (1, 129, 3), (1, 200, 2), (2, 333, 1), (1, 1000, 1)]
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
 @pytest.mark.parametrize("shape", SMALL, ids=lambda s: "B%dN%dH%d" % s)
-def test_fp8_small(shape, causal):
+def test_fp8_small(shape, causal, d):
     B, N, H = shape
-    d = 128
-    seed = 10100 + N + int(causal)
+    seed = 10100 + N + int(causal) + d
     scale = 1.0 / math.sqrt(d)
     announce(f"fp8 fwd shape={(B, N, H, d)} causal={causal} seed={seed}")
     b8 = si.draw_fp8(B, N, H, d, seed)
@@ -106,17 +106,18 @@ def test_fp8_small(shape, causal):
                        causal, scale, what=f"b{bb} h{h}")
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("span", [4.0, 16.0], ids=["span4", "span16"])
 @pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
-def test_fp8_growing_scores(causal, span):
+def test_fp8_growing_scores(causal, span, d):
     """Scores that grow along the keys: with span 16 a tile's P taken from
     the running maximum leaves e4m3's range on nearly every tile and is taken
     again from the tile's own row maxima; with span 4 it stays within 448
     while the running maximum lags. Every element within the derived bound."""
-    B, N, H, d = 1, 1000, 2, 128
+    B, N, H = 1, 1000, 2
     scale = 1.0 / math.sqrt(d)
-    announce(f"fp8 growing scores causal={causal} span={span}")
-    b8 = si.draw_fp8_growing_scores(B, N, H, d, 7200 + int(span), span)
+    announce(f"fp8 growing scores causal={causal} span={span} d={d}")
+    b8 = si.draw_fp8_growing_scores(B, N, H, d, 7200 + int(span) + d, span)
     o, lse = run(b8, causal, scale)
     q, k, v = deq(b8, "q"), deq(b8, "k"), deq(b8, "v")
     ro, rl = oracle.attention_forward_fp8(b8["q"], b8["k"], b8["v"], b8["q_descale"], b8["k_descale"],
@@ -126,12 +127,13 @@ def test_fp8_growing_scores(causal, span):
                    causal, scale, what=f"h{h}")
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("qd_sign", [1.0, -1.0], ids=["pos", "neg"])
-def test_fp8_descales(qd_sign):
+def test_fp8_descales(qd_sign, d):
     """Descales far from 1 and a negative Q descale (negates the scores)."""
-    B, N, H, d = 1, 300, 2, 128
-    announce(f"fp8 descales sign={qd_sign}")
-    b8 = si.draw_fp8(B, N, H, d, 10200)
+    B, N, H = 1, 300, 2
+    announce(f"fp8 descales sign={qd_sign} d={d}")
+    b8 = si.draw_fp8(B, N, H, d, 10200 + d)
     b8["q_descale"] = (b8["q_descale"] * np.float32(qd_sign) * np.float32(8.0)).astype(np.float32)
     b8["k_descale"] = (b8["k_descale"] / np.float32(4.0)).astype(np.float32)
     b8["v_descale"] = (b8["v_descale"] * np.float32(1000.0)).astype(np.float32)

@@ -85,12 +85,12 @@ def check_all(b8, causal, scale, o, lse):
 SMALL = [(1, 1, 1), (1, 17, 2), (2, 64, 2), (1, 129, 3), (1, 200, 2), (2, 333, 1), (1, 1000, 1)]
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
 @pytest.mark.parametrize("shape", SMALL, ids=lambda s: "B%dN%dH%d" % s)
-def test_mxfp8_small(shape, causal):
+def test_mxfp8_small(shape, causal, d):
     B, N, H = shape
-    d = 128
-    seed = 12100 + N + int(causal)
+    seed = 12100 + N + int(causal) + d
     scale = 1.0 / math.sqrt(d)
     announce(f"mxfp8 fwd shape={(B, N, H, d)} causal={causal} seed={seed}")
     b8 = si.draw_mxfp8(B, N, H, d, seed)
@@ -98,32 +98,34 @@ def test_mxfp8_small(shape, causal):
     check_all(b8, causal, scale, o, lse)
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("span", [4.0, 16.0], ids=["span4", "span16"])
 @pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
-def test_mxfp8_growing_scores(causal, span):
+def test_mxfp8_growing_scores(causal, span, d):
     """Scores that grow along the keys (the running max moves on most tiles
     with span 16, lags within e4m3's range with span 4)."""
-    B, N, H, d = 1, 1000, 2, 128
+    B, N, H = 1, 1000, 2
     scale = 1.0 / math.sqrt(d)
-    announce(f"mxfp8 growing scores causal={causal} span={span}")
-    b8 = si.draw_mxfp8_growing_scores(B, N, H, d, 7300 + int(span), span)
+    announce(f"mxfp8 growing scores causal={causal} span={span} d={d}")
+    b8 = si.draw_mxfp8_growing_scores(B, N, H, d, 7300 + int(span) + d, span)
     o, lse = run(b8, causal, scale)
     check_all(b8, causal, scale, o, lse)
 
 
-def test_mxfp8_block_scales_matter():
+@pytest.mark.parametrize("d", [64, 128])
+def test_mxfp8_block_scales_matter(d):
     """Scales that differ from block to block by large factors, so that a
     scale applied to the wrong block (or to the wrong half of a lane's
     operand, or to the wrong keys of a tile) moves the result far outside the
-    bound: Q's four d-blocks at 2^-6 .. 2^+3 of each other, K's the other way
+    bound: Q's d-blocks at 2^-6 .. 2^+3 of each other, K's the other way
     round, V's key blocks alternating by 2^5 and its columns by 2^3, and a
     negative softmax scale."""
-    B, N, H, d = 1, 300, 2, 128
-    announce("mxfp8 block scales far apart")
-    b8 = si.draw_mxfp8(B, N, H, d, 12300)
+    B, N, H = 1, 300, 2
+    announce(f"mxfp8 block scales far apart d={d}")
+    b8 = si.draw_mxfp8(B, N, H, d, 12300 + d)
     rng = np.random.Generator(np.random.PCG64(12301))
-    b8["q_scale"] = (b8["q_scale"].astype(np.int64) + np.array([-6, 3, 0, -2])).astype(np.uint8)
-    b8["k_scale"] = (b8["k_scale"].astype(np.int64) + np.array([4, -3, 1, 0])).astype(np.uint8)
+    b8["q_scale"] = (b8["q_scale"].astype(np.int64) + np.array([-6, 3, 0, -2])[: d // 32]).astype(np.uint8)
+    b8["k_scale"] = (b8["k_scale"].astype(np.int64) + np.array([4, -3, 1, 0])[: d // 32]).astype(np.uint8)
     vs = b8["v_scale"].astype(np.int64)
     vs += 5 * (np.arange(vs.shape[1]) % 2)[None, :, None, None] + 3 * (np.arange(d) % 3 == 0)[None, None, None, :]
     vs += rng.integers(-2, 3, vs.shape)
