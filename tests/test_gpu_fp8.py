@@ -182,3 +182,22 @@ def test_fp8_workload(name):
     lerr = max(r[3] for r in res)
     report(f"[parity] {name} O: max error / bound {ratio:.3f}, max-abs {mx:.3e} mean-abs {mean:.3e} over "
              f"{o.size} elements; LSE max-abs {lerr:.3e}")
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_fp8_d64_short_sequences(causal):
+    """d = 64 at the short-sequence shape (B=32 H=16 N=512; 2048 workgroups,
+    four per CU): every element of every head within the bound."""
+    B, N, H, d = 32, 512, 16, 64
+    scale = 1.0 / math.sqrt(d)
+    announce(f"fp8 d=64 B={B} N={N} H={H} causal={causal}")
+    b8 = si.draw_fp8(B, N, H, d, 10300 + int(causal))
+    o, lse = run(b8, causal, scale)
+    ro, rl = oracle.attention_forward_fp8(b8["q"], b8["k"], b8["v"], b8["q_descale"], b8["k_descale"],
+                                          b8["v_descale"], causal, scale)
+    q, k, v = deq(b8, "q"), deq(b8, "k"), deq(b8, "v")
+    res = [check_head(o[bb, :, h], lse[bb, h], ro[bb, :, h], rl[bb, h], q[bb, :, h], k[bb, :, h], v[bb, :, h],
+                      causal, scale, what=f"b{bb} h{h}") for bb in range(B) for h in range(H)]
+    report(f"[parity] fp8 d=64 B={B} N={N} H={H} causal={causal} O: max error / bound "
+           f"{max(r[0] for r in res):.3f}; LSE max-abs {max(r[3] for r in res):.3e}")
+

@@ -192,3 +192,16 @@ def test_mxfp8_workload(name):
            f"elements; LSE max-abs {max(r[3] for r in res):.3e}")
     announce(msg)
     parity_log.record(msg)
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_mxfp8_d64_short_sequences(causal):
+    """d = 64 at the short-sequence shape (B=32 H=16 N=512): every element of
+    every head within the bound."""
+    B, N, H, d = 32, 512, 16, 64
+    scale = 1.0 / math.sqrt(d)
+    announce(f"mxfp8 d=64 B={B} N={N} H={H} causal={causal}")
+    b8 = si.draw_mxfp8(B, N, H, d, 12500 + int(causal))
+    o, lse = run(b8, causal, scale)
+    check_all(b8, causal, scale, o, lse)
+
