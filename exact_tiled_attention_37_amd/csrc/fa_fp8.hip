@@ -42,17 +42,20 @@
 // per-lane scale operands. The instruction pairs a lane's scale with one
 // 32-deep block of its 64-deep reduction: bytes 0-15 of lanes m and m + 32
 // form block 0 (the scale of lane m), bytes 16-31 of both form block 1 (the
-// scale of lane m + 32). So in this form lane half g loads d = 32 ks + 16 g
-// .. + 15 into bytes 0-15 and d = 64 + 32 ks + 16 g .. + 15 into bytes
-// 16-31 of the Q and K operands: block 0 of k-step ks is d-block ks, block 1
-// is d-block 2 + ks, and lane half g needs d-blocks 2 g and 2 g + 1 (bytes
-// 2 g, 2 g + 1 of a token's four scale bytes) for its two k-steps, one
-// 16-bit read. The P and V^T operands already hold key block g of the tile
-// in that position (key rows 8 g .. + 7 and 16 + 8 g .. + 7 of each 32-key
-// block, the V^T transpose reads above), so V's scale for (column, 32-key
-// block) is lane (column, g)'s. Each tile's K and V scales come into LDS
-// with the tile (one 4-byte LDS-DMA per lane and tensor); Q's stay in a
-// register. P's scale is 2^0.
+// scale of lane m + 32). So in this form, with KS = d / 64 k-steps, lane
+// half g loads d = 32 ks + 16 g .. + 15 into bytes 0-15 and d = 32 (KS +
+// ks) + 16 g .. + 15 into bytes 16-31 of the Q and K operands: block 0 of
+// k-step ks is d-block ks, block 1 is d-block KS + ks, and lane half g needs
+// d-blocks KS g .. KS g + KS - 1 (consecutive bytes of a token's d / 32
+// scale bytes: one 16-bit read at d = 128, one byte at d = 64). The P and
+// V^T operands already hold key block g of the tile in that position (key
+// rows 8 g .. + 7 and 16 + 8 g .. + 7 of each 32-key block, the V^T
+// transpose reads above), so V's scale for (column, 32-key block) is lane
+// (column, g)'s. At d = 128 each tile's K and V scales come into LDS with
+// the tile (one 4-byte LDS-DMA per lane and tensor); at d = 64 (2 bytes per
+// token, which a 4-byte load would read past a sequence's last token) each
+// lane loads its own into registers a tile ahead. Q's stay in a register.
+// P's scale is 2^0.
 
 #include <type_traits>
 
@@ -166,12 +169,12 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(kF8W
     }
   }
   // MX: Q's scales of row myq (D / 32 bytes, d-block i in byte i), shifted so
-  // that this lane half's block of k-step ks (KS g + ks) is byte ks.
-  // Block scales of a tile's keys and values: rows past N read as zeros.
-  // The tile's scales come from wave 0 (K: lane i, the 4 bytes of key row
-  // i) and wave 1 (V: lane i, bytes 4 (i % 32) .. + 3 of key block i / 32);
-  // the tile's position goes into the (scalar) resource, the lane's part
-  // stays fixed.
+  // that this lane half's block of k-step ks (KS g + ks) is byte ks. Block
+  // scales of a tile's keys and values: rows and key blocks past the end read
+  // as zeros. At d = 128 they come from wave 0 (K: lane i, the 4 bytes of key
+  // row i) and wave 1 (V: lane i, bytes 4 (i % 32) .. + 3 of key block
+  // i / 32), the tile's position in the (scalar) resource and the lane's
+  // part fixed.
   uint32_t qsw = 0;
   u32x4 rks = {}, rvs = {};
   constexpr int SB = D / 32;                               // scale bytes per token of q_scale / k_scale
@@ -241,7 +244,7 @@ __global__ __launch_bounds__(kF8Threads) __attribute__((amdgpu_waves_per_eu(kF8W
   float l_run = 0.f;
 
   // Per-lane LDS offsets: K row reads (row l32 of a 32-key block, chunk
-  // 4 ks + 2 g + hi) and V transpose reads (row 8 g + j16 / 2 of a 16-key
+  // 4 ks + 2 g + hi; MX: 2 (hi KS + ks) + g) and V transpose reads (row 8 g + j16 / 2 of a 16-key
   // group, chunk 2 db + G % 2, byte half j16 % 2); the block and group add
   // whole rows, which leave the swizzle unchanged (it reads row bits 1-3).
   int koff[KS][2], voff[DB];
