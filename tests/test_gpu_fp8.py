@@ -201,3 +201,14 @@ def test_fp8_d64_short_sequences(causal):
     report(f"[parity] fp8 d=64 B={B} N={N} H={H} causal={causal} O: max error / bound "
            f"{max(r[0] for r in res):.3f}; LSE max-abs {max(r[3] for r in res):.3e}")
 
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_fp8_deterministic(d):
+    """Two calls on the same inputs give bit-identical outputs."""
+    B, N, H = 2, 700, 3
+    announce(f"fp8 determinism d={d}")
+    b8 = si.draw_fp8(B, N, H, d, 10400 + d)
+    o1, l1 = run(b8, True, 0.11)
+    o2, l2 = run(b8, True, 0.11)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
