@@ -89,13 +89,14 @@ BIAS_WORKLOADS = {
 }
 
 
-# FP8 (e4m3) forward workloads: the bf16 training shape and the long
-# sequence, with Q, K, V given as e4m3 codes and a descale factor per
+# FP8 (e4m3) forward workloads: the bf16 training shape (d = 128 and 64) and
+# the long sequence, with Q, K, V given as e4m3 codes and a descale factor per
 # (batch, head) (a low-precision attention variant named on the
 # related-papers page for "FlashAttention on a Napkin").
 FP8_WORKLOADS = {
     "fp8_train_causal": Workload("fp8_train_causal", 4, 16, 4096, 128, True, False, 10),
     "fp8_long_causal": Workload("fp8_long_causal", 1, 16, 16384, 128, True, False, 11),
+    "fp8_train_causal_d64": Workload("fp8_train_causal_d64", 4, 16, 4096, 64, True, False, 14),
 }
 
 # Largest |value| an input is scaled to before rounding to e4m3 (of the 448
@@ -108,6 +109,7 @@ FP8_INPUT_AMAX = 224.0
 MXFP8_WORKLOADS = {
     "mxfp8_train_causal": Workload("mxfp8_train_causal", 4, 16, 4096, 128, True, False, 12),
     "mxfp8_long_causal": Workload("mxfp8_long_causal", 1, 16, 16384, 128, True, False, 13),
+    "mxfp8_train_causal_d64": Workload("mxfp8_train_causal_d64", 4, 16, 4096, 64, True, False, 15),
 }
 # Exponent of the largest power of two an e4m3 code holds (448 = 1.75 * 2^8):
 # the OCP MX rule scales a block so that its largest magnitude lands in
