@@ -119,7 +119,8 @@ def random_bias(B, H, N, seed, holes=True):
     return si.draw_bias_with_holes(B, H, N, seed, holes)
 
 
-SMALL = [(1, 1, 1, 64), (1, 17, 2, 64), (2, 64, 2, 128), (1, 129, 3, 64), (1, 200, 2, 128), (2, 256, 1, 128)]
+SMALL = [(1, 1, 1, 64), (1, 17, 2, 64), (2, 64, 2, 128), (1, 129, 3, 64), (1, 200, 2, 128), (2, 256, 1, 128),
+         (1, 700, 2, 64), (1, 1000, 1, 128)]  # (the last two: many tiles, a ragged end)
 
 
 @pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
