@@ -582,7 +582,7 @@ def main():
                    "global_batch": w.B, "seq_len": w.N, "parallelism": "single GPU"},
         "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "roofline": roof(bf, bwd_s, "fa_bwd call (bwd_dq_kernel, which also forms the row terms, + bwd_dkdv_kernel)", "fa_bwd"),
-        "roofline_fwd": roof(ff, fwd_s, "fwd_kernel", "fa_fwd"),
+        "roofline_fwd": roof(ff, fwd_s, "fwd48_kernel (the causal d = 128 form with 192-row workgroups)", "fa_fwd"),
         "cpu_baseline": cpu,
         "detail": detail,
     }

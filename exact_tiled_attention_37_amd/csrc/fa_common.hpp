@@ -50,6 +50,13 @@ constexpr int kNumXcd = 8;  // MI355X: 8 accelerator complex dies, one L2 each
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
+// v_mfma_f32_16x16x32_bf16, lane l, G = l / 16:
+//   A operand (16 x 32, M x K): lane l holds row m = l % 16, k = 8G .. 8G+7
+//   B operand (32 x 16, K x N): lane l holds column n = l % 16, k = 8G .. 8G+7
+//   C/D (16 x 16):              lane l holds column n = l % 16, rows 4G .. 4G+3
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
 
 // Generic pointers into __shared__ arrays are converted to LDS (address
 // space 3) pointers so that ds_read / ds_write instructions are emitted.
@@ -141,6 +148,18 @@ __device__ __forceinline__ float xhalf_sum(float x) {
   uint32_t u = __float_as_uint(x);
   auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// Combine a value over the four lanes l, l ^ 16, l ^ 32, l ^ 48
+// (v_permlane16_swap, then v_permlane32_swap).
+__device__ __forceinline__ float xquad_max(float x) {
+  uint32_t u = __float_as_uint(x);
+  auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return xhalf_max(vmax(__uint_as_float(r[0]), __uint_as_float(r[1])));
+}
+__device__ __forceinline__ float xquad_sum(float x) {
+  uint32_t u = __float_as_uint(x);
+  auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return xhalf_sum(__uint_as_float(r[0]) + __uint_as_float(r[1]));
 }
 
 __device__ __forceinline__ bf16x8 to_bf16x8(f32x8 x) { return __builtin_convertvector(x, bf16x8); }

@@ -16,7 +16,9 @@
 // softmax arithmetic overlaps another's matrix instructions; a d = 128
 // launch too small for that (at most one workgroup per CU) gives each
 // workgroup two groups of 4 waves that split the key tiles between them and
-// combine their partial results at the end.
+// combine their partial results at the end. Causal self-attention launches
+// at d = 128 with more than a round of work take fwd48_kernel instead:
+// 192-row workgroups of four 48-row waves, two per CU (see there).
 //
 // K/V tiles move from memory straight into LDS with buffer loads
 // that write LDS directly (no register staging), double-buffered: the next
@@ -97,6 +99,8 @@ struct FwdCfgSplit128 : KernelCfg<128, 128, 64, 2, 2> {
   static constexpr int KSPLIT = 2;
 };
 constexpr int kNumCus = kNumXcd * kCusPerXcd;
+// Query rows per workgroup of fwd48_kernel (4 waves x 48 rows).
+constexpr int kFwd48Rows = 192;
 // Decode-shaped calls (a few query rows against a long key history) are
 // bound by streaming K and V from memory, and their parallelism comes from
 // splitting the keys, not from query blocks: one wave per workgroup holds
@@ -552,6 +556,225 @@ __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD))) v
   }
 }
 
+// Causal self-attention at d = 128 (bf16 output, no bias): 48 query rows per wave
+// on 16x16x32 MFMAs, 4 waves (192 rows) per workgroup sharing each K/V tile,
+// two workgroups per CU. Every K and V^T operand read from LDS feeds three
+// MFMAs (one per 16-row query block of the wave), and every K/V tile brought
+// into LDS serves 192 rows: a third fewer LDS and LDS-DMA bytes per flop than
+// 32-row waves in 128-row workgroups, at the cost of the third wave per SIMD
+// (48 rows need ~240 registers).
+//
+// Per wave and 32-key tile:
+//   S^T = K Q^T  as 2 x 3 blocks of 16 keys x 16 query rows (lane l owns
+//                query column l % 16 of each block and keys 4G .. 4G+3,
+//                G = l / 16; a row's 32 scores sit in four lanes)
+//   online softmax in the log2 domain with the sum test of fwd_kernel, per
+//                query block (three running maxima and sums per lane)
+//   O^T += V^T P^T  as 8 x 3 blocks of 16 columns x 16 rows: P^T is taken
+//                straight from the S^T accumulators (keys 4G .. 4G+3 of the
+//                two 16-key blocks as the k slots 8G .. 8G+7), V^T with LDS
+//                transpose reads of the same keys.
+// Blocks are aligned to the end of the sequence, so the one partial block is
+// the lightest (rows before 0 are absent: their Q reads as zeros, every key
+// is masked for them, nothing of theirs is stored).
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd48_kernel(
+    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V, bf16* __restrict__ O,
+    float* __restrict__ LSE, int N, int H, int nqb, int total_blocks, float c2, uint32_t q_sign) {
+  constexpr int D = 128, NW = 4, WR = kFwd48Rows / NW, QB = WR / 16;
+  constexpr int BC = 32, KB = BC / 16, DS = D / 32, DB = D / 16, STAGES = 2;
+  using T = Tile<BC, D>;
+  constexpr int TILE = T::BYTES;
+  constexpr int DMA_PER_WAVE = T::LOADS / NW;
+  static_assert(T::LOADS % NW == 0, "tile loads split evenly over the waves");
+  __shared__ __attribute__((aligned(1024))) char ring[STAGES * 2 * TILE];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar registers
+  const int G = lane >> 4, c16 = lane & 15;
+  const HeadRank hr = block_order<true>(blockIdx.x, total_blocks / nqb, nqb, kCusPerXcd * 2, 2);
+  const int head = hr.head, qblk = nqb - 1 - hr.rank;  // longest causal rows first
+  const int b = head / H, h = head - b * H;
+  const long hoff = ((long)b * N * H + h) * D;
+  const uint32_t tokb = (uint32_t)H * D * 2;
+  const uint32_t nrec = (uint32_t)(N - 1) * tokb + D * 2;
+  const auto rq = make_rsrc(Q + hoff, nrec);
+  const u32x4 rk = make_raw_rsrc(K + hoff, nrec), rv = make_raw_rsrc(V + hoff, nrec);
+
+  const int row0 = N - (nqb - qblk) * kFwd48Rows;
+  const int qw0 = row0 + wave * WR;  // first query row of this wave (may be < 0)
+  // Q as the B operand: query block qb, row qw0 + 16 qb + c16, d = 32 ds + 8G .. +7.
+  bf16x8 qf[QB][DS];
+  int key_lim[QB];  // the last key each of the lane's rows sees
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int row = qw0 + 16 * qb + c16;
+    key_lim[qb] = min(row, N - 1);
+    const uint32_t off = (uint32_t)((row < 0 || row >= N) ? N : row) * tokb + 16u * G;
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) qf[qb][ds] = __builtin_bit_cast(bf16x8, buf_load16(rq, off + 64 * ds) ^ q_sign);
+  }
+
+  // LDS-DMA of a tile as in fwd_kernel: fixed per-lane offsets, the tile's
+  // position in the scalar resource.
+  uint32_t dma_off[DMA_PER_WAVE];
+#pragma unroll
+  for (int t = 0; t < DMA_PER_WAVE; ++t) {
+    const int u = wave + NW * t;
+    dma_off[t] = (uint32_t)T::dma_row(u, lane) * tokb + 16u * T::dma_chunk(u, lane);
+  }
+  const uint32_t ring_lds = lds_base(ring);
+  auto issue = [&](int tile) __attribute__((always_inline)) {
+    const uint32_t toff = (uint32_t)(tile * BC) * tokb;
+    const u32x4 rkt = rsrc_advance(rk, toff), rvt = rsrc_advance(rv, toff);
+    const uint32_t l0 = ring_lds + (uint32_t)((tile % STAGES) * 2 * TILE);
+#pragma unroll
+    for (int t = 0; t < DMA_PER_WAVE; ++t) {
+      const int u = wave + NW * t;
+      dma16_at(rkt, l0 + T::dma_dst(u), dma_off[t]);
+      dma16_at(rvt, l0 + T::dma_dst(u) + TILE, dma_off[t]);
+    }
+  };
+
+  // Tiles 0 .. ntiles - 1; those before tu need no mask for any row of the block.
+  const int kv_len = max(0, min(N, row0 + kFwd48Rows));
+  const int ntiles = (kv_len + BC - 1) / BC;
+  const int tu = min(min(max(0, row0 + 1) / BC, N / BC), ntiles);
+
+  f32x4 oacc[DB][QB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) oacc[db][qb] = f32x4{};
+  float m_run[QB], l_run[QB];  // per query block: running max (log2 domain, stale by <= 8), lane's sum share
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) m_run[qb] = kNoMax, l_run[qb] = 0.f;
+
+  auto compute = [&](int j, const char* kt, auto mask_tag, bool first) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    const char* vt = kt + TILE;
+    const int key0 = j * BC;
+    f32x4 s[KB][QB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) s[kb][qb] = f32x4{};
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const bf16x8 a = T::row8(kt, 16 * kb + c16, 4 * ds + G);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) s[kb][qb] = mfma16(a, qf[qb][ds], s[kb][qb]);
+      }
+    if constexpr (MASK) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (key0 + 16 * kb + 4 * G + i > key_lim[qb]) s[kb][qb][i] = -INFINITY;
+    }
+    // P^T in bf16 (k slots 8G .. 8G+7 = keys 4G .. 4G+3 of both 16-key
+    // blocks) and the lane's fp32 sums of P per query block.
+    bf16x8 pf[QB];
+    float t[QB];
+    auto probs = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        f32x8 p;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float sv = s[e >> 2][qb][e & 3];
+          float x = fast_exp2(__builtin_fmaf(sv, c2, -m_run[qb]));
+          if constexpr (MASK) x = (sv == -INFINITY) ? 0.f : x;  // exact zero even when c2 = 0
+          p[e] = x;
+        }
+        t[qb] = sum8(p);
+        pf[qb] = to_bf16x8(p);
+      }
+    };
+    // The sum test of fwd_kernel, for all three query blocks at once; the
+    // scores stay in registers for the second path.
+    bool slow = true;  // wave-uniform
+    if (!first) {
+      probs();
+      slow = __builtin_amdgcn_ballot_w64(!(t[0] <= kPSumMax && t[1] <= kPSumMax && t[2] <= kPSumMax)) != 0;
+    }
+    if (slow) {
+      asm volatile("" ::: "memory");  // a branch
+      bool grow[QB], any = false;
+      float tile_m[QB];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) mx = vmax3(mx, vmax(s[kb][qb][0], s[kb][qb][1]), vmax(s[kb][qb][2], s[kb][qb][3]));
+        mx = xquad_max(mx);
+        tile_m[qb] = (mx == -INFINITY) ? -INFINITY : mx * c2;
+        grow[qb] = tile_m[qb] > m_run[qb];
+        any |= grow[qb];
+      }
+      if (__builtin_amdgcn_ballot_w64(any)) {  // wave-uniform
+        asm volatile("" ::: "memory");        // keep it a branch (no speculation)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          const float m_new = grow[qb] ? tile_m[qb] : m_run[qb];
+          const float alpha = fast_exp2(m_run[qb] - m_new);  // 0 from kNoMax, 1 when unchanged
+          l_run[qb] *= alpha;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) oacc[db][qb] *= alpha;
+          m_run[qb] = m_new;
+        }
+      }
+      probs();
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) l_run[qb] += t[qb];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const bf16x8 a = T::col8(vt, 4 * G, 16 + 4 * G, 16 * db, lane);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) oacc[db][qb] = mfma16(a, pf[qb], oacc[db][qb]);
+    }
+  };
+
+  // Double-buffered ring: iteration t loads tile t + 1 into the stage tile
+  // t - 1 used (every wave finished it before the last barrier), computes
+  // tile t, waits for its own loads and meets the other waves at the barrier.
+  if (ntiles > 0) issue(0);
+  wait_vmem();
+  __syncthreads();
+  int t = 0;
+  for (; t < tu; ++t) {
+    if (t + 1 < ntiles) issue(t + 1);
+    compute(t, ring + (t % STAGES) * 2 * TILE, std::false_type{}, t == 0);
+    wait_vmem();
+    __syncthreads();
+  }
+  for (; t < ntiles; ++t) {
+    if (t + 1 < ntiles) issue(t + 1);
+    // A tile whose first key lies past this wave's last row is fully masked for it.
+    if (t * BC <= qw0 + WR - 1) compute(t, ring + (t % STAGES) * 2 * TILE, std::true_type{}, t == 0);
+    wait_vmem();
+    __syncthreads();
+  }
+
+  // A row that saw no key (only rows before 0) has l = 0 and is not stored.
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const float l_tot = xquad_sum(l_run[qb]);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const int row = qw0 + 16 * qb + c16;
+    if (row >= 0 && row < N) {
+      if (G == 0) LSE[(long)head * N + row] = l_tot > 0.f ? (m_run[qb] + log2f(l_tot)) * kLn2 : -INFINITY;
+      bf16* const orow = O + hoff + (long)row * H * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) *reinterpret_cast<bf16x4*>(orow + 16 * db + 4 * G) = to_bf16x4(oacc[db][qb] * inv);
+    }
+  }
+}
+
 }  // namespace
 
 template <int D, bool CAUSAL>
@@ -588,10 +811,21 @@ hipError_t launch_fwd(const FwdArgs& a) {
     else
       plain(FwdCfg<D>{});
   } else {
-    if (total <= kNumCus)
+    // Causal self-attention with more than one round of 192-row workgroups
+    // (two per CU) takes fwd48_kernel; measured 1-7% faster there (most on
+    // long rows: B=4 H=16 N=4096 262 -> 249 us, N = 16384 974 -> 905 us) and
+    // 4-15% slower with a single round or less, where the heaviest blocks
+    // set the time. Non-causal launches measured the same or slower with it.
+    const int nqb48 = (a.Nq + kFwd48Rows - 1) / kFwd48Rows;
+    const int total48 = a.B * a.H * nqb48;
+    if (total <= kNumCus) {
       plain(FwdCfgSplit128{});
-    else
+    } else if (CAUSAL && !a.f32_out && a.delta == 0 && a.Nq == a.Nk && total48 > 2 * kNumCus) {
+      hipLaunchKernelGGL(fwd48_kernel, dim3(total48), dim3(256), 0, a.stream, q, k, v,
+                         static_cast<bf16*>(a.o), a.lse, a.Nq, a.H, nqb48, total48, c2, q_sign);
+    } else {
       plain(FwdCfg<D>{});
+    }
   }
   return hipGetLastError();
 }
