@@ -80,8 +80,14 @@ __device__ __forceinline__ i16x4 lds_read_tr(const char* base, int off) {
 // LDS tile of R rows (R = 32, 64 or 128) by D bfloat16 columns, laid out as
 // described at the top of this file: block (row / 16, chunk / 4) at
 // ((row / 16) * (D / 32) + chunk / 4) * 1024 bytes; inside a block, row r
-// (0..15) and chunk c (0..3) sit in 16-byte slot 4 r + (c ^ (r / 4)).
-template <int R, int D>
+// (0..15) and chunk c (0..3) sit in 16-byte slot 4 r + (c ^ s(r)) with
+// s(r) = r / 4. SWAP: s(r) is r / 4 with its two bits swapped (0, 2, 1, 3),
+// for transpose reads whose four 16-lane groups take four consecutive rows
+// each, groups 4 rows apart, at the same columns: the LDS serves such a
+// read 32 lanes at a time, and with s(r) = r / 4 rows r and r + 4 put the
+// same two chunks on the same banks (a 2-way conflict on every read), while
+// the swapped order moves rows 4..7 to the other two chunk slots.
+template <int R, int D, bool SWAP = false>
 struct Tile {
   static_assert(R == 32 || R == 64 || R == 128, "tile rows");
   static_assert(D == 64 || D == 128, "head dimension");
@@ -90,23 +96,25 @@ struct Tile {
   static constexpr int BYTES = R * D * 2;
   static constexpr int LOADS = BYTES / 1024;  // whole-wave 1 KiB loads per tile
 
+  // the chunk swizzle of row rl (0..15) of a block
+  __device__ static constexpr int swz(int rl) { return SWAP ? (((rl >> 2) & 1) << 1) | (rl >> 3) : rl >> 2; }
   __device__ static constexpr int addr(int row, int c) {
     const int rl = row & 15;
-    return (((row >> 4) * NCB + (c >> 2)) << 10) + ((rl << 2) + ((c & 3) ^ (rl >> 2))) * 16;
+    return (((row >> 4) * NCB + (c >> 2)) << 10) + ((rl << 2) + ((c & 3) ^ swz(rl))) * 16;
   }
   // Whole-wave load u fills block u (bytes [1024 u, 1024 u + 1024)); lane i
   // writes slot i, which holds chunk dma_chunk of row dma_row.
   __device__ static constexpr int dma_dst(int u) { return u << 10; }
   __device__ static constexpr int dma_row(int u, int lane) { return (u / NCB) * 16 + (lane >> 2); }
   __device__ static constexpr int dma_chunk(int u, int lane) {
-    return (u % NCB) * 4 + ((lane & 3) ^ ((lane >> 2) >> 2));
+    return (u % NCB) * 4 + ((lane & 3) ^ swz(lane >> 2));
   }
 
   // Byte offset in memory (rows row_bytes apart) of what lane `lane` loads
   // for whole-wave load u, split into a part that depends only on the lane
   // and a part that depends only on u (wave-uniform).
   __device__ static uint32_t dma_lane_off(int lane, uint32_t row_bytes) {
-    return (uint32_t)(lane >> 2) * row_bytes + 16u * (uint32_t)((lane & 3) ^ (lane >> 4));
+    return (uint32_t)(lane >> 2) * row_bytes + 16u * (uint32_t)((lane & 3) ^ swz(lane >> 2));
   }
   __device__ static uint32_t dma_load_off(int u, uint32_t row_bytes) {
     return (uint32_t)(u / NCB) * 16u * row_bytes + 64u * (uint32_t)(u % NCB);
