@@ -81,12 +81,14 @@ __device__ __forceinline__ i16x4 lds_read_tr(const char* base, int off) {
 // described at the top of this file: block (row / 16, chunk / 4) at
 // ((row / 16) * (D / 32) + chunk / 4) * 1024 bytes; inside a block, row r
 // (0..15) and chunk c (0..3) sit in 16-byte slot 4 r + (c ^ s(r)) with
-// s(r) = r / 4. SWAP: s(r) is r / 4 with its two bits swapped (0, 2, 1, 3),
-// for transpose reads whose four 16-lane groups take four consecutive rows
-// each, groups 4 rows apart, at the same columns: the LDS serves such a
-// read 32 lanes at a time, and with s(r) = r / 4 rows r and r + 4 put the
-// same two chunks on the same banks (a 2-way conflict on every read), while
-// the swapped order moves rows 4..7 to the other two chunk slots.
+// s(r) = r / 4. SWAP: s(r) = (r / 2) % 4, for waves whose four 16-lane
+// groups read four different chunks of the same 16 rows (row reads) or
+// four consecutive rows each, 4 rows apart, at the same columns (transpose
+// reads). Measured with the LDS bank-conflict counter on a probe of exactly
+// those reads: with s(r) = r / 4 every ds_read_b128 of the row pattern
+// costs 4 conflict cycles and every ds_read_b64_tr_b16 of the transpose
+// pattern 2; with (r / 2) % 4 neither conflicts. (The 32-row waves' reads,
+// 32 consecutive rows per chunk, are conflict-free with r / 4.)
 template <int R, int D, bool SWAP = false>
 struct Tile {
   static_assert(R == 32 || R == 64 || R == 128, "tile rows");
@@ -97,7 +99,7 @@ struct Tile {
   static constexpr int LOADS = BYTES / 1024;  // whole-wave 1 KiB loads per tile
 
   // the chunk swizzle of row rl (0..15) of a block
-  __device__ static constexpr int swz(int rl) { return SWAP ? (((rl >> 2) & 1) << 1) | (rl >> 3) : rl >> 2; }
+  __device__ static constexpr int swz(int rl) { return SWAP ? (rl >> 1) & 3 : rl >> 2; }
   __device__ static constexpr int addr(int row, int c) {
     const int rl = row & 15;
     return (((row >> 4) * NCB + (c >> 2)) << 10) + ((rl << 2) + ((c & 3) ^ swz(rl))) * 16;

@@ -582,7 +582,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     float* __restrict__ LSE, int N, int H, int nqb, int total_blocks, float c2, uint32_t q_sign) {
   constexpr int D = 128, NW = 4, WR = kFwd48Rows / NW, QB = WR / 16;
   constexpr int BC = 32, KB = BC / 16, DS = D / 32, DB = D / 16, STAGES = 2;
-  using T = Tile<BC, D, true>;  // swapped swizzle: the V^T reads below are conflict-free with it
+  using T = Tile<BC, D, true>;  // the swizzle under which the K and V^T reads below are conflict-free
   constexpr int TILE = T::BYTES;
   constexpr int DMA_PER_WAVE = T::LOADS / NW;
   static_assert(T::LOADS % NW == 0, "tile loads split evenly over the waves");
