@@ -16,9 +16,10 @@
 // softmax arithmetic overlaps another's matrix instructions; a d = 128
 // launch too small for that (at most one workgroup per CU) gives each
 // workgroup two groups of 4 waves that split the key tiles between them and
-// combine their partial results at the end. Causal self-attention launches
-// at d = 128 with more than a round of work take fwd48_kernel instead:
-// 192-row workgroups of four 48-row waves, two per CU (see there).
+// combine their partial results at the end. Self-attention launches at
+// d = 128 over at least 2048 keys with more than a round of work take
+// fwd48_kernel instead: 192-row workgroups of four 48-row waves, two per CU
+// (see there).
 //
 // K/V tiles move from memory straight into LDS with buffer loads
 // that write LDS directly (no register staging), double-buffered: the next
@@ -99,8 +100,10 @@ struct FwdCfgSplit128 : KernelCfg<128, 128, 64, 2, 2> {
   static constexpr int KSPLIT = 2;
 };
 constexpr int kNumCus = kNumXcd * kCusPerXcd;
-// Query rows per workgroup of fwd48_kernel (4 waves x 48 rows).
+// Query rows per workgroup of fwd48_kernel (4 waves x 48 rows), and the
+// shortest sequence it takes (launch_fwd).
 constexpr int kFwd48Rows = 192;
+constexpr int kFwd48MinKeys = 2048;
 // Decode-shaped calls (a few query rows against a long key history) are
 // bound by streaming K and V from memory, and their parallelism comes from
 // splitting the keys, not from query blocks: one wave per workgroup holds
@@ -556,7 +559,7 @@ __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD))) v
   }
 }
 
-// Causal self-attention at d = 128 (bf16 output, no bias): 48 query rows per wave
+// Self-attention at d = 128 (bf16 output, no bias): 48 query rows per wave
 // on 16x16x32 MFMAs, 4 waves (192 rows) per workgroup sharing each K/V tile,
 // two workgroups per CU. Every K and V^T operand read from LDS feeds three
 // MFMAs (one per 16-row query block of the wave), and every K/V tile brought
@@ -574,9 +577,11 @@ __attribute__((amdgpu_waves_per_eu(Cfg::WAVES_PER_SIMD, Cfg::WAVES_PER_SIMD))) v
 //                straight from the S^T accumulators (keys 4G .. 4G+3 of the
 //                two 16-key blocks as the k slots 8G .. 8G+7), V^T with LDS
 //                transpose reads of the same keys.
-// Blocks are aligned to the end of the sequence, so the one partial block is
-// the lightest (rows before 0 are absent: their Q reads as zeros, every key
-// is masked for them, nothing of theirs is stored).
+// Causal blocks are aligned to the end of the sequence, so the one partial
+// block is the lightest (rows before 0 are absent: their Q reads as zeros,
+// every key is masked for them, nothing of theirs is stored); non-causal
+// blocks start at row 0 and the last one is partial.
+template <bool CAUSAL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd48_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V, bf16* __restrict__ O,
     float* __restrict__ LSE, int N, int H, int nqb, int total_blocks, float c2, uint32_t q_sign) {
@@ -591,7 +596,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar registers
   const int G = lane >> 4, c16 = lane & 15;
-  const HeadRank hr = block_order<true>(blockIdx.x, total_blocks / nqb, nqb, kCusPerXcd * 2, 2);
+  const HeadRank hr = block_order<CAUSAL>(blockIdx.x, total_blocks / nqb, nqb, kCusPerXcd * 2, 2);
   const int head = hr.head, qblk = nqb - 1 - hr.rank;  // longest causal rows first
   const int b = head / H, h = head - b * H;
   const long hoff = ((long)b * N * H + h) * D;
@@ -600,7 +605,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const auto rq = make_rsrc(Q + hoff, nrec);
   const u32x4 rk = make_raw_rsrc(K + hoff, nrec), rv = make_raw_rsrc(V + hoff, nrec);
 
-  const int row0 = N - (nqb - qblk) * kFwd48Rows;
+  const int row0 = CAUSAL ? N - (nqb - qblk) * kFwd48Rows : qblk * kFwd48Rows;
   const int qw0 = row0 + wave * WR;  // first query row of this wave (may be < 0)
   // Q as the B operand: query block qb, row qw0 + 16 qb + c16, d = 32 ds + 8G .. +7.
   bf16x8 qf[QB][DS];
@@ -608,7 +613,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int row = qw0 + 16 * qb + c16;
-    key_lim[qb] = min(row, N - 1);
+    key_lim[qb] = CAUSAL ? min(row, N - 1) : N - 1;
     const uint32_t off = (uint32_t)((row < 0 || row >= N) ? N : row) * tokb + 16u * G;
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds) qf[qb][ds] = __builtin_bit_cast(bf16x8, buf_load16(rq, off + 64 * ds) ^ q_sign);
@@ -636,9 +641,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   };
 
   // Tiles 0 .. ntiles - 1; those before tu need no mask for any row of the block.
-  const int kv_len = max(0, min(N, row0 + kFwd48Rows));
+  const int kv_len = CAUSAL ? max(0, min(N, row0 + kFwd48Rows)) : N;
   const int ntiles = (kv_len + BC - 1) / BC;
-  const int tu = min(min(max(0, row0 + 1) / BC, N / BC), ntiles);
+  const int tu = min(CAUSAL ? min(max(0, row0 + 1) / BC, N / BC) : N / BC, ntiles);
 
   f32x4 oacc[DB][QB];
 #pragma unroll
@@ -754,13 +759,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
   for (; t < ntiles; ++t) {
     if (t + 1 < ntiles) issue(t + 1);
-    // A tile whose first key lies past this wave's last row is fully masked for it.
-    if (t * BC <= qw0 + WR - 1) compute(t, ring + (t % STAGES) * 2 * TILE, std::true_type{}, t == 0);
+    // A causal tile whose first key lies past this wave's last row is fully masked for it.
+    if (!CAUSAL || t * BC <= qw0 + WR - 1) compute(t, ring + (t % STAGES) * 2 * TILE, std::true_type{}, t == 0);
     wait_vmem();
     __syncthreads();
   }
 
-  // A row that saw no key (only rows before 0) has l = 0 and is not stored.
+  // A row that saw no key (only causal rows before 0) has l = 0 and is not stored.
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float l_tot = xquad_sum(l_run[qb]);
@@ -811,17 +816,19 @@ hipError_t launch_fwd(const FwdArgs& a) {
     else
       plain(FwdCfg<D>{});
   } else {
-    // Causal self-attention with more than one round of 192-row workgroups
-    // (two per CU) takes fwd48_kernel; measured 1-7% faster there (most on
-    // long rows: B=4 H=16 N=4096 262 -> 249 us, N = 16384 974 -> 905 us) and
-    // 4-15% slower with a single round or less, where the heaviest blocks
-    // set the time. Non-causal launches measured the same or slower with it.
+    // Self-attention over at least 2048 keys with more than one round of
+    // 192-row workgroups (two per CU) takes fwd48_kernel. Measured against
+    // the 128-row kernel: causal 1-8% faster (B=4 H=16 N=4096 262 -> 239 us,
+    // N = 16384 974 -> 864 us), non-causal 1-2.5% faster; with one round or
+    // less it was 4-15% slower (the heaviest blocks set the time), and below
+    // 2048 keys equal to 12% slower (short rows: the per-block start and the
+    // rounding of the block count to whole rounds weigh more).
     const int nqb48 = (a.Nq + kFwd48Rows - 1) / kFwd48Rows;
     const int total48 = a.B * a.H * nqb48;
     if (total <= kNumCus) {
       plain(FwdCfgSplit128{});
-    } else if (CAUSAL && !a.f32_out && a.delta == 0 && a.Nq == a.Nk && total48 > 2 * kNumCus) {
-      hipLaunchKernelGGL(fwd48_kernel, dim3(total48), dim3(256), 0, a.stream, q, k, v,
+    } else if (!a.f32_out && a.delta == 0 && a.Nq == a.Nk && a.Nq >= kFwd48MinKeys && total48 > 2 * kNumCus) {
+      hipLaunchKernelGGL(fwd48_kernel<CAUSAL>, dim3(total48), dim3(256), 0, a.stream, q, k, v,
                          static_cast<bf16*>(a.o), a.lse, a.Nq, a.H, nqb48, total48, c2, q_sign);
     } else {
       plain(FwdCfg<D>{});
