@@ -372,16 +372,23 @@ def test_workload_train_forward_backward():
 MAX_ELEMS = (1 << 31) - (1 << 16)  # per tensor, the limit the library states
 
 
+MAX_SHAPES = [
+    (4681, 224, 16, 128),  # 224 = 128 + 96 rows: the 128-row forward
+    (248, 4228, 16, 128),  # 4228 = 22 * 192 + 4 rows: the 192-row forward; its first causal block holds 4 rows
+]
+
+
+@pytest.mark.parametrize("shape", MAX_SHAPES, ids=lambda s: "B%dN%dH%dd%d" % s)
 @pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
-def test_max_size_sampled_heads(causal):
+def test_max_size_sampled_heads(causal, shape):
     """B*N*H*d exactly at the library's limit (4 GiB per bf16 tensor), N
-    ragged (224 = 128 + 96 rows): the heads farthest from the base pointers
+    ragged, for each forward form: the heads farthest from the base pointers
     are compared whole, forward and backward, with the oracle. Heads are
     independent, so the other heads hold filler drawn on the device; their
     outputs are only required to be finite."""
     import torch
 
-    B, N, H, d = 4681, 224, 16, 128
+    B, N, H, d = shape
     assert B * N * H * d == MAX_ELEMS
     announce(f"max size B={B} N={N} H={H} d={d} causal={causal}")
     scale = d ** -0.5
