@@ -158,3 +158,17 @@ def test_large_launch_deterministic_and_head_permutation(causal):
     torch.cuda.synchronize()
     p = torch.as_tensor(perm, device="cuda")
     assert torch.equal(o3, o1.index_select(2, p)) and torch.equal(l3, l1.index_select(1, p))
+
+
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
+@pytest.mark.parametrize("case", [(1, 2048, 46), (1, 2048, 47), (1, 2047, 60)], ids=lambda c: "B%dN%dH%d" % c)
+def test_switch_boundary(case, causal):
+    """Both sides of the launch switch at N = 2048: 46 heads (506 workgroups
+    of 192 rows, one round or less: the 128-row form), 47 heads (517: the
+    192-row form) and N = 2047 (below the key limit: the 128-row form), each
+    against the oracle."""
+    B, N, H = case
+    assert in_regime(B, N, H) == (H == 47)
+    announce(f"switch boundary B={B} N={N} H={H} causal={causal}")
+    bits = si.draw(B, N, H, 128, 5000 + H)
+    run_and_compare(bits, B, N, H, 1.0 / math.sqrt(128), causal=causal)
