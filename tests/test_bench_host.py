@@ -58,9 +58,23 @@ def test_stored_traffic_follows_the_sources(tmp_path, monkeypatch):
     assert bench.stored_traffic("train_causal") is None
 
 
-def test_source_hash_covers_the_measured_kernels():
-    """Every file the hash covers exists, and changing any byte of one changes it."""
+def test_source_hash_covers_the_measured_kernels(tmp_path, monkeypatch):
+    """Every file the hash covers exists, and changing one byte of any of
+    them changes the hash."""
+    import shutil
+
     csrc = os.path.join(ROOT, "exact_tiled_attention_37_amd", "csrc")
-    for name in bench.TRAFFIC_SOURCES:
-        assert os.path.isfile(os.path.join(csrc, name)), name
     assert {"fa_fwd.hip", "fa_bwd.hip", "fa_common.hpp"} <= set(bench.TRAFFIC_SOURCES)
+    copy = tmp_path / "exact_tiled_attention_37_amd" / "csrc"
+    copy.mkdir(parents=True)
+    for name in bench.TRAFFIC_SOURCES:
+        shutil.copy(os.path.join(csrc, name), copy / name)
+    base = bench.kernel_source_hash()
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.kernel_source_hash() == base
+    for name in bench.TRAFFIC_SOURCES:
+        data = (copy / name).read_bytes()
+        (copy / name).write_bytes(data[:-1] + bytes([data[-1] ^ 1]))
+        assert bench.kernel_source_hash() != base, name
+        (copy / name).write_bytes(data)
+    assert bench.kernel_source_hash() == base
