@@ -33,6 +33,7 @@ CAUSAL_CASES = [
     (1, 2200, 44),  # block 0 starts at row -104: its first two waves have no row, the third starts at row 0
     (1, 2304, 45),  # N a multiple of 192: no partial block
     (1, 2900, 40),  # 16 blocks, ragged last key tile
+    (48, 2050, 1),  # one head per batch: 256-byte token stride, batch offsets carry the heads
 ]
 NONCAUSAL_CASES = [
     (1, 2100, 48),  # partial last block (rows past N absent), ragged last key tile
